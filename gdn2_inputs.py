@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for the Gated DeltaNet-2 token mixer.
+
+This module is shared by the tests, the benchmark and the oracle checks. It
+holds none of the mixer's arithmetic: it only draws random numbers and applies
+the input transforms that the pages put in front of the mixer (L2-normalised
+q and k, sigmoid gates b and w, a non-positive log-decay), then rounds to the
+working dtype.
+
+Recipe (all draws are float32 from numpy's PCG64 `default_rng`):
+
+* Every (sequence i, token block j) of 1024 tokens has its own stream
+  ``default_rng([seed, i, j])``. Within a block the draws come in this order,
+  each of shape ``[block_len, H, d]``: q, k, v, x_alpha, x_b, x_w, then for
+  collapsed heads beta and a (shape ``[block_len, H_c]``). Any token range can
+  therefore be regenerated on its own, and blocks are drawn in parallel.
+* q, k ~ N(0, 1), L2-normalised over the key axis (in float64, then rounded).
+* v ~ N(0, 1).
+* log_alpha = -softplus(x_alpha), x_alpha ~ N(-3, 1), kept float32.
+* b = sigmoid(x_b), w = sigmoid(x_w), x ~ N(0, 1).
+* Collapsed heads (scalar gates): b = w = beta broadcast over channels with
+  beta = sigmoid(N(0,1)); log_alpha = -softplus(N(-3,1)) broadcast over d_k.
+* S0 ~ N(0, s0_std) float32 per sequence, stream ``default_rng([seed, i, 2**20])``.
+* Variable lengths: ``default_rng([seed, 2**21]).integers(lo, hi, endpoint=True)``.
+* Decode step s: per-step stream ``default_rng([seed, 2**22, s])`` drawing
+  q, k, v, x_alpha, x_b, x_w of shape ``[N, H, d]``; the resident state is
+  drawn from ``default_rng([seed, 2**22, 0])``.
+
+bf16 rounding is round-to-nearest-even on the float32 bit pattern; the arrays
+returned are float32 holding exactly the values the GPU receives.
+"""
+from __future__ import annotations
+
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+BLOCK = 1024  # tokens per independent random stream
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 value (ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _l2n(x: np.ndarray) -> np.ndarray:
+    x64 = x.astype(np.float64)
+    return (x64 / np.sqrt(np.sum(x64 * x64, axis=-1, keepdims=True))).astype(np.float32)
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(np.float32(0), x).astype(np.float32)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+@dataclasses.dataclass
+class Prefill:
+    """One packed prefill batch. Token tensors are ``[tokens, H, d]`` float32."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    log_alpha: np.ndarray
+    b: np.ndarray
+    w: np.ndarray
+    S0: Optional[np.ndarray]      # [N, H, dk, dv] float32 or None (zeros)
+    cu_seqlens: np.ndarray        # [N+1] int32 token offsets
+    B: int                        # batch rows when uniform, else 1
+    T: int                        # tokens per row (uniform) or total tokens
+    H: int
+    dk: int
+    dv: int
+    dtype: str                    # 'bf16' or 'f32'
+    varlen: bool
+
+    @property
+    def N(self) -> int:
+        return len(self.cu_seqlens) - 1
+
+    @property
+    def tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def _draw_block(seed, i, j, n, H, dk, dv, dtype, collapsed):
+    rng = np.random.default_rng([seed, i, j])
+    f = np.float32
+    q = rng.standard_normal((n, H, dk), dtype=f)
+    k = rng.standard_normal((n, H, dk), dtype=f)
+    v = rng.standard_normal((n, H, dv), dtype=f)
+    xa = rng.standard_normal((n, H, dk), dtype=f) - f(3.0)
+    xb = rng.standard_normal((n, H, dk), dtype=f)
+    xw = rng.standard_normal((n, H, dv), dtype=f)
+    q, k = _l2n(q), _l2n(k)
+    la = -_softplus(xa)
+    b, w = _sigmoid(xb), _sigmoid(xw)
+    if collapsed:
+        h0 = H - collapsed
+        beta = _sigmoid(rng.standard_normal((n, collapsed), dtype=f))
+        a = -_softplus(rng.standard_normal((n, collapsed), dtype=f) - f(3.0))
+        b[:, h0:, :] = beta[:, :, None]
+        w[:, h0:, :] = beta[:, :, None]
+        la[:, h0:, :] = a[:, :, None]
+    if dtype == 'bf16':
+        q, k, v, b, w = (bf16_round(t) for t in (q, k, v, b, w))
+    return q, k, v, la, b, w
+
+
+def prefill(seed: int, lengths, H: int, dk: int, dv: int, dtype: str = 'bf16',
+            s0_std: float = 0.0, collapsed: int = 0, uniform: bool = True,
+            threads: int = 8) -> Prefill:
+    """Generate a packed batch of sequences with the given lengths.
+
+    ``uniform=True`` means the batch is B equal rows of T tokens (no cu_seqlens
+    at the C-ABI); ``collapsed`` is the number of trailing heads whose gates
+    are scalar per token (b = w = beta, scalar alpha).
+    """
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    total = int(cu[-1])
+    out = {name: np.empty((total, H, d), np.float32)
+           for name, d in (('q', dk), ('k', dk), ('v', dv), ('la', dk), ('b', dk), ('w', dv))}
+    jobs = []
+    for i, L in enumerate(lengths):
+        for j in range(0, (L + BLOCK - 1) // BLOCK):
+            jobs.append((i, j, int(cu[i]) + j * BLOCK, min(BLOCK, L - j * BLOCK)))
+
+    def run(job):
+        i, j, t0, n = job
+        arrs = _draw_block(seed, i, j, n, H, dk, dv, dtype, collapsed)
+        for name, a in zip(('q', 'k', 'v', 'la', 'b', 'w'), arrs):
+            out[name][t0:t0 + n] = a
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(run, jobs))
+    S0 = None
+    if s0_std > 0:
+        S0 = np.empty((len(lengths), H, dk, dv), np.float32)
+        for i in range(len(lengths)):
+            rng = np.random.default_rng([seed, i, 2 ** 20])
+            S0[i] = rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    if uniform:
+        assert len(set(lengths)) == 1
+    return Prefill(q=out['q'], k=out['k'], v=out['v'], log_alpha=out['la'], b=out['b'],
+                   w=out['w'], S0=S0, cu_seqlens=cu, B=len(lengths) if uniform else 1,
+                   T=lengths[0] if uniform else total, H=H, dk=dk, dv=dv, dtype=dtype,
+                   varlen=not uniform)
+
+
+def varlen_lengths(seed: int, n: int, lo: int, hi: int) -> list:
+    return [int(x) for x in np.random.default_rng([seed, 2 ** 21]).integers(lo, hi, size=n, endpoint=True)]
+
+
+@dataclasses.dataclass
+class DecodeStep:
+    q: np.ndarray          # [N, H, dk]
+    k: np.ndarray
+    v: np.ndarray          # [N, H, dv]
+    log_alpha: np.ndarray  # [N, H, dk] float32
+    b: np.ndarray
+    w: np.ndarray
+
+
+def decode_state(seed: int, N: int, H: int, dk: int, dv: int, s0_std: float = 0.02) -> np.ndarray:
+    rng = np.random.default_rng([seed, 2 ** 22, 0])
+    return rng.standard_normal((N, H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+
+
+def decode_step(seed: int, step: int, N: int, H: int, dk: int, dv: int,
+                dtype: str = 'bf16') -> DecodeStep:
+    rng = np.random.default_rng([seed, 2 ** 22, step])
+    f = np.float32
+    q = _l2n(rng.standard_normal((N, H, dk), dtype=f))
+    k = _l2n(rng.standard_normal((N, H, dk), dtype=f))
+    v = rng.standard_normal((N, H, dv), dtype=f)
+    la = -_softplus(rng.standard_normal((N, H, dk), dtype=f) - f(3.0))
+    b = _sigmoid(rng.standard_normal((N, H, dk), dtype=f))
+    w = _sigmoid(rng.standard_normal((N, H, dv), dtype=f))
+    if dtype == 'bf16':
+        q, k, v, b, w = (bf16_round(t) for t in (q, k, v, b, w))
+    return DecodeStep(q=q, k=k, v=v, log_alpha=la, b=b, w=w)
+
+
+# The five workloads, by name. Sizes follow the configuration list that the
+# measurements are quoted on; `seed` doubles as the workload index.
+WORKLOADS = {
+    'tiny': dict(seed=0, B=1, T=128, H=1, dk=16, dv=16, dtype='f32', s0_std=0.0),
+    'prefill_b4_t4096': dict(seed=1, B=4, T=4096, H=16, dk=128, dv=128, dtype='bf16', s0_std=0.0),
+    'prefill_t65536': dict(seed=2, B=1, T=65536, H=16, dk=128, dv=128, dtype='bf16', s0_std=0.02),
+    'decode_n256': dict(seed=3, N=256, H=16, dk=128, dv=128, dtype='bf16', steps=1000, s0_std=0.02),
+    'varlen_32seq': dict(seed=4, n_seqs=32, lo=512, hi=16384, H=32, dk=128, dv=128,
+                         dtype='bf16', s0_std=0.02, collapsed=16),
+}
+
+
+def workload(name: str, threads: int = 8) -> Prefill:
+    """Full-size prefill workload by name (not for the decode workload)."""
+    c = WORKLOADS[name]
+    if name == 'varlen_32seq':
+        lens = varlen_lengths(c['seed'], c['n_seqs'], c['lo'], c['hi'])
+        return prefill(c['seed'], lens, c['H'], c['dk'], c['dv'], c['dtype'], c['s0_std'],
+                       collapsed=c['collapsed'], uniform=False, threads=threads)
+    return prefill(c['seed'], [c['T']] * c['B'], c['H'], c['dk'], c['dv'], c['dtype'],
+                   c['s0_std'], uniform=True, threads=threads)
