@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet-2 token mixer on one MI355X.
+
+Headline: prefill tokens/s on the long-context workload (B=1, H=16, T=65536,
+d_k=d_v=128, bf16 q/k/v/b/w, fp32 log alpha, fp32 state and output, S0 ~
+N(0, 0.02)). One step = one gdn2_chunk_fwd call over the whole batch (chunk
+prep + sequential state pass). The decode workload (256 sequences x 16 heads,
+fp32 state resident, 1000 single-token steps with fresh inputs) is measured in
+the same run and reported under "decode".
+
+Prints ONE JSON line. Inputs are synthetic and seeded (gdn2_inputs), resident
+in HBM before timing starts. Per-kernel durations come from HIP events that
+the library records on its stream during the timed region; the roofline uses
+algorithmic bytes (what the method must read and write), not measured traffic.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
+METRIC = 'GDN-2 prefill tokens/s (H=16,d=128,T=64K); decode steps/s; % of roofline'
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, 'gated_delta_rule_wy_amd', 'csrc')
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), 'rb') as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, 'profiles', 'traffic.json')
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(f'{kernel}@{workload}')
+    if not e or e.get('source_sha') != src_hash():
+        return None
+    return e['fetch_bytes'] + e['write_bytes']
+
+
+def roofline(kernel, alg_bytes, avg_ms, workload):
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    return {'bound': 'hbm', 'kernel': kernel, 'achieved': round(achieved, 1), 'peak': PEAK_HBM_GBS,
+            'unit': 'GB/s', 'frac': round(achieved / PEAK_HBM_GBS, 4),
+            'traffic': traffic_for(kernel, workload), 'alg_bytes_per_launch': int(alg_bytes),
+            'avg_launch_ms': round(avg_ms, 5)}
+
+
+def nthreads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def bench_prefill(args, torch, gdn2, gi):
+    name = 'prefill_t65536'
+    c = gi.WORKLOADS[name]
+    B, T, H, dk, dv = c['B'], c['T'], c['H'], c['dk'], c['dv']
+    t0 = time.time()
+    p = gi.workload(name, threads=nthreads())
+    log(f'[bench] generated {name} in {time.time() - t0:.1f}s')
+    dev = torch.device('cuda:0')
+    to = lambda x, dt: torch.from_numpy(x).to(dev).to(dt).reshape(B, T, H, x.shape[-1])
+    bf = torch.bfloat16
+    q, k, v, b, w = (to(x, bf) for x in (p.q, p.k, p.v, p.b, p.w))
+    la = to(p.log_alpha, torch.float32)
+    S0 = torch.from_numpy(p.S0).to(dev)
+    o = torch.empty(B, T, H, dv, device=dev)
+    ST = torch.empty(B, H, dk, dv, device=dev)
+    ws = torch.empty(gdn2.workspace_bytes(B, T, B, H, dk, dv, bf, False), dtype=torch.uint8, device=dev)
+    run = lambda: gdn2.chunk_fwd(q, k, v, la, b, w, S0, out=o, final_state=ST, workspace=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    gdn2.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = gdn2.profile_end()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f'[bench] prefill {ms:.3f} ms/step; kernels: ' +
+        ', '.join(f'{k} {v[1] / max(1, v[0]):.4f} ms' for k, v in prof.items()))
+
+    TH = B * T * H
+    in_b = 2 if p.dtype == 'bf16' else 4
+    alg = {
+        # what each kernel must read or write at the least: prep reads q, k, b and
+        # log alpha; the pass reads v, w and S0, writes o and S_T
+        'gdn2_chunk_prep': TH * (3 * dk * in_b + dk * 4),
+        'gdn2_chunk_pass': TH * (2 * dv * in_b + dv * 4) + 2 * B * H * dk * dv * 4,
+    }
+    avg = {k: v[1] / v[0] for k, v in prof.items() if v[0]}
+    dom = max(avg, key=avg.get)
+    step_bytes = sum(alg.values())
+    res = {
+        'ms_per_step': round(ms, 4), 'value': B * T / (ms * 1e-3),
+        'roofline': roofline(dom, alg[dom], avg[dom], name),
+        'step_roofline': {'bound': 'hbm', 'alg_bytes_per_step': int(step_bytes),
+                          'achieved': round(step_bytes / (ms * 1e-3) / 1e9, 1), 'peak': PEAK_HBM_GBS,
+                          'unit': 'GB/s', 'frac': round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        'kernels_ms': {k: round(v, 5) for k, v in avg.items()},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        n_s = args.cpu_sample_tokens
+        sl = slice(0, n_s)
+        nt = nthreads()
+        t0 = time.perf_counter()
+        o_ref, _ = oracle.forward(p.q[sl], p.k[sl], p.v[sl], p.log_alpha[sl], p.b[sl], p.w[sl], p.S0,
+                                  nthreads=nt)
+        dt = time.perf_counter() - t0
+        res['cpu_baseline'] = {'value': round(n_s / dt, 1), 'unit': 'tokens/s', 'cores': min(nt, H),
+                               'kind': 'oracle',
+                               'sample': f'first {n_s} of {T} tokens, all {H} heads (one thread per head '
+                                         f'chain, {min(nt, H)} chains at once), fp64; {dt:.1f}s'}
+        o_gpu = o[0, :n_s].float().cpu().numpy()
+        rms = float(np.sqrt(np.mean(o_ref ** 2)))
+        res['parity_sample'] = {'max_abs_err_over_rms': float(np.max(np.abs(o_gpu - o_ref)) / rms),
+                                'tokens': n_s}
+        log(f'[bench] oracle {n_s} tokens in {dt:.1f}s; parity {res["parity_sample"]}')
+    del q, k, v, b, w, la, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, torch, gdn2, gi):
+    name = 'decode_n256'
+    c = gi.WORKLOADS[name]
+    N, H, d = c['N'], c['H'], c['dk']
+    steps = args.decode_steps
+    dev = torch.device('cuda:0')
+    bf = torch.bfloat16
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.time()
+    with ThreadPoolExecutor(nthreads()) as ex:
+        host = list(ex.map(lambda s: gi.decode_step(c['seed'], s, N, H, d, d), range(1, steps + 1)))
+    stack = lambda f, dt: torch.from_numpy(np.stack([getattr(h, f) for h in host])).to(dev).to(dt)
+    q, k, v, b, w = (stack(f, bf) for f in ('q', 'k', 'v', 'b', 'w'))
+    la = stack('log_alpha', torch.float32)
+    S_np = gi.decode_state(c['seed'], N, H, d, d, c['s0_std'])
+    S = torch.from_numpy(S_np).to(dev)
+    o = torch.empty(N, H, d, device=dev)
+    log(f'[bench] generated {steps} decode steps in {time.time() - t0:.1f}s')
+    step = lambda s: gdn2.decode_step(q[s], k[s], v[s], la[s], b[s], w[s], S, out=o)
+    for s in range(min(10, steps)):
+        step(s)
+    torch.cuda.synchronize()
+    gdn2.profile_begin(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = gdn2.profile_end()
+    n, tot = prof['gdn2_decode']
+    avg = tot / n
+    per_chain = 2 * d * d * 4 + (3 * d + 2 * d) * 2 + d * 4 + d * 4   # S r+w, q k b v w, log alpha, o
+    res = {'metric': 'decode steps/s', 'value': steps / (t1 - t0), 'unit': 'steps/s',
+           'steps': steps, 'ms_per_step': round((t1 - t0) * 1e3 / steps, 5),
+           'config': {'workload': name, 'N': N, 'H': H, 'dk': d, 'dv': d,
+                      'state': 'fp32 [N,H,dk,dv] resident, updated in place', 'inputs': 'bf16, fresh per step'},
+           'roofline': roofline('gdn2_decode', per_chain * N * H, avg, name)}
+    log(f'[bench] decode {res["ms_per_step"]} ms/step, kernel {avg * 1e3:.1f} us')
+    if not args.no_cpu_baseline:
+        import oracle
+        ns = args.cpu_decode_steps
+        nt = nthreads()
+        S_c = S_np
+        t0 = time.perf_counter()
+        for s in range(ns):
+            h = host[s]
+            _, S_c = oracle.decode_step(h.q, h.k, h.v, h.log_alpha, h.b, h.w, S_c, nthreads=nt)
+        dt = time.perf_counter() - t0
+        res['cpu_baseline'] = {'value': round(ns / dt, 3), 'unit': 'steps/s', 'cores': nt, 'kind': 'oracle',
+                               'sample': f'{ns} of {steps} steps over all {N * H} chains, fp64; {dt:.1f}s'}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument('--gpus', type=int, default=1)
+    ap.add_argument('--steps', type=int, default=20)
+    ap.add_argument('--warmup', type=int, default=3)
+    ap.add_argument('--decode-steps', type=int, default=1000)
+    ap.add_argument('--cpu-sample-tokens', type=int, default=16384)
+    ap.add_argument('--cpu-decode-steps', type=int, default=10)
+    ap.add_argument('--no-cpu-baseline', action='store_true')
+    ap.add_argument('--no-decode', action='store_true')
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f'bench.py measures one GPU only: the mixer is benchmarked on one MI355X '
+              f'(--gpus {args.gpus} is not supported)', file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_wy_amd as gdn2
+    import gdn2_inputs as gi
+
+    pre = bench_prefill(args, torch, gdn2, gi)
+    out = {
+        'metric': METRIC, 'value': round(pre['value'], 1), 'unit': 'tokens/s', 'n_gpus': 1,
+        'steps': args.steps, 'warmup': args.warmup, 'ms_per_step': pre['ms_per_step'],
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None, 'dtype': 'f16',
+        'data': 'synthetic',
+        'config': {'workload': 'prefill_t65536', 'B': 1, 'T': 65536, 'H': 16, 'dk': 128, 'dv': 128,
+                   'chunk': 64, 'inputs': 'bf16 q,k,v,b,w; fp32 log_alpha; fp32 S0, S_T and o',
+                   'compute': 'f16 MFMA operands, fp32 accumulation and state'},
+        'roofline': pre['roofline'],
+    }
+    if 'cpu_baseline' in pre:
+        out['cpu_baseline'] = pre['cpu_baseline']
+    out['step_roofline'] = pre['step_roofline']
+    out['kernels_ms'] = pre['kernels_ms']
+    if 'parity_sample' in pre:
+        out['parity_sample'] = pre['parity_sample']
+    if not args.no_decode:
+        out['decode'] = bench_decode(args, torch, gdn2, gi)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == '__main__':
+    main()

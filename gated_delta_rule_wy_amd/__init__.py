@@ -1,0 +1,216 @@
+"""Gated DeltaNet-2 token mixer for MI355X (gfx950): Python binding of libgdn2.
+
+A thin ctypes layer over the C ABI in ``include/gdn2.h``: it checks tensor
+shapes, dtypes and devices, allocates outputs and workspace with PyTorch, sets
+the library's stream to PyTorch's current stream and calls the library. Every
+step of the computation runs in the HIP kernels; there is no other code path,
+and importing this package fails if the library has not been built.
+
+Recurrence (snilld.dk, "Hvad Gated DeltaNet-2 ændrer", update equation), per
+sequence and head, state S in R^{dk x dv}:
+    S_t = (I - k_t (b_t * k_t)^T) Diag(exp(log_alpha_t)) S_{t-1} + k_t (w_t * v_t)^T
+    o_t = S_t^T q_t
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, 'libgdn2.so')
+
+GDN2_OK, GDN2_ERR_INVALID, GDN2_ERR_UNSUPPORTED, GDN2_ERR_WORKSPACE, GDN2_ERR_HIP = range(5)
+GDN2_F32, GDN2_BF16 = 0, 1
+CHUNK = 64
+
+EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
+           'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_decode_step',
+           'gdn2_profile_begin', 'gdn2_profile_end', 'gdn2_profile_kernel')
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f'{where}: {status_string(status)}')
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f'{LIB_PATH} is missing: build it first (python -c "import __graft_entry__ as g; g.build()")')
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdn2_set_stream.argtypes = [vp]
+    lib.gdn2_set_stream.restype = i
+    lib.gdn2_get_stream.argtypes = []
+    lib.gdn2_get_stream.restype = vp
+    lib.gdn2_status_string.argtypes = [i]
+    lib.gdn2_status_string.restype = ctypes.c_char_p
+    lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [i] * 8
+    lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_fwd.argtypes = [vp] * 10 + [i] * 8 + [vp, sz]
+    lib.gdn2_chunk_fwd.restype = i
+    lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 6
+    lib.gdn2_decode_step.restype = i
+    lib.gdn2_profile_begin.argtypes = [i]
+    lib.gdn2_profile_begin.restype = i
+    lib.gdn2_profile_end.argtypes = []
+    lib.gdn2_profile_end.restype = i
+    lib.gdn2_profile_kernel.argtypes = [i, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.gdn2_profile_kernel.restype = i
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.gdn2_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN2_BF16
+    if t.dtype == torch.float32:
+        return GDN2_F32
+    raise TypeError(f'unsupported input dtype {t.dtype} (bfloat16 or float32)')
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f'{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}')
+    if t.dtype != dtype:
+        raise TypeError(f'{name}: expected {dtype}, got {t.dtype}')
+    if t.device != device:
+        raise ValueError(f'{name}: expected device {device}, got {t.device}')
+    if not t.is_contiguous():
+        raise ValueError(f'{name}: must be contiguous')
+
+
+def set_stream(stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Point the library at ``stream`` (default: PyTorch's current stream)."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    _lib.gdn2_set_stream(ctypes.c_void_p(s.cuda_stream))
+
+
+def workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, dtype: torch.dtype,
+                    varlen: bool) -> int:
+    code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
+    return int(_lib.gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen)))
+
+
+def profile_begin(max_calls: int) -> None:
+    """Time each kernel of this thread's next ``max_calls`` library calls with HIP events."""
+    st = _lib.gdn2_profile_begin(int(max_calls))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_profile_begin')
+
+
+def profile_end() -> dict:
+    """Stop recording; return {kernel name: (launches, total ms)} for the recorded calls."""
+    _lib.gdn2_profile_end()
+    out = {}
+    idx = 0
+    while True:
+        name, n, ms = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_double()
+        st = _lib.gdn2_profile_kernel(idx, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms))
+        if st == GDN2_ERR_INVALID:
+            break
+        if st != GDN2_OK:
+            raise Gdn2Error(st, 'gdn2_profile_kernel')
+        out[name.value.decode()] = (n.value, ms.value)
+        idx += 1
+    return out
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+              b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill. q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (bf16 or
+    fp32); log_alpha: [B, T, H, dk] fp32. With ``cu_seqlens`` (int32 [N+1] on
+    the device) B must be 1 and the sequences are packed along T. S0: [N, H,
+    dk, dv] fp32 or None (zeros). Returns (o [B, T, H, dv] fp32, S_T [N, H, dk,
+    dv] fp32 or None)."""
+    if q.dim() != 4:
+        raise ValueError('q must be [B, T, H, dk]')
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (('q', q, dk), ('k', k, dk), ('b', b, dk), ('v', v, dv), ('w', w, dv)):
+        _check(t, name, (B, T, H, d), dt, dev)
+    _check(log_alpha, 'log_alpha', (B, T, H, dk), torch.float32, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+            raise ValueError('cu_seqlens must be a 1-D int32 tensor on the same device')
+        if not cu_seqlens.is_contiguous():
+            raise ValueError('cu_seqlens must be contiguous')
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _check(S0, 'S0', (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(out, 'out', (B, T, H, dv), torch.float32, dev)
+    ST = None
+    if final_state is not None:
+        _check(final_state, 'final_state', (N, H, dk, dv), torch.float32, dev)
+        ST = final_state
+    elif output_final_state:
+        ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    varlen = cu_seqlens is not None
+    need = _lib.gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen))
+    if need == 0:
+        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, 'gdn2_chunk_fwd_workspace_bytes')
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    set_stream()
+    st = _lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                             _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
+                             B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace),
+                             workspace.numel() * workspace.element_size())
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_chunk_fwd')
+    return out, ST
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                b: torch.Tensor, w: torch.Tensor, S: torch.Tensor, *,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence. q, k, b: [N, H, dk]; v, w: [N, H, dv]; log_alpha
+    [N, H, dk] fp32; S: [N, H, dk, dv] fp32, updated in place. Returns o [N, H, dv] fp32."""
+    if q.dim() != 3:
+        raise ValueError('q must be [N, H, dk]')
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (('q', q, dk), ('k', k, dk), ('b', b, dk), ('v', v, dv), ('w', w, dv)):
+        _check(t, name, (N, H, d), dt, dev)
+    _check(log_alpha, 'log_alpha', (N, H, dk), torch.float32, dev)
+    _check(S, 'S', (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(out, 'out', (N, H, dv), torch.float32, dev)
+    set_stream()
+    st = _lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                               _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_decode_step')
+    return out

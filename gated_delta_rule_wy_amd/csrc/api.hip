@@ -1,0 +1,224 @@
+// C ABI of libgdn2 (declared in include/gdn2.h): argument validation, the
+// per-thread stream, and dispatch to the kernels. Nothing is enqueued unless
+// every check passes.
+#include "../../include/gdn2.h"
+#include "gdn2_launch.hpp"
+
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+namespace {
+
+thread_local hipStream_t g_stream = nullptr;
+
+// Per-thread kernel timing state (gdn2_profile_*).
+struct Prof {
+    bool on = false;          // recording requested
+    bool active = false;      // the current call is being recorded
+    int max_calls = 0, calls = 0;
+    std::vector<hipEvent_t> ev;
+    size_t used = 0;
+    struct Rec { const char *name; size_t e0; };
+    std::vector<Rec> recs;
+    void release() {
+        for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+        ev.clear();
+        recs.clear();
+        used = 0;
+        calls = 0;
+        on = active = false;
+    }
+    // no destructor: events are left to the process teardown, whose order
+    // relative to the HIP runtime's is not defined
+};
+thread_local Prof g_prof;
+
+constexpr int kEventsPerCall = 6;   // at most three kernels per call
+
+// Marks the start of a library call: decides whether its kernels are timed.
+void prof_call()
+{
+    g_prof.active = g_prof.on && g_prof.calls < g_prof.max_calls;
+    if (g_prof.active) ++g_prof.calls;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+} // namespace
+
+namespace gdn2 {
+
+void prof_before(const char *kernel, hipStream_t st)
+{
+    if (!g_prof.active || g_prof.used + 2 > g_prof.ev.size()) return;
+    (void)hipEventRecord(g_prof.ev[g_prof.used], st);
+    g_prof.recs.push_back({kernel, g_prof.used});
+    g_prof.used += 1;
+}
+
+void prof_after(hipStream_t st)
+{
+    if (!g_prof.active || g_prof.recs.empty() || g_prof.recs.back().e0 + 1 != g_prof.used) return;
+    (void)hipEventRecord(g_prof.ev[g_prof.used], st);
+    g_prof.used += 1;
+}
+
+} // namespace gdn2
+
+extern "C" {
+
+int gdn2_profile_begin(int max_calls)
+{
+    if (max_calls < 1 || max_calls > 4096) return GDN2_ERR_INVALID;
+    g_prof.release();
+    g_prof.ev.resize((size_t)max_calls * kEventsPerCall);
+    for (size_t i = 0; i < g_prof.ev.size(); ++i) {
+        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+            g_prof.ev.resize(i);
+            g_prof.release();
+            return GDN2_ERR_HIP;
+        }
+    }
+    g_prof.max_calls = max_calls;
+    g_prof.on = true;
+    return GDN2_OK;
+}
+
+int gdn2_profile_end(void)
+{
+    g_prof.on = g_prof.active = false;
+    return g_prof.calls;
+}
+
+int gdn2_profile_kernel(int idx, const char **name, int *launches, double *total_ms)
+{
+    // distinct names in order of first launch
+    std::vector<const char *> names;
+    for (const auto &r : g_prof.recs) {
+        bool seen = false;
+        for (const char *n : names) seen = seen || strcmp(n, r.name) == 0;
+        if (!seen) names.push_back(r.name);
+    }
+    if (idx < 0 || idx >= (int)names.size()) return GDN2_ERR_INVALID;
+    int cnt = 0;
+    double tot = 0.0;
+    for (const auto &r : g_prof.recs) {
+        if (strcmp(r.name, names[idx]) != 0 || r.e0 + 1 >= g_prof.used) continue;
+        float ms = 0.f;
+        if (hipEventSynchronize(g_prof.ev[r.e0 + 1]) != hipSuccess) return GDN2_ERR_HIP;
+        if (hipEventElapsedTime(&ms, g_prof.ev[r.e0], g_prof.ev[r.e0 + 1]) != hipSuccess) return GDN2_ERR_HIP;
+        ++cnt;
+        tot += ms;
+    }
+    if (name) *name = names[idx];
+    if (launches) *launches = cnt;
+    if (total_ms) *total_ms = tot;
+    return GDN2_OK;
+}
+
+int gdn2_set_stream(void *hip_stream)
+{
+    g_stream = (hipStream_t)hip_stream;
+    return GDN2_OK;
+}
+
+void *gdn2_get_stream(void) { return (void *)g_stream; }
+
+const char *gdn2_status_string(int status)
+{
+    switch (status) {
+    case GDN2_OK: return "GDN2_OK";
+    case GDN2_ERR_INVALID: return "GDN2_ERR_INVALID: invalid argument";
+    case GDN2_ERR_UNSUPPORTED: return "GDN2_ERR_UNSUPPORTED: sizes or dtypes not supported";
+    case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE: workspace missing or too small";
+    case GDN2_ERR_HIP: return "GDN2_ERR_HIP: HIP runtime error";
+    }
+    return "GDN2: unknown status";
+}
+
+static int chunk_check(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype, int varlen,
+                       gdn2::ChunkPlan *plan)
+{
+    if (B <= 0 || T < 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
+    if (in_dtype != GDN2_F32 && in_dtype != GDN2_BF16) return GDN2_ERR_INVALID;
+    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID;
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > 0x7fffffffLL * 16LL) return GDN2_ERR_UNSUPPORTED;
+    if ((long long)B * T > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
+    if (H > 65535) return GDN2_ERR_UNSUPPORTED;   // grid y dimension
+    if (!gdn2::chunk_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, plan))
+        return GDN2_ERR_UNSUPPORTED;
+    return GDN2_OK;
+}
+
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
+                                      gdn2_dtype in_dtype, int varlen)
+{
+    gdn2::ChunkPlan plan;
+    if (chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan) != GDN2_OK) return 0;
+    return plan.total_bytes > 0 ? plan.total_bytes : 256;
+}
+
+int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const void *b, const void *w, const float *S0, void *o, float *ST,
+                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                   gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                   size_t workspace_bytes)
+{
+    gdn2::ChunkPlan plan;
+    const int varlen = cu_seqlens != nullptr;
+    int st = chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan);
+    if (st != GDN2_OK) return st;
+    if (out_dtype != GDN2_F32) return out_dtype == GDN2_BF16 ? GDN2_ERR_UNSUPPORTED : GDN2_ERR_INVALID;
+    const bool have_tokens = (long long)B * T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDN2_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, o, ST, cu_seqlens, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID;
+    if (!workspace || workspace_bytes < plan.total_bytes) return GDN2_ERR_WORKSPACE;
+
+    gdn2::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
+    a.log_alpha = log_alpha;
+    a.S0 = S0;
+    a.o = o;
+    a.ST = ST;
+    a.cu_seqlens = cu_seqlens;
+    a.B = B; a.T = T; a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = in_dtype == GDN2_BF16;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    prof_call();
+    if (gdn2::launch_chunk_fwd(a, plan, g_stream) != hipSuccess) return GDN2_ERR_HIP;
+    return GDN2_OK;
+}
+
+int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const void *b, const void *w, float *S, void *o, int N, int H, int dk,
+                     int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+{
+    if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
+    if (in_dtype != GDN2_F32 && in_dtype != GDN2_BF16) return GDN2_ERR_INVALID;
+    if (out_dtype != GDN2_F32) return out_dtype == GDN2_BF16 ? GDN2_ERR_UNSUPPORTED : GDN2_ERR_INVALID;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
+    if ((long long)N * H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S, o};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID;
+    gdn2::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
+    a.log_alpha = log_alpha;
+    a.S = S;
+    a.o = o;
+    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = in_dtype == GDN2_BF16;
+    prof_call();
+    if (gdn2::launch_decode(a, g_stream) != hipSuccess) return GDN2_ERR_HIP;
+    return GDN2_OK;
+}
+
+} // extern "C"

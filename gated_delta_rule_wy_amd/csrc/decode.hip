@@ -1,0 +1,137 @@
+// Fused single-token decode step of the Gated Delta Rule-2.
+//
+// For each (sequence, head) with state S [dk][dv] fp32 (rows = key channels),
+// one token (snilld.dk, "Hvad Gated DeltaNet-2 ændrer", update equation):
+//   S~ = Diag(alpha) S,  e = S~^T (b*k),  r = S~^T q,
+//   delta = w*v - e,     S_new = S~ + k delta^T,   o = S_new^T q = r + delta (k.q)
+// The last identity lets the readout come from the same pass that reads S,
+// so S is read from HBM once and written once (the step is bound by HBM
+// bandwidth: about 0.86 flop per byte).
+//
+// One workgroup per (sequence, head). Thread t owns 4 consecutive columns and
+// DK/ROWG rows of S, kept in registers between the reductions and the update.
+#include "gdn2_device.hpp"
+#include "gdn2_launch.hpp"
+
+namespace gdn2 {
+
+template <int DK, int DV> struct DecodeShape {
+    static constexpr int COLG = DV / 4;                                  // column groups
+    static constexpr int ROWG = (DK < 256 / COLG) ? DK : 256 / COLG;     // row groups
+    static constexpr int RPT = DK / ROWG;                                // rows per thread
+    static constexpr int NT = COLG * ROWG;                               // threads
+};
+
+template <typename In, int DK, int DV>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
+    const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
+    const float *__restrict__ la, const In *__restrict__ b, const In *__restrict__ w,
+    float *__restrict__ S, float *__restrict__ o)
+{
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int COLG = Sh::COLG, ROWG = Sh::ROWG, RPT = Sh::RPT, NT = Sh::NT;
+    const int nh = blockIdx.x;            // sequence * H + head
+    const int t = threadIdx.x;
+    const int cg = t % COLG, rg = t / COLG;
+
+    __shared__ float s_a[DK], s_bk[DK], s_q[DK], s_k[DK], s_u[DV];
+    __shared__ f4 s_e[ROWG][COLG], s_r[ROWG][COLG];
+    __shared__ float s_kq[NT / 64 > 0 ? NT / 64 : 1];
+
+    float *Sp = S + (size_t)nh * DK * DV;
+    f4 sv[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        sv[r] = *reinterpret_cast<const f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg);
+
+    float kq = 0.f;
+    for (int c = t; c < DK; c += NT) {
+        const size_t i = (size_t)nh * DK + c;
+        const float kc = Ld<In>::one(k + i), qc = Ld<In>::one(q + i);
+        s_a[c] = __expf(la[i]);
+        s_k[c] = kc;
+        s_q[c] = qc;
+        s_bk[c] = Ld<In>::one(b + i) * kc;
+        kq += kc * qc;
+    }
+    for (int j = t; j < DV; j += NT) {
+        const size_t i = (size_t)nh * DV + j;
+        s_u[j] = Ld<In>::one(w + i) * Ld<In>::one(v + i);
+    }
+    // k.q: wave reduction, then across waves
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
+    if ((t & 63) == 0) s_kq[t >> 6] = kq;
+    __syncthreads();
+
+    f4 e = f4zero(), rr = f4zero();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int c = rg + r * ROWG;
+        sv[r] = sv[r] * s_a[c];
+        e += sv[r] * s_bk[c];
+        rr += sv[r] * s_q[c];
+    }
+    s_e[rg][cg] = e;
+    s_r[rg][cg] = rr;
+    __syncthreads();
+
+    f4 E = f4zero(), R = f4zero();
+#pragma unroll
+    for (int g = 0; g < ROWG; ++g) { E += s_e[g][cg]; R += s_r[g][cg]; }
+    float KQ = 0.f;
+#pragma unroll
+    for (int i = 0; i < (NT / 64 > 0 ? NT / 64 : 1); ++i) KQ += s_kq[i];
+    f4 u = *reinterpret_cast<const f4 *>(&s_u[4 * cg]);
+    const f4 delta = u - E;
+    if (rg == 0)
+        *reinterpret_cast<f4 *>(o + (size_t)nh * DV + 4 * cg) = R + delta * KQ;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int c = rg + r * ROWG;
+        *reinterpret_cast<f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg) = sv[r] + delta * s_k[c];
+    }
+}
+
+template <typename In, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st)
+{
+    constexpr int NT = DecodeShape<DK, DV>::NT;
+    prof_before("gdn2_decode", st);
+    hipLaunchKernelGGL((decode_kernel<In, DK, DV>), dim3(a.N * a.H), dim3(NT), 0, st,
+                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
+                       (const In *)a.b, (const In *)a.w, a.S, (float *)a.o);
+    prof_after(st);
+    return hipGetLastError();
+}
+
+template <typename In, int DK>
+static hipError_t dispatch_dv(const DecodeArgs &a, hipStream_t st)
+{
+    switch (a.dv) {
+    case 16: return launch_decode_t<In, DK, 16>(a, st);
+    case 32: return launch_decode_t<In, DK, 32>(a, st);
+    case 64: return launch_decode_t<In, DK, 64>(a, st);
+    case 128: return launch_decode_t<In, DK, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename In>
+static hipError_t dispatch_dk(const DecodeArgs &a, hipStream_t st)
+{
+    switch (a.dk) {
+    case 16: return dispatch_dv<In, 16>(a, st);
+    case 32: return dispatch_dv<In, 32>(a, st);
+    case 64: return dispatch_dv<In, 64>(a, st);
+    case 128: return dispatch_dv<In, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st)
+{
+    return a.bf16 ? dispatch_dk<uint16_t>(a, st) : dispatch_dk<float>(a, st);
+}
+
+} // namespace gdn2

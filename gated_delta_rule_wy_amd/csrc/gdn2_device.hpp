@@ -1,0 +1,110 @@
+// Device-side helpers shared by the gdn2 kernels (gfx950 / CDNA4).
+//
+// MFMA fragment conventions used throughout (one 64-wide wavefront, lane
+// l = n + 16*g with n = l % 16 and g = l / 16):
+//  * D / accumulator tile 16x16 fp32: lane l holds rows 4g..4g+3 of column n.
+//  * A fragment of a 16 x KB block (rows m, contraction k): lane l = m + 16g
+//    holds KB/4 values A[m][kofs(g, i)], i = 0..KB/4-1.
+//  * B fragment of a KB x 16 block: lane l = n + 16g holds B[kofs(g, i)][n].
+//  kofs(g, i) = 16*(i/4) + 4g + (i%4). Any bijection works as long as A and B
+//  use the same one, because the hardware pairs A element i of lane m+16g
+//  with B element i of lane n+16g. This one makes the B fragment of a
+//  32-deep block equal to two stacked accumulator tiles, so a product can
+//  feed the next product without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int kofs(int g, int i) { return 16 * (i >> 2) + 4 * g + (i & 3); }
+
+// ---- input element loads (bf16 bit patterns or fp32) -----------------------
+__device__ __forceinline__ float bf16f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename In> struct Ld;
+template <> struct Ld<uint16_t> {
+    // two consecutive elements
+    static __device__ __forceinline__ f2 two(const uint16_t *p) {
+        uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        f2 r;
+        r[0] = __uint_as_float(u << 16);
+        r[1] = __uint_as_float(u & 0xFFFF0000u);
+        return r;
+    }
+    static __device__ __forceinline__ float one(const uint16_t *p) { return bf16f(*p); }
+};
+template <> struct Ld<float> {
+    static __device__ __forceinline__ f2 two(const float *p) { return *reinterpret_cast<const f2 *>(p); }
+    static __device__ __forceinline__ float one(const float *p) { return *p; }
+};
+
+// ---- matrix-core operand traits ---------------------------------------------
+// Op = _Float16: v_mfma_f32_16x16x32_f16, k-blocks of 32, 8 halves per lane.
+// Op = float:    four v_mfma_f32_16x16x4_f32, k-blocks of 16, 4 floats per lane.
+template <typename Op> struct Mma;
+
+template <> struct Mma<_Float16> {
+    static constexpr int KB = 32;
+    static constexpr int NE = 8;
+    typedef h8 frag;
+    static __device__ __forceinline__ f4 mma(const frag &a, const frag &b, f4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    // 16x16x16 product from fp32 values (lane holds A[m][4g+i], B[4g+i][n]).
+    static __device__ __forceinline__ f4 mma16(const f4 &a, const f4 &b, f4 c) {
+        h4 ah, bh;
+        for (int i = 0; i < 4; ++i) { ah[i] = (_Float16)a[i]; bh[i] = (_Float16)b[i]; }
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KB = 16;
+    static constexpr int NE = 4;
+    typedef f4 frag;
+    static __device__ __forceinline__ f4 mma(const frag &a, const frag &b, f4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f4 mma16(const f4 &a, const f4 &b, f4 c) { return mma(a, b, c); }
+};
+
+__device__ __forceinline__ f4 f4zero() { f4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// ---- chunk bookkeeping -------------------------------------------------------
+// Sequences are token ranges [cu[i], cu[i+1]); each is cut into 64-token
+// chunks starting at its first token; chunk ids are numbered sequence by
+// sequence (co[i] = first chunk id of sequence i). Uniform batches (no
+// cu_seqlens) use cu[i] = i*T and co[i] = i*ceil(T/64) computed in place.
+struct SeqMap {
+    const int32_t *cu;   // device [N+1] or null (uniform)
+    const int32_t *co;   // device [N+1] chunk offsets (varlen) or null
+    int N, T;            // T: tokens per sequence when uniform
+    __device__ __forceinline__ int tok0(int i) const { return cu ? cu[i] : i * T; }
+    __device__ __forceinline__ int tok1(int i) const { return cu ? cu[i + 1] : (i + 1) * T; }
+    __device__ __forceinline__ int chunk0(int i) const { return co ? co[i] : i * ((T + 63) >> 6); }
+    __device__ __forceinline__ int nchunks() const { return co ? co[N] : N * ((T + 63) >> 6); }
+    // sequence owning chunk id j (j < nchunks()): largest i with chunk0(i) <= j
+    __device__ __forceinline__ int seq_of(int j) const {
+        if (!co) return j / ((T + 63) >> 6);
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (co[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    }
+};
+
+} // namespace gdn2

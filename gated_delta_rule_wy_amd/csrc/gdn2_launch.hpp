@@ -1,0 +1,53 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *b, *w;
+    const float *log_alpha;
+    float *S;
+    void *o;
+    int N, H, dk, dv;
+    bool bf16;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v, *b, *w;
+    const float *log_alpha;
+    const float *S0;
+    void *o;
+    float *ST;
+    const int32_t *cu_seqlens;   // device, or null for uniform batches
+    int B, T, N, H, dk, dv;
+    bool bf16;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Workspace layout for one call (all offsets 256-byte aligned):
+//   [0, plan_bytes)            int32 chunk offsets co[N+1] (varlen only)
+//   [plan_bytes, ...)          per (chunk, head) operand blocks
+struct ChunkPlan {
+    int max_chunks;              // grid bound on chunk ids
+    size_t plan_bytes;           // bytes reserved for co[]
+    size_t block_bytes;          // bytes per (chunk, head) operand block
+    size_t total_bytes;
+};
+
+// Returns false when the sizes are not supported.
+bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p);
+
+// Optional per-kernel event timing (see gdn2_profile_begin): the launchers
+// bracket every kernel launch with these; they do nothing unless enabled.
+void prof_before(const char *kernel, hipStream_t st);
+void prof_after(hipStream_t st);
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_chunk_fwd(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st);
+
+} // namespace gdn2

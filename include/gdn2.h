@@ -1,0 +1,141 @@
+/*
+ * gdn2.h - C ABI of libgdn2, the MI355X (gfx950) Gated DeltaNet-2 token mixer.
+ *
+ * The operation (snilld.dk, "Gated DeltaNet-2 fra NVIDIA ...", section "Hvad
+ * Gated DeltaNet-2 ændrer", compact update equation), per sequence and head:
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = S_t^T q_t
+ *
+ * with state S in R^{dk x dv} (rows are key channels), channel-wise decay
+ * alpha_t = exp(log_alpha_t) in (0, 1]^{dk} applied before the edit, erase
+ * gate b_t in [0, 1]^{dk} and write gate w_t in [0, 1]^{dv} (both already
+ * passed through their sigmoid), and readout after the update (aifetchly-
+ * blog.pages.dev, "Gated DeltaNet-2 Guide", layer workflow step 4). No query
+ * scale is applied. A missing initial state means zeros, and the final state
+ * is returned, as in that guide's "End-to-End PyTorch Implementation".
+ *
+ * Conventions for every entry point:
+ *  - All pointers are DEVICE pointers except where stated. The caller owns
+ *    every buffer; the library allocates no device memory and keeps no pointer
+ *    after a call returns.
+ *  - Layouts are dense row-major. Token tensors are [tokens, H, d], where
+ *    tokens = B*T (equal-length rows back to back) or the packed total.
+ *  - Work is enqueued on the calling thread's stream (gdn2_set_stream) and the
+ *    call returns without synchronising. Device-side faults surface at the
+ *    caller's next synchronisation, like any other stream work.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    non-OK status nothing has been launched. GDN2_ERR_HIP reports a launch
+ *    error from the HIP runtime.
+ *  - Preconditions that are not checked on the host: contiguity; finite
+ *    log_alpha <= 0; cu_seqlens starting at 0, non-decreasing and ending at T.
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN2_OK = 0,
+    GDN2_ERR_INVALID = 1,     /* null/misaligned pointer, bad size or dims    */
+    GDN2_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dims, dtype) */
+    GDN2_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+    GDN2_ERR_HIP = 4          /* the HIP runtime reported an error            */
+} gdn2_status;
+
+typedef enum {
+    GDN2_F32 = 0,
+    GDN2_BF16 = 1
+} gdn2_dtype;
+
+/* Set the HIP stream (a hipStream_t) used by this thread's later calls.
+ * NULL selects the default stream. Always returns GDN2_OK. */
+int gdn2_set_stream(void *hip_stream);
+
+/* The stream set by this thread (NULL = default stream). */
+void *gdn2_get_stream(void);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *gdn2_status_string(int status);
+
+/*
+ * Bytes of device workspace that gdn2_chunk_fwd needs for these sizes, or 0
+ * if the arguments are invalid or unsupported. `varlen` is 1 when the call
+ * will pass cu_seqlens (then B must be 1 and T is the total token count).
+ */
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
+                                      gdn2_dtype in_dtype, int varlen);
+
+/*
+ * Prefill forward over a batch, chunkwise (64-token chunks, WY form: the
+ * chunk's rank-one erase factors with the cumulative decay folded in are
+ * applied as one block per chunk, snilld.dk, section "Hvad betyder det for
+ * træning og inferens").
+ *
+ *   q, k, b    [tokens, H, dk]  in_dtype (GDN2_BF16 or GDN2_F32)
+ *   v, w       [tokens, H, dv]  in_dtype
+ *   log_alpha  [tokens, H, dk]  float, finite, <= 0
+ *   S0         [N, H, dk, dv]   float, or NULL for zeros
+ *   o          [tokens, H, dv]  out_dtype (GDN2_F32 only)
+ *   ST         [N, H, dk, dv]   float, or NULL; may alias S0
+ *   cu_seqlens [N + 1]          int32 device array, or NULL
+ *
+ * Without cu_seqlens the batch is B sequences of T tokens each and N must
+ * equal B. With cu_seqlens, B must be 1, T is the total token count and
+ * sequence i is tokens [cu_seqlens[i], cu_seqlens[i+1]); sequences may be
+ * empty (then ST[i] = S0[i]). Outputs must not alias the token inputs.
+ * Supported head dims: dk in {32, 64, 128} for bf16 inputs and
+ * {16, 32, 64, 128} for f32 inputs; dv in {16, 32, 64, 128}.
+ * workspace: device memory of at least gdn2_chunk_fwd_workspace_bytes(...).
+ */
+int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const void *b, const void *w, const float *S0, void *o, float *ST,
+                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                   gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                   size_t workspace_bytes);
+
+/*
+ * One recurrent decode step for N independent sequences (the same update
+ * and readout for a single token; constant-size state, aifetchly, "Gated
+ * DeltaNet-2 Guide", section "3. Chunkwise Parallel Algorithm ...": O(1)
+ * memory during token generation).
+ *
+ *   q, k, b    [N, H, dk]       in_dtype
+ *   v, w       [N, H, dv]       in_dtype
+ *   log_alpha  [N, H, dk]       float, finite, <= 0
+ *   S          [N, H, dk, dv]   float, read and updated in place
+ *   o          [N, H, dv]       out_dtype (GDN2_F32 only)
+ *
+ * dk, dv in {16, 32, 64, 128}. S is read once and written once.
+ */
+int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const void *b, const void *w, float *S, void *o, int N, int H, int dk,
+                     int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+
+/*
+ * Per-kernel timing, for measurement tools (not needed for computing).
+ * gdn2_profile_begin(max_calls) makes this thread's next gdn2_chunk_fwd /
+ * gdn2_decode_step calls (up to max_calls of them, 1..4096) record a HIP
+ * event before and after each kernel they launch, on the call's stream.
+ * Events are created here, on the current device. gdn2_profile_end() stops
+ * recording and returns the number of calls recorded (or a negative status).
+ * gdn2_profile_kernel(idx, ...) then reports, for the idx-th distinct kernel
+ * name in launch order, its launch count and summed duration in ms; it waits
+ * for the recorded events and returns GDN2_ERR_INVALID when idx is past the
+ * last kernel. `name` points to static storage.
+ */
+int gdn2_profile_begin(int max_calls);
+int gdn2_profile_end(void);
+int gdn2_profile_kernel(int idx, const char **name, int *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

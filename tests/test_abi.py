@@ -1,0 +1,142 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_wy_amd as gdn2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, 'include', 'gdn2.h')
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r'/\*.*?\*/', '', src, flags=re.S)
+    return sorted(set(re.findall(r'\b(gdn2_\w+)\s*\(', src)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(gdn2.EXPORTS)
+
+
+@pytest.mark.parametrize('name', declared_functions())
+def test_symbol_exported(name):
+    assert hasattr(gdn2.lib(), name), name
+    nm = os.popen(f'nm -D --defined-only {gdn2.LIB_PATH}').read()
+    assert re.search(rf'\bT {name}\b', nm), f'{name} is not a defined dynamic symbol'
+
+
+def test_status_strings():
+    for s in range(5):
+        assert gdn2.status_string(s).startswith('GDN2_')
+    assert 'unknown' in gdn2.status_string(99)
+
+
+def test_stream_is_per_thread_state():
+    lib = gdn2.lib()
+    assert lib.gdn2_set_stream(ctypes.c_void_p(0x1234)) == 0
+    assert lib.gdn2_get_stream() == 0x1234
+    import threading
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(lib.gdn2_get_stream()))
+    th.start(); th.join()
+    assert seen == [None]
+    lib.gdn2_set_stream(None)
+
+
+WS = gdn2.lib().gdn2_chunk_fwd_workspace_bytes
+
+
+def test_workspace_bytes():
+    # (B, T, N, H, dk, dv, dtype, varlen)
+    one = WS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0)
+    assert one > 0 and one % 256 == 0
+    assert WS(1, 65, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) == 2 * one
+    assert WS(4, 64, 4, 1, 128, 128, gdn2.GDN2_BF16, 0) == 4 * one
+    assert WS(1, 64, 1, 3, 128, 128, gdn2.GDN2_BF16, 0) == 3 * one
+    # varlen reserves the chunk-offset table and one extra chunk per sequence
+    assert WS(1, 64, 2, 1, 128, 128, gdn2.GDN2_BF16, 1) == 256 + 3 * one
+    assert WS(1, 4096, 1, 16, 128, 128, gdn2.GDN2_F32, 0) > WS(1, 4096, 1, 16, 128, 128, gdn2.GDN2_BF16, 0)
+    # invalid or unsupported sizes give 0
+    assert WS(0, 64, 0, 1, 128, 128, gdn2.GDN2_BF16, 0) == 0
+    assert WS(2, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) == 0      # N != B
+    assert WS(2, 64, 2, 1, 128, 128, gdn2.GDN2_BF16, 1) == 0      # varlen needs B == 1
+    assert WS(1, 64, 1, 1, 96, 128, gdn2.GDN2_BF16, 0) == 0       # dk not supported
+    assert WS(1, 64, 1, 1, 16, 128, gdn2.GDN2_BF16, 0) == 0       # bf16 needs dk >= 32
+    assert WS(1, 64, 1, 1, 16, 16, gdn2.GDN2_F32, 0) > 0
+    assert WS(1, 64, 1, 1, 128, 128, 7, 0) == 0                   # unknown dtype
+
+
+def _chunk(**kw):
+    P = 0x10000   # a fake, aligned, never-dereferenced address
+    a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S0=None, o=P, ST=P, cu=None, B=1, T=64, N=1, H=1,
+             dk=128, dv=128, dt=gdn2.GDN2_BF16, odt=gdn2.GDN2_F32, ws=P, wsb=1 << 30)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return gdn2.lib().gdn2_chunk_fwd(*(vp(a[x]) if a[x] else None for x in
+                                       ('q', 'k', 'v', 'la', 'b', 'w', 'S0', 'o', 'ST', 'cu')),
+                                     a['B'], a['T'], a['N'], a['H'], a['dk'], a['dv'], a['dt'], a['odt'],
+                                     vp(a['ws']) if a['ws'] else None, a['wsb'])
+
+
+@pytest.mark.parametrize('kw,status', [
+    (dict(q=None), gdn2.GDN2_ERR_INVALID),
+    (dict(la=None), gdn2.GDN2_ERR_INVALID),
+    (dict(o=None), gdn2.GDN2_ERR_INVALID),
+    (dict(k=0x10004), gdn2.GDN2_ERR_INVALID),            # misaligned
+    (dict(S0=0x10008), gdn2.GDN2_ERR_INVALID),
+    (dict(B=0), gdn2.GDN2_ERR_INVALID),
+    (dict(H=-1), gdn2.GDN2_ERR_INVALID),
+    (dict(T=-5), gdn2.GDN2_ERR_INVALID),
+    (dict(N=2), gdn2.GDN2_ERR_INVALID),                  # N != B without cu_seqlens
+    (dict(cu=0x20000, B=2, N=2), gdn2.GDN2_ERR_INVALID), # cu_seqlens needs B == 1
+    (dict(dt=5), gdn2.GDN2_ERR_INVALID),
+    (dict(odt=9), gdn2.GDN2_ERR_INVALID),
+    (dict(odt=gdn2.GDN2_BF16), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(dk=48), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(dv=256), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(dk=16), gdn2.GDN2_ERR_UNSUPPORTED),            # bf16 path needs dk >= 32
+    (dict(ws=None), gdn2.GDN2_ERR_WORKSPACE),
+    (dict(wsb=1024), gdn2.GDN2_ERR_WORKSPACE),
+])
+def test_chunk_fwd_rejects(kw, status):
+    assert _chunk(**kw) == status
+
+
+def _decode(**kw):
+    P = 0x10000
+    a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S=P, o=P, N=4, H=2, dk=128, dv=128,
+             dt=gdn2.GDN2_BF16, odt=gdn2.GDN2_F32)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return gdn2.lib().gdn2_decode_step(*(vp(a[x]) if a[x] else None for x in
+                                         ('q', 'k', 'v', 'la', 'b', 'w', 'S', 'o')),
+                                       a['N'], a['H'], a['dk'], a['dv'], a['dt'], a['odt'])
+
+
+@pytest.mark.parametrize('kw,status', [
+    (dict(S=None), gdn2.GDN2_ERR_INVALID),
+    (dict(o=None), gdn2.GDN2_ERR_INVALID),
+    (dict(v=0x10002), gdn2.GDN2_ERR_INVALID),
+    (dict(N=0), gdn2.GDN2_ERR_INVALID),
+    (dict(dk=100), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(dt=3), gdn2.GDN2_ERR_INVALID),
+    (dict(odt=gdn2.GDN2_BF16), gdn2.GDN2_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_python_binding_validates_before_calling():
+    import torch
+    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    la = torch.zeros(1, 64, 1, 128)
+    with pytest.raises(TypeError):
+        gdn2.chunk_fwd(x, x, x, la.to(torch.bfloat16), x, x)
+    with pytest.raises(ValueError):
+        gdn2.chunk_fwd(x, x[:, :32], x, la, x, x)
+    with pytest.raises(TypeError):
+        gdn2.chunk_fwd(x.half(), x.half(), x.half(), la, x.half(), x.half())

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Bars: fp32 inputs max-abs <= 1e-4; bf16 inputs max-abs
+<= 2e-2 x RMS of the reference, for o and for the final state."""
+import numpy as np
+import pytest
+
+import gdn2_inputs as gi
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip('torch')
+if not torch.cuda.is_available():
+    pytest.skip('no GPU', allow_module_level=True)
+
+import gated_delta_rule_wy_amd as gdn2  # noqa: E402
+import oracle  # noqa: E402
+from gpu_util import (DEV, assert_close, dev, oracle_prefill, run_prefill, tdtype,  # noqa: E402
+                      threads)
+
+
+def check_prefill(p, label, seqs=None, **kw):
+    print(f'[{label}] N={p.N} tokens={p.tokens} H={p.H} dk={p.dk} dv={p.dv} {p.dtype}', flush=True)
+    o, ST = run_prefill(p, **kw)
+    if seqs is None:
+        o_ref, ST_ref = oracle_prefill(p)
+        assert_close(o, o_ref, p.dtype, f'{label} o')
+        assert_close(ST, ST_ref, p.dtype, f'{label} S_T')
+    else:
+        ref = oracle_prefill(p, seqs)
+        for i in seqs:
+            s = slice(int(p.cu_seqlens[i]), int(p.cu_seqlens[i + 1]))
+            assert_close(o[s], ref[i][0], p.dtype, f'{label} seq {i} o')
+            assert_close(ST[i:i + 1], ref[i][1], p.dtype, f'{label} seq {i} S_T')
+    return o, ST
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_f32_workload():
+    """B=1, H=1, T=128, d=16, fp32 inputs (two chunks)."""
+    check_prefill(gi.workload('tiny'), 'tiny')
+
+
+@pytest.mark.parametrize('dk,dv', [(16, 16), (32, 64), (64, 32), (128, 128), (16, 128)])
+@pytest.mark.parametrize('T', [1, 63, 64, 65, 200])
+def test_f32_shapes(dk, dv, T):
+    p = gi.prefill(100 + T, [T, max(1, T // 2)], H=2, dk=dk, dv=dv, dtype='f32', s0_std=0.05, uniform=False)
+    check_prefill(p, f'f32 dk={dk} dv={dv} T={T}')
+
+
+@pytest.mark.parametrize('dk,dv', [(128, 128), (64, 64), (32, 32), (128, 64), (64, 128), (32, 16)])
+@pytest.mark.parametrize('T', [1, 63, 64, 65, 300])
+def test_bf16_shapes(dk, dv, T):
+    p = gi.prefill(200 + T, [T, T + 7, 1], H=3, dk=dk, dv=dv, dtype='bf16', s0_std=0.02, uniform=False)
+    check_prefill(p, f'bf16 dk={dk} dv={dv} T={T}')
+
+
+def test_bf16_uniform_batch_no_s0():
+    p = gi.prefill(300, [257] * 3, H=4, dk=128, dv=128, dtype='bf16', s0_std=0.0, uniform=True)
+    check_prefill(p, 'uniform B=3 T=257')
+
+
+def test_varlen_edges():
+    """Empty sequences keep S0; length-1 and 64-multiple lengths; several ragged tails."""
+    lens = [0, 1, 64, 0, 65, 128, 127, 3, 0]
+    for dt in ('bf16', 'f32'):
+        p = gi.prefill(400, lens, H=2, dk=128 if dt == 'bf16' else 32, dv=64, dtype=dt, s0_std=0.05,
+                       uniform=False)
+        o, ST = check_prefill(p, f'varlen edges {dt}')
+        for i, L in enumerate(lens):
+            if L == 0:
+                assert np.array_equal(ST[i], p.S0[i]), 'empty sequence must return S0 unchanged'
+
+
+@pytest.mark.parametrize('dt', ['bf16', 'f32'])
+def test_strong_decay(dt):
+    """log alpha = -5 per token: the chunk-cumulative decay reaches -320, which
+    takes the exact (pairwise-exponent) path for the diagonal blocks."""
+    p = gi.prefill(500, [200, 64, 37], H=2, dk=128 if dt == 'bf16' else 64, dv=64, dtype=dt,
+                   s0_std=0.02, uniform=False)
+    p.log_alpha[:] = -5.0
+    check_prefill(p, f'strong decay {dt}')
+
+
+def test_mixed_decay_rates():
+    """Strong decay in some channels and tokens only (mixes fast and exact blocks)."""
+    p = gi.prefill(501, [300], H=2, dk=128, dv=128, dtype='bf16', s0_std=0.02, uniform=False)
+    rng = np.random.default_rng(0)
+    mask = rng.random(p.log_alpha.shape) < 0.05
+    p.log_alpha[mask] = -8.0
+    check_prefill(p, 'mixed decay')
+
+
+@pytest.mark.parametrize('mode', ['accumulate', 'overwrite', 'erase', 'preserve'])
+def test_edit_modes(mode):
+    """The four editing modes: (b, w) in {0, 1} with unit keys."""
+    p = gi.prefill(600, [150], H=2, dk=128, dv=128, dtype='bf16', s0_std=0.05, uniform=False)
+    bval, wval = {'overwrite': (1, 1), 'erase': (1, 0), 'accumulate': (0, 1), 'preserve': (0, 0)}[mode]
+    p.b[:] = bval
+    p.w[:] = wval
+    if mode == 'preserve':
+        p.log_alpha[:] = 0.0
+    check_prefill(p, f'mode {mode}')
+
+
+# ------------------------------------------------------------------ consistency
+
+def test_deterministic_and_overwrites_outputs():
+    p = gi.prefill(700, [333, 100], H=4, dk=128, dv=128, dtype='bf16', s0_std=0.02, uniform=False)
+    T = p.tokens
+    o1 = torch.full((1, T, p.H, p.dv), float('nan'), device=DEV)
+    s1 = torch.full((p.N, p.H, p.dk, p.dv), float('nan'), device=DEV)
+    o1n, s1n = run_prefill(p, out=o1, final_state=s1)
+    o2n, s2n = run_prefill(p)
+    assert np.all(np.isfinite(o1n)) and np.all(np.isfinite(s1n))
+    assert np.array_equal(o1n, o2n) and np.array_equal(s1n, s2n), 'run-to-run results differ'
+
+
+def test_split_call_equals_one_call():
+    """State passing: [0, T) in one call equals [0, t) then [t, T) from its S_T."""
+    p = gi.prefill(800, [320], H=2, dk=64, dv=64, dtype='f32', s0_std=0.05, uniform=False)
+    o, ST = run_prefill(p)
+    t = 150
+    a = gi.Prefill(**{**p.__dict__})
+    for name in ('q', 'k', 'v', 'log_alpha', 'b', 'w'):
+        setattr(a, name, getattr(p, name)[:t])
+    a.cu_seqlens = np.array([0, t], np.int32)
+    o1, S1 = run_prefill(a)
+    c = gi.Prefill(**{**p.__dict__})
+    for name in ('q', 'k', 'v', 'log_alpha', 'b', 'w'):
+        setattr(c, name, getattr(p, name)[t:])
+    c.cu_seqlens = np.array([0, p.tokens - t], np.int32)
+    c.S0 = S1
+    o2, S2 = run_prefill(c)
+    assert np.max(np.abs(np.concatenate([o1, o2]) - o)) <= 1e-5
+    assert np.max(np.abs(S2 - ST)) <= 1e-5
+
+
+def test_decode_steps_equal_prefill():
+    """T decode steps through gdn2_decode_step equal one gdn2_chunk_fwd over T tokens."""
+    N, H, d, T = 3, 2, 64, 70
+    p = gi.prefill(900, [T] * N, H=H, dk=d, dv=d, dtype='f32', s0_std=0.05, uniform=True)
+    o_pre, ST_pre = run_prefill(p)
+    r = lambda x: x.reshape(N, T, H, -1)
+    S = dev(p.S0, torch.float32).clone()
+    for t in range(T):
+        args = [dev(r(x)[:, t], torch.float32) for x in (p.q, p.k, p.v, p.log_alpha, p.b, p.w)]
+        o_t = gdn2.decode_step(*args, S)
+        assert np.max(np.abs(o_t.cpu().numpy() - r(o_pre)[:, t])) <= 1e-4
+    assert np.max(np.abs(S.cpu().numpy() - ST_pre)) <= 1e-4
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize('dk,dv', [(16, 16), (32, 128), (128, 32), (64, 64), (128, 128)])
+@pytest.mark.parametrize('dt', ['f32', 'bf16'])
+def test_decode_shapes(dk, dv, dt):
+    N, H = 5, 3
+    S_np = gi.decode_state(11, N, H, dk, dv, s0_std=0.3)
+    S = dev(S_np, torch.float32)
+    for step in (1, 2):
+        st = gi.decode_step(11, step, N, H, dk, dv, dtype=dt)
+        o = gdn2.decode_step(*(dev(x, tdtype(dt)) for x in (st.q, st.k, st.v)),
+                             dev(st.log_alpha, torch.float32), dev(st.b, tdtype(dt)), dev(st.w, tdtype(dt)), S)
+        o_ref, S_np = oracle.decode_step(st.q, st.k, st.v, st.log_alpha, st.b, st.w, S_np)
+        assert_close(o.cpu().numpy(), o_ref, 'f32', f'decode {dt} dk={dk} dv={dv} step {step} o')
+        assert_close(S.cpu().numpy(), S_np, 'f32', f'decode {dt} dk={dk} dv={dv} step {step} S')
+
+
+def test_decode_workload_full_size():
+    """256 sequences x 16 heads x d=128, fp32 state resident, bf16 step inputs
+    (the decode workload's launch configuration), three consecutive steps."""
+    c = gi.WORKLOADS['decode_n256']
+    N, H, d = c['N'], c['H'], c['dk']
+    S_np = gi.decode_state(c['seed'], N, H, d, d, c['s0_std'])
+    S = dev(S_np, torch.float32)
+    for step in (1, 2, 3):
+        st = gi.decode_step(c['seed'], step, N, H, d, d)
+        bf = torch.bfloat16
+        o = gdn2.decode_step(dev(st.q, bf), dev(st.k, bf), dev(st.v, bf), dev(st.log_alpha, torch.float32),
+                             dev(st.b, bf), dev(st.w, bf), S)
+        o_ref, S_np = oracle.decode_step(st.q, st.k, st.v, st.log_alpha, st.b, st.w, S_np, nthreads=threads())
+        assert_close(o.cpu().numpy(), o_ref, 'f32', f'decode workload step {step} o')
+    assert_close(S.cpu().numpy(), S_np, 'f32', 'decode workload S after 3 steps')
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def test_prefill_b4_t4096_full():
+    """B=4, H=16, T=4096, d=128, bf16: every output against the oracle."""
+    check_prefill(gi.workload('prefill_b4_t4096', threads=threads()), 'prefill B=4 T=4096')
+
+
+def test_prefill_t65536_full():
+    """B=1, H=16, T=65536 (1024 chunks), d=128, bf16, S0 ~ N(0, 0.02): every output."""
+    check_prefill(gi.workload('prefill_t65536', threads=threads()), 'prefill T=65536')
+
+
+def test_varlen_32seq_full_sampled():
+    """32 packed sequences (lengths U[512, 16384]), H=32, half the heads with
+    scalar gates; the GPU runs the whole packed batch, the oracle checks a
+    sample of sequences (shortest, longest and two others) on all heads."""
+    p = gi.workload('varlen_32seq', threads=threads())
+    lens = np.diff(p.cu_seqlens)
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 17})
+    check_prefill(p, 'varlen 32 seqs', seqs=seqs)
