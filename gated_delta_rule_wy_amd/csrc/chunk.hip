@@ -451,6 +451,80 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Sequential state pass.
+//
+// Workgroup = (chain = sequence*H + head, 16-column slice of dv); wave w owns
+// rows 16w..16w+15 of each chunk's Delta and O, and state tiles
+// [w*TPW, (w+1)*TPW) (16 key channels each). Per chunk, two barriers:
+//   1: state operand tiles and U = w*v (hi + lo f16) ready in LDS
+//      Delta_w = T_w U - W_w S,  O_w = Q+_w S          (MFMA)
+//   2: Delta tiles ready in LDS
+//      O_w += P_w Delta,  S_tile = gamma * S_tile + Khat^T_tile Delta
+// The next chunk's operand fragments and v/w tile are loaded into registers
+// while the current chunk computes.
+//
+// Workgroups are numbered so that the slices of one chain land on the same
+// XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), where they
+// share that XCD's L2 for the chain's operand blocks.
+template <typename Op, int DK> struct PassFrags {
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    static constexpr int TPW = (L::NCT + 3) / 4;
+    frag nW[L::NKB], Qp[L::NKB], Ti[L::NSB], Pm[L::NSB], Kh[TPW][L::NSB];
+    f4 gam[TPW];
+    __device__ __forceinline__ void load(const uint8_t *blk, int wv, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb) {
+            nW[kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
+            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int sb = 0; sb < L::NSB; ++sb) {
+            Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
+            Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int ct = wv * TPW + u;
+            if (ct < L::NCT) {
+                gam[u] = *reinterpret_cast<const f4 *>(blk + L::oG + (size_t)(16 * ct + 4 * (lane >> 4)) * 4);
+#pragma unroll
+                for (int sb = 0; sb < L::NSB; ++sb)
+                    Kh[u][sb] = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)(ct * L::NSB + sb) * 64 + lane) * 16);
+            }
+        }
+    }
+};
+
+// v and w for one chunk and column slice: thread t holds row t/4, columns
+// 4*(t%4)..+3 of both.
+template <typename In> struct UVTile {
+    In v[4], w[4];
+    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, bool ok) {
+        if (ok) {
+            if constexpr (sizeof(In) == 2) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
+                const uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
+                v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
+                w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
+            } else {
+                const f4 a = *reinterpret_cast<const f4 *>(vp + off);
+                const f4 b = *reinterpret_cast<const f4 *>(wp + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = (In)0; w[e] = (In)0; }
+        }
+    }
+};
+
+template <typename In> __device__ __forceinline__ float in2f(In x);
+template <> __device__ __forceinline__ float in2f<uint16_t>(uint16_t x) { return bf16f(x); }
+template <> __device__ __forceinline__ float in2f<float>(float x) { return x; }
+
 template <typename In, typename Op, int DK, int DV>
 __global__ __launch_bounds__(256) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
@@ -460,15 +534,26 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
+    using F = PassFrags<Op, DK>;
     constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
-    constexpr int TPW = (NCT + 3) / 4;       // state tiles per wave
+    constexpr int TPW = F::TPW;
     constexpr int TPK = KB / 16;              // accumulator tiles per k-block
+    constexpr int NSL = DV / 16;              // column slices
 
-    __shared__ __attribute__((aligned(16))) Op sS[NCT * 64 * 4];   // state tiles (operand copy)
-    __shared__ __attribute__((aligned(16))) Op sD[4 * 64 * 4];     // Delta tiles
+    __shared__ __attribute__((aligned(16))) Op sS[NCT * 64 * 4];        // state operand tiles
+    __shared__ __attribute__((aligned(16))) Op sD[4 * 64 * 4];          // Delta tiles
+    __shared__ __attribute__((aligned(16))) Op sU[2 * NSB * 64 * NE];   // U hi / lo B-fragments
 
-    const int i = blockIdx.x, h = blockIdx.y, js = blockIdx.z;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, m16 = lane & 15, g4 = lane >> 4;
+    // XCD-aware numbering: slices of chain c sit on XCD c % 8
+    const int Lid = blockIdx.x;
+    const int kq = Lid >> 3, js = kq % NSL;
+    const int chain = (kq / NSL) * 8 + (Lid & 7);
+    const int chains = sq.m.N * H;
+    if (chain >= chains) return;
+    const int i = chain / H, h = chain % H;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
     const int col = 16 * js + m16;
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
 
@@ -489,84 +574,89 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
 
     const int tb = sq.t0(i), te = sq.t1(i);
     const int cbeg = sq.m.chunk0(i);
+    const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
     const int sbmax = (16 * wv + 15) / KB;
-    for (int tok = tb, c = cbeg; tok < te && c < sq.max_chunks; tok += 64, ++c) {
+    // v / w tile coordinates of this thread
+    const int ur = t >> 2, uc = 4 * (t & 3);
+    const size_t uoff0 = (size_t)h * DV + 16 * js + uc;
+    // where this thread's 4 U values go in the B-fragment layout
+    const int usb = ur / KB, usl = ur % KB;
+    const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
+
+    auto blk_of = [&](int c) { return ops + ((size_t)(cbeg + c) * H + h) * L::bytes; };
+    auto uv_ok = [&](int c) { return tb + 64 * c + ur < te; };
+    auto uv_off = [&](int c) { return (size_t)(tb + 64 * c + ur) * H * DV + uoff0; };
+
+    F fa, fb;
+    UVTile<In> ua, ub;
+    if (nch > 0) {
+        fa.load(blk_of(0), wv, lane);
+        ua.load(v, w, uv_off(0), uv_ok(0));
+    }
+
+    auto step = [&](int c, F &cur, F &nxt, UVTile<In> &ucur, UVTile<In> &unxt) {
+        const int tok = tb + 64 * c;
         const int n = min(64, te - tok);
-        const uint8_t *blk = ops + ((size_t)c * H + h) * L::bytes;
-        frag nW[NKB], Qp[NKB], Ti[NSB], Pm[NSB], Kh[TPW][NSB];
-        f4 gam[TPW];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            nW[kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(wv * NKB + kb) * 64 + lane) * 16);
-            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wv * NKB + kb) * 64 + lane) * 16);
+        if (c + 1 < nch) {
+            nxt.load(blk_of(c + 1), wv, lane);
+            unxt.load(v, w, uv_off(c + 1), uv_ok(c + 1));
         }
+        // U = w * v as hi + lo operand-precision parts, into B-fragment order
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-            Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)(wv * NSB + sb) * 64 + lane) * 16);
-            Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)(wv * NSB + sb) * 64 + lane) * 16);
+        for (int e = 0; e < 4; ++e) {
+            const float uu = in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]);
+            const Op hi = (Op)uu;
+            const int ln = (uc + e) + 16 * ug;
+            sU[((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
+            sU[((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
         }
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int ct = wv * TPW + u;
-            gam[u] = f4zero();
-            if (ct < NCT) {
-                gam[u] = *reinterpret_cast<const f4 *>(blk + L::oG + (size_t)(16 * ct + 4 * g4) * 4);
-#pragma unroll
-                for (int sb = 0; sb < NSB; ++sb)
-                    Kh[u][sb] = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)(ct * NSB + sb) * 64 + lane) * 16);
-            }
-        }
-        // U = w * v for this column, split into two operand-precision terms
-        frag Uh[NSB], Ul[NSB];
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-            for (int i4 = 0; i4 < NE; ++i4) {
-                const int s = sb * KB + kofs(g4, i4);
-                float uu = 0.f;
-                if (sb <= sbmax && s < n) {
-                    const size_t off = ((size_t)(tok + s) * H + h) * DV + col;
-                    uu = Ld<In>::one(w + off) * Ld<In>::one(v + off);
-                }
-                const Op hi = (Op)uu;
-                Uh[sb][i4] = hi;
-                Ul[sb][i4] = (Op)(uu - (float)hi);
-            }
-        }
-        __syncthreads();   // state operand tiles ready
+        __syncthreads();   // (1) state tiles and U ready
 
         f4 acc = f4zero(), oacc = f4zero();
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             if (sb > sbmax) break;
-            acc = M::mma(Ti[sb], Uh[sb], acc);
-            acc = M::mma(Ti[sb], Ul[sb], acc);
+            const frag uh = *reinterpret_cast<const frag *>(&sU[((0 * NSB + sb) * 64 + lane) * NE]);
+            const frag ul = *reinterpret_cast<const frag *>(&sU[((1 * NSB + sb) * 64 + lane) * NE]);
+            acc = M::mma(cur.Ti[sb], uh, acc);
+            acc = M::mma(cur.Ti[sb], ul, acc);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             frag sbf;
 #pragma unroll
-            for (int p = 0; p < TPK; ++p)
+            for (int p = 0; p < TPK; ++p) {
+                typedef Op op4 __attribute__((ext_vector_type(4)));
+                const op4 x = *reinterpret_cast<const op4 *>(&sS[((kb * TPK + p) * 64 + lane) * 4]);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) sbf[4 * p + ii] = sS[((kb * TPK + p) * 64 + lane) * 4 + ii];
-            acc = M::mma(nW[kb], sbf, acc);
-            oacc = M::mma(Qp[kb], sbf, oacc);
+                for (int ii = 0; ii < 4; ++ii) sbf[4 * p + ii] = x[ii];
+            }
+            acc = M::mma(cur.nW[kb], sbf, acc);
+            oacc = M::mma(cur.Qp[kb], sbf, oacc);
         }
+        {
+            typedef Op op4 __attribute__((ext_vector_type(4)));
+            op4 x;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sD[(wv * 64 + lane) * 4 + ii] = (Op)acc[ii];
-        __syncthreads();   // Delta tiles ready
+            for (int ii = 0; ii < 4; ++ii) x[ii] = (Op)acc[ii];
+            *reinterpret_cast<op4 *>(&sD[(wv * 64 + lane) * 4]) = x;
+        }
+        __syncthreads();   // (2) Delta tiles ready
 
         frag Db[NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int p = 0; p < TPK; ++p)
+            for (int p = 0; p < TPK; ++p) {
+                typedef Op op4 __attribute__((ext_vector_type(4)));
+                const op4 x = *reinterpret_cast<const op4 *>(&sD[((sb * TPK + p) * 64 + lane) * 4]);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Db[sb][4 * p + ii] = sD[((sb * TPK + p) * 64 + lane) * 4 + ii];
+                for (int ii = 0; ii < 4; ++ii) Db[sb][4 * p + ii] = x[ii];
+            }
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             if (sb > sbmax) break;
-            oacc = M::mma(Pm[sb], Db[sb], oacc);
+            oacc = M::mma(cur.Pm[sb], Db[sb], oacc);
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -577,14 +667,23 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
         for (int u = 0; u < TPW; ++u) {
             const int ct = wv * TPW + u;
             if (ct >= NCT) continue;
-            f4 s = Sr[u] * gam[u];
+            f4 s = Sr[u] * cur.gam[u];
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) s = M::mma(Kh[u][sb], Db[sb], s);
+            for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[sb], s);
             Sr[u] = s;
+            typedef Op op4 __attribute__((ext_vector_type(4)));
+            op4 x;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sS[(ct * 64 + lane) * 4 + ii] = (Op)s[ii];
+            for (int ii = 0; ii < 4; ++ii) x[ii] = (Op)s[ii];
+            *reinterpret_cast<op4 *>(&sS[(ct * 64 + lane) * 4]) = x;
         }
+    };
+
+    for (int c = 0; c < nch; c += 2) {
+        step(c, fa, fb, ua, ub);
+        if (c + 1 < nch) step(c + 1, fb, fa, ub, ua);
     }
+
     if (ST) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
@@ -651,7 +750,10 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     prof_before("gdn2_chunk_pass", st);
-    hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3(a.N, a.H, DV / 16), dim3(256), 0, st,
+    const long long chains = (long long)a.N * a.H;
+    const long long pass_grid = 8LL * (DV / 16) * ((chains + 7) / 8);
+    if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3((unsigned)pass_grid), dim3(256), 0, st,
                        (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
                        (const uint8_t *)ops);
     prof_after(st);
