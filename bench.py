@@ -209,6 +209,9 @@ def main():
     ap.add_argument('--cpu-decode-steps', type=int, default=10)
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--no-decode', action='store_true')
+    ap.add_argument('--copy-calibration-mib', type=int, default=0,
+                    help='only run a plain device copy of this many MiB (x3), to calibrate '
+                         'the FETCH_SIZE / WRITE_SIZE counters; prints nothing else')
     args = ap.parse_args()
     if args.gpus != 1:
         print(f'bench.py measures one GPU only: the mixer is benchmarked on one MI355X '
@@ -216,6 +219,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, device='cuda:0')
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f'[bench] copied {args.copy_calibration_mib} MiB x3')
+        return
 
     import gated_delta_rule_wy_amd as gdn2
     import gdn2_inputs as gi

@@ -35,6 +35,8 @@
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
+#include <type_traits>
+
 namespace gdn2 {
 
 // Operand block written by chunk_prep for one (chunk, head); every fragment
@@ -487,7 +489,7 @@ template <typename Op, int DK> struct PassFrags {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int ct = wv * TPW + u;
-            if (ct < L::NCT) {
+            if (L::NCT % 4 == 0 || ct < L::NCT) {   // static when all waves own tiles
                 gam[u] = *reinterpret_cast<const f4 *>(blk + L::oG + (size_t)(16 * ct + 4 * (lane >> 4)) * 4);
 #pragma unroll
                 for (int sb = 0; sb < L::NSB; ++sb)
@@ -501,23 +503,22 @@ template <typename Op, int DK> struct PassFrags {
 // 4*(t%4)..+3 of both.
 template <typename In> struct UVTile {
     In v[4], w[4];
+    // `off` always addresses a valid row; `ok` false zeroes the values after
+    // the load (no branch, so the load count per iteration stays fixed)
     __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, bool ok) {
-        if (ok) {
-            if constexpr (sizeof(In) == 2) {
-                const uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
-                const uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
-                v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
-                w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
-            } else {
-                const f4 a = *reinterpret_cast<const f4 *>(vp + off);
-                const f4 b = *reinterpret_cast<const f4 *>(wp + off);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
-            }
+        if constexpr (sizeof(In) == 2) {
+            uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
+            uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
+            v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
+            w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
         } else {
+            const f4 a = *reinterpret_cast<const f4 *>(vp + off);
+            const f4 b = *reinterpret_cast<const f4 *>(wp + off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] = (In)0; w[e] = (In)0; }
+            for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = ok ? v[e] : (In)0; w[e] = ok ? w[e] : (In)0; }
     }
 };
 
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
 
     auto blk_of = [&](int c) { return ops + ((size_t)(cbeg + c) * H + h) * L::bytes; };
     auto uv_ok = [&](int c) { return tb + 64 * c + ur < te; };
-    auto uv_off = [&](int c) { return (size_t)(tb + 64 * c + ur) * H * DV + uoff0; };
+    auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
 
     F fa, fb;
     UVTile<In> ua, ub;
@@ -594,13 +595,17 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
         ua.load(v, w, uv_off(0), uv_ok(0));
     }
 
-    auto step = [&](int c, F &cur, F &nxt, UVTile<In> &ucur, UVTile<In> &unxt) {
+    // One chunk. The next chunk's loads are issued unconditionally (the index
+    // is clamped, re-reading the last chunk at the end) so that the compiler
+    // can count them and only wait for the current chunk's data. LAST marks
+    // the final, possibly partial, chunk: only there are o stores guarded.
+    auto step = [&](auto last_tag, int c, F &cur, F &nxt, UVTile<In> &ucur, UVTile<In> &unxt) {
+        constexpr bool LAST = decltype(last_tag)::value;
         const int tok = tb + 64 * c;
         const int n = min(64, te - tok);
-        if (c + 1 < nch) {
-            nxt.load(blk_of(c + 1), wv, lane);
-            unxt.load(v, w, uv_off(c + 1), uv_ok(c + 1));
-        }
+        const int cn = min(c + 1, nch - 1);
+        nxt.load(blk_of(cn), wv, lane);
+        unxt.load(v, w, uv_off(cn), uv_ok(cn));
         // U = w * v as hi + lo operand-precision parts, into B-fragment order
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -661,12 +666,12 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int r = 16 * wv + 4 * g4 + ii;
-            if (r < n) o[((size_t)(tok + r) * H + h) * DV + col] = oacc[ii];
+            if (!LAST || r < n) o[((size_t)(tok + r) * H + h) * DV + col] = oacc[ii];
         }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int ct = wv * TPW + u;
-            if (ct >= NCT) continue;
+            if (NCT % 4 != 0 && ct >= NCT) continue;
             f4 s = Sr[u] * cur.gam[u];
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[sb], s);
@@ -679,9 +684,18 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
         }
     };
 
-    for (int c = 0; c < nch; c += 2) {
-        step(c, fa, fb, ua, ub);
-        if (c + 1 < nch) step(c + 1, fb, fa, ub, ua);
+    using NotLast = std::integral_constant<bool, false>;
+    using Last = std::integral_constant<bool, true>;
+    int c = 0;
+    for (; c + 2 < nch; c += 2) {
+        step(NotLast{}, c, fa, fb, ua, ub);
+        step(NotLast{}, c + 1, fb, fa, ub, ua);
+    }
+    if (c + 1 < nch) {
+        step(NotLast{}, c, fa, fb, ua, ub);
+        step(Last{}, c + 1, fb, fa, ub, ua);
+    } else if (c < nch) {
+        step(Last{}, c, fa, fb, ua, ub);
     }
 
     if (ST) {
