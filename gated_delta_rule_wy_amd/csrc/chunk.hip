@@ -25,13 +25,17 @@
 //    transition acts on the key axis only, which is what allows the slicing.
 //
 // Decay factoring. Exponent differences g_r - g_s (s <= r) are <= 0, but
-// the products above are formed as (row factor) x (column factor). Row block
-// R (rows 16R..16R+15) uses ref_R = g_{16R-1} (0 for R = 0):
-//   off-diagonal blocks S < R: e^{g_r - ref_R} * e^{ref_R - ref_{S+1}} * e^{ref_{S+1} - g_s},
-//   every factor <= 1, so nothing overflows whatever the decay;
-//   diagonal blocks: factors around the block's middle row, which are bounded
-//   by e^{LIM}; a block whose decay spread exceeds LIM is computed exactly
-//   (pairwise exponents) on the vector ALUs instead.
+// the products above are formed as (row factor) x (column factor).
+//  * When the chunk's decay spread is moderate (half spread <= Lim::chunk,
+//    every chunk of ordinary gating), all factors are taken around one
+//    per-channel midpoint and stay within e^{+-Lim::chunk}.
+//  * Otherwise row block R (rows 16R..16R+15) uses ref_R = g_{16R-1}
+//    (0 for R = 0): off-diagonal blocks S < R use
+//    e^{g_r - ref_R} * e^{ref_R - ref_{S+1}} * e^{ref_{S+1} - g_s}, every
+//    factor <= 1, so nothing overflows whatever the decay; diagonal blocks
+//    take factors around the block's middle row, bounded by e^{Lim::v}, and
+//    a block whose decay spread exceeds that is computed exactly (pairwise
+//    exponents) on the vector ALUs instead.
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
@@ -57,9 +61,11 @@ template <typename Op, int DK> struct Blk {
     static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
 };
 
+// Bounds on decay-factor exponents: `v` for the diagonal blocks of the
+// per-block factoring, `chunk` for the half spread of the chunk-wide one.
 template <typename Op> struct Lim;
-template <> struct Lim<_Float16> { static constexpr float v = 8.0f; };
-template <> struct Lim<float> { static constexpr float v = 60.0f; };
+template <> struct Lim<_Float16> { static constexpr float v = 8.0f, chunk = 6.0f; };
+template <> struct Lim<float> { static constexpr float v = 60.0f, chunk = 40.0f; };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -104,6 +110,16 @@ struct Seqs {
 };
 
 // ---------------------------------------------------------------------------
+// Chunk preparation, one workgroup (4 waves) per (chunk, head).
+//
+// Fast path (the chunk's decay spread is moderate): every exponent is taken
+// around one per-channel midpoint m = (g_first + g_last) / 2, so
+//   E^m_r = b_r k_r e^{g_r - m},  Q^m_r = q_r e^{g_r - m},  K^m_s = k_s e^{m - g_s}
+// are bounded by e^{LIMC} and A = E^m K^mT, P = Q^m K^mT need no per-tile
+// scaling. Otherwise the per-block factoring described at the top of the file
+// is used, with the exact pairwise path for diagonal blocks that need it.
+// All global loads are issued up front and unconditionally (rows past the
+// chunk's end are clamped and zeroed), so the wave waits once.
 template <typename In, typename Op, int DK>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ la,
@@ -112,21 +128,22 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
+    using raw2 = typename Ld<In>::raw2;
     constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
-    constexpr int PAD = 16 / (int)sizeof(Op);
-    constexpr int LDE = DK + PAD;               // row stride of the [64][DK] tiles
-    constexpr int LDT = 64 + PAD;               // row stride of the [64][64] tiles
+    constexpr int LDE = DK + 4;                 // row stride of the [64][DK] tiles
+    constexpr int LDT = 64 + 4;                 // row stride of the [64][64] tiles
     constexpr int REG = 64 * (LDE > LDT ? LDE : LDT);
     constexpr int LDA = 65;
     constexpr int CP = DK / 2, NRG = 256 / CP, RPG = 64 / NRG;
     constexpr float LIM = Lim<Op>::v;
+    constexpr float LIMC = Lim<Op>::chunk;
 
-    __shared__ __attribute__((aligned(16))) Op sE[REG];   // E^ ; later -W staging
-    __shared__ __attribute__((aligned(16))) Op sQ[REG];   // Q^ ; later P
-    __shared__ __attribute__((aligned(16))) Op sK[REG];   // K- ; later T
+    __shared__ __attribute__((aligned(16))) Op sE[REG];   // E-side operand; later -W staging
+    __shared__ __attribute__((aligned(16))) Op sQ[REG];   // Q-side operand; later P
+    __shared__ __attribute__((aligned(16))) Op sK[REG];   // K-side operand; later T
     __shared__ float sA[64 * LDA];                        // A (fp32); early: cumsum scratch
     __shared__ float sTab[19 * DK];
-    __shared__ int sFlag[4];
+    __shared__ int sFlag[5];                              // [0,4): exact diagonal blocks; [4]: slow chunk
 
     const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
@@ -136,32 +153,42 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int n = min(64, sq.t1(i) - t0);
     uint8_t *blk = ops + ((size_t)j * H + h) * L::bytes;
 
-    // tables: [0,4) e^{ref_R}  [4,8) e^{g_n - ref_{R+1}}  [8,11) e^{ref_R - ref_{S+1}}
-    //         for (R,S) = (2,0),(3,0),(3,1)   [11,15) e^{ref_R - mid_R}  [15,19) e^{mid_R - ref_{R+1}}
+    // tables (rows of DK floats): [0,4) Q+/E scale per row block; [4,8) Khat
+    // scale per row block; [8,11) e^{ref_R - ref_{S+1}} for (R,S) = (2,0),
+    // (3,0), (3,1); [11,15) e^{ref_R - mid_R}; [15,19) e^{mid_R - ref_{R+1}}.
+    // The fast path uses rows 0 and 4 for every block.
     float *tExpRef = sTab, *tExpKh = sTab + 4 * DK, *tDec = sTab + 8 * DK;
     float *tDiagE = sTab + 11 * DK, *tDiagK = sTab + 15 * DK;
 
-    // ---- stage 1: cumulative log-decay g (registers), block references ----
+    // ---- stage 1: all loads, cumulative log-decay g, references ----
     const int cp = t % CP, rg = t / CP, c0 = 2 * cp, r0 = rg * RPG;
     float *sPart = sA;                  // [NRG][DK]
     float *sRef = sA + NRG * DK;        // [5][DK]: ref_0..ref_4 (ref_4 = g_n)
     float *sMid = sRef + 5 * DK;        // [4][DK]
-    f2 al[RPG], gg[RPG];
+    float *sG0 = sMid + 4 * DK;         // [DK]: g at the chunk's first row
+    f2 gg[RPG];
+    raw2 kr[RPG], br[RPG], qr[RPG];
     {
-        f2 run = {0.f, 0.f};
+        f2 lv[RPG];
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
-            f2 x = {0.f, 0.f};
-            if (r < n) x = *reinterpret_cast<const f2 *>(la + ((size_t)(t0 + r) * H + h) * DK + c0);
-            al[u][0] = __expf(x[0]);
-            al[u][1] = __expf(x[1]);
-            run += x;
-            gg[u] = run;
+            const bool ok = r < n;
+            const size_t off = ((size_t)(t0 + min(r, n - 1)) * H + h) * DK + c0;
+            const f2 x = *reinterpret_cast<const f2 *>(la + off);
+            const raw2 kk = Ld<In>::ldraw2(k + off), bb = Ld<In>::ldraw2(b + off), qq = Ld<In>::ldraw2(q + off);
+            const f2 z = {0.f, 0.f};
+            lv[u] = ok ? x : z;
+            kr[u] = ok ? kk : Ld<In>::zero2();
+            br[u] = ok ? bb : Ld<In>::zero2();
+            qr[u] = ok ? qq : Ld<In>::zero2();
         }
+        f2 run = {0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) { run += lv[u]; gg[u] = run; }
         *reinterpret_cast<f2 *>(sPart + rg * DK + c0) = run;
     }
-    if (t < 4) sFlag[t] = 0;
+    if (t < 5) sFlag[t] = 0;
     __syncthreads();
     {
         f2 pre = {0.f, 0.f};
@@ -172,37 +199,66 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             const int r = r0 + u;
             if ((r & 15) == 15) *reinterpret_cast<f2 *>(sRef + ((r + 1) >> 4) * DK + c0) = gg[u];
             if ((r & 15) == 7) *reinterpret_cast<f2 *>(sMid + (r >> 4) * DK + c0) = gg[u];
+            if (r == 0) *reinterpret_cast<f2 *>(sG0 + c0) = gg[u];
         }
         if (rg == 0) { sRef[c0] = 0.f; sRef[c0 + 1] = 0.f; }
     }
     __syncthreads();
+    for (int c = t; c < DK; c += 256)
+        if (0.5f * (sG0[c] - sRef[4 * DK + c]) > LIMC) atomicOr(&sFlag[4], 1);
+    __syncthreads();
+    const bool fast = sFlag[4] == 0;
 
-    // ---- stage 2: factor tables, gamma, decay-scaled operands in LDS ----
-    for (int idx = t; idx < 4 * DK; idx += 256) {
-        const int R = idx / DK, c = idx % DK;
-        const float rR = sRef[R * DK + c], rR1 = sRef[(R + 1) * DK + c];
-        const float mid = sMid[R * DK + c], gn = sRef[4 * DK + c];
-        tExpRef[R * DK + c] = __expf(rR);
-        tExpKh[R * DK + c] = __expf(gn - rR1);
-        const float de = rR - mid, dq = mid - rR1;
-        tDiagE[R * DK + c] = __expf(de);
-        tDiagK[R * DK + c] = __expf(dq);
-        if (fmaxf(de, dq) > LIM) atomicOr(&sFlag[R], 1);
-        if (R < 3) {
-            const int Rr = R == 0 ? 2 : 3, Ss = R == 2 ? 1 : 0;
-            tDec[R * DK + c] = __expf(sRef[Rr * DK + c] - sRef[(Ss + 1) * DK + c]);
-        }
-    }
+    // ---- stage 2: decay factors, gamma, scaled operands in LDS ----
     if (t < DK) reinterpret_cast<float *>(blk + L::oG)[t] = __expf(sRef[4 * DK + t]);
-    {
-        // e1_r = e^{g_r - ref_R} forward, e2_r = e^{ref_{R+1} - g_r} backward,
-        // both as running products of alpha within the 16-row block.
-        f2 e1[RPG], e2[RPG];
+    if (fast) {
+        for (int c = t; c < DK; c += 256) {
+            const float gn = sRef[4 * DK + c], mid = 0.5f * (sG0[c] + gn);
+            tExpRef[c] = __expf(mid);
+            tExpKh[c] = __expf(gn - mid);
+        }
+        const f2 mid = 0.5f * (*reinterpret_cast<const f2 *>(sG0 + c0) + *reinterpret_cast<const f2 *>(sRef + 4 * DK + c0));
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
-            if ((r & 15) == 0) e1[u] = al[u];
-            else if (u == 0) {
+            f2 e1, e2;
+            e1[0] = __expf(gg[u][0] - mid[0]); e1[1] = __expf(gg[u][1] - mid[1]);
+            e2[0] = __expf(mid[0] - gg[u][0]); e2[1] = __expf(mid[1] - gg[u][1]);
+            const f2 kv = Ld<In>::cvt2(kr[u]), bv = Ld<In>::cvt2(br[u]), qv = Ld<In>::cvt2(qr[u]);
+            const f2 eh = bv * kv * e1, qh = qv * e1, kb_ = kv * e2;
+            sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
+            sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
+            sK[r * LDE + c0] = (Op)kb_[0]; sK[r * LDE + c0 + 1] = (Op)kb_[1];
+        }
+    } else {
+        for (int idx = t; idx < 4 * DK; idx += 256) {
+            const int R = idx / DK, c = idx % DK;
+            const float rR = sRef[R * DK + c], rR1 = sRef[(R + 1) * DK + c];
+            const float mid = sMid[R * DK + c], gn = sRef[4 * DK + c];
+            tExpRef[R * DK + c] = __expf(rR);
+            tExpKh[R * DK + c] = __expf(gn - rR1);
+            const float de = rR - mid, dq = mid - rR1;
+            tDiagE[R * DK + c] = __expf(de);
+            tDiagK[R * DK + c] = __expf(dq);
+            if (fmaxf(de, dq) > LIM) atomicOr(&sFlag[R], 1);
+            if (R < 3) {
+                const int Rr = R == 0 ? 2 : 3, Ss = R == 2 ? 1 : 0;
+                tDec[R * DK + c] = __expf(sRef[Rr * DK + c] - sRef[(Ss + 1) * DK + c]);
+            }
+        }
+        // e1_r = e^{g_r - ref_R} forward, e2_r = e^{ref_{R+1} - g_r} backward,
+        // as running products of alpha within the 16-row block
+        f2 al[RPG], e1[RPG], e2[RPG];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const f2 gprev = u ? gg[u - 1] : gg[0];
+            al[u][0] = __expf(u ? gg[u][0] - gprev[0] : 0.f);
+            al[u][1] = __expf(u ? gg[u][1] - gprev[1] : 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int r = r0 + u;
+            if (u == 0 || (r & 15) == 0) {
                 const float *ref = sRef + (r >> 4) * DK + c0;
                 e1[u][0] = __expf(gg[u][0] - ref[0]);
                 e1[u][1] = __expf(gg[u][1] - ref[1]);
@@ -221,13 +277,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
-            f2 kv = {0.f, 0.f}, bv = {0.f, 0.f}, qv = {0.f, 0.f};
-            if (r < n) {
-                const size_t off = ((size_t)(t0 + r) * H + h) * DK + c0;
-                kv = Ld<In>::two(k + off);
-                bv = Ld<In>::two(b + off);
-                qv = Ld<In>::two(q + off);
-            }
+            const f2 kv = Ld<In>::cvt2(kr[u]), bv = Ld<In>::cvt2(br[u]), qv = Ld<In>::cvt2(qr[u]);
             const f2 eh = bv * kv * e1[u], qh = qv * e1[u], kb_ = kv * e2[u];
             sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
             sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
@@ -235,70 +285,103 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         }
     }
     __syncthreads();
+    // Q+ / E scale of row block R, Khat scale of row block S
+    const int tabR = fast ? 0 : 1;   // table row step per block
 
     // ---- stage 3: A and P blocks on the matrix cores; pack Q+ and Khat^T ----
-    // zero the strictly-upper 16x16 blocks of A
-    for (int idx = t; idx < 6 * 256; idx += 256) {
+    for (int idx = t; idx < 6 * 256; idx += 256) {   // strictly-upper blocks of A
         const int bi = idx >> 8, e = idx & 255;
         const int R = bi < 3 ? 0 : (bi < 5 ? 1 : 2);
         const int S = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
         sA[(16 * R + (e >> 4)) * LDA + 16 * S + (e & 15)] = 0.f;
     }
-    const bool any_slow = sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3];
-    // wave wv takes jobs wv + 4*qq: ids 0..9 are the A blocks, 10..19 the P blocks
+    const bool any_slow = !fast && (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]);
     f4 pacc[5];
     int ptile[5];
-#pragma unroll
-    for (int qq = 0; qq < 5; ++qq) {
-        const int jb = wv + 4 * qq;
-        const int kind = jb / 10, tile = jb % 10;
-        const int R = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int S = tile - (R * (R + 1)) / 2;
-        ptile[qq] = -1;
-        pacc[qq] = f4zero();
-        if (R == S && sFlag[R]) continue;   // exact path below
+    if (fast) {
+        // waves 0,1 build A, waves 2,3 build P; wave parity picks the row
+        // blocks {0,3} or {1,2}, five 16x16 blocks each
+        const int kind = wv >> 1, par = wv & 1;
         const Op *src = kind ? sQ : sE;
-        f4 acc = f4zero();
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            frag a, bb;
+        for (int qq = 0; qq < 5; ++qq) {
+            const int R = par ? (qq < 2 ? 1 : 2) : (qq == 0 ? 0 : 3);
+            const int S = par ? (qq < 2 ? qq : qq - 2) : (qq == 0 ? 0 : qq - 1);
+            f4 acc = f4zero();
 #pragma unroll
-            for (int i4 = 0; i4 < NE; ++i4) {
-                const int ch = kb * KB + kofs(g4, i4);
-                float av = (float)src[(16 * R + m16) * LDE + ch];
-                float bvv = (float)sK[(16 * S + m16) * LDE + ch];
-                if (R == S) { av *= tDiagE[R * DK + ch]; bvv *= tDiagK[R * DK + ch]; }
-                else if (R > S + 1) bvv *= tDec[(R == 2 ? 0 : (S == 0 ? 1 : 2)) * DK + ch];
-                a[i4] = (Op)av;
-                bb[i4] = (Op)bvv;
-            }
-            acc = M::mma(a, bb, acc);
-        }
-        if (kind == 0) {
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = M::mma(lds_row_frag<Op>(src + (16 * R + m16) * LDE, kb * KB, g4),
+                             lds_row_frag<Op>(sK + (16 * S + m16) * LDE, kb * KB, g4), acc);
+            if (kind == 0) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int rr = 4 * g4 + ii;
-                sA[(16 * R + rr) * LDA + 16 * S + m16] = (R > S || rr > m16) ? acc[ii] : 0.f;
-            }
-        } else {
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    sA[(16 * R + rr) * LDA + 16 * S + m16] = (R > S || rr > m16) ? acc[ii] : 0.f;
+                }
+                ptile[qq] = -1;
+            } else {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int rr = 4 * g4 + ii;
-                acc[ii] = (R > S || rr >= m16) ? acc[ii] : 0.f;
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    acc[ii] = (R > S || rr >= m16) ? acc[ii] : 0.f;
+                }
+                ptile[qq] = (R * (R + 1)) / 2 + S;
             }
             pacc[qq] = acc;
-            ptile[qq] = tile;
+        }
+    } else {
+        // wave wv takes jobs wv + 4*qq: ids 0..9 are the A blocks, 10..19 the P blocks
+#pragma unroll
+        for (int qq = 0; qq < 5; ++qq) {
+            const int jb = wv + 4 * qq;
+            const int kind = jb / 10, tile = jb % 10;
+            const int R = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int S = tile - (R * (R + 1)) / 2;
+            ptile[qq] = -1;
+            pacc[qq] = f4zero();
+            if (R == S && sFlag[R]) continue;   // exact path below
+            const Op *src = kind ? sQ : sE;
+            f4 acc = f4zero();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                frag a, bb;
+#pragma unroll
+                for (int i4 = 0; i4 < NE; ++i4) {
+                    const int ch = kb * KB + kofs(g4, i4);
+                    float av = (float)src[(16 * R + m16) * LDE + ch];
+                    float bvv = (float)sK[(16 * S + m16) * LDE + ch];
+                    if (R == S) { av *= tDiagE[R * DK + ch]; bvv *= tDiagK[R * DK + ch]; }
+                    else if (R > S + 1) bvv *= tDec[(R == 2 ? 0 : (S == 0 ? 1 : 2)) * DK + ch];
+                    a[i4] = (Op)av;
+                    bb[i4] = (Op)bvv;
+                }
+                acc = M::mma(a, bb, acc);
+            }
+            if (kind == 0) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    sA[(16 * R + rr) * LDA + 16 * S + m16] = (R > S || rr > m16) ? acc[ii] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    acc[ii] = (R > S || rr >= m16) ? acc[ii] : 0.f;
+                }
+                pacc[qq] = acc;
+                ptile[qq] = tile;
+            }
         }
     }
-    // Q+ fragments: rows 16 mt + m, channels kb*KB + kofs; scaled by e^{ref_R}
+    // Q+ fragments: rows 16 mt + m, channels kb*KB + kofs, scaled to e^{g_r}
     for (int f = wv; f < 4 * NKB; f += 4) {
         const int mt = f / NKB, kb = f % NKB;
+        const frag x = lds_row_frag<Op>(sQ + (16 * mt + m16) * LDE, kb * KB, g4);
+        const float *sc = tExpRef + mt * tabR * DK + kb * KB;
         frag a;
 #pragma unroll
-        for (int i4 = 0; i4 < NE; ++i4) {
-            const int ch = kb * KB + kofs(g4, i4);
-            a[i4] = (Op)((float)sQ[(16 * mt + m16) * LDE + ch] * tExpRef[mt * DK + ch]);
-        }
+        for (int i4 = 0; i4 < NE; ++i4) a[i4] = (Op)((float)x[i4] * sc[kofs(g4, i4)]);
         *reinterpret_cast<frag *>(blk + L::oQ + ((size_t)f * 64 + lane) * 16) = a;
     }
     // Khat^T fragments: rows = channel 16 ct + m, contraction = chunk rows
@@ -309,7 +392,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int i4 = 0; i4 < NE; ++i4) {
             const int s = sb * KB + kofs(g4, i4);
-            a[i4] = (Op)((float)sK[s * LDE + c] * tExpKh[(s >> 4) * DK + c]);
+            a[i4] = (Op)((float)sK[s * LDE + c] * tExpKh[(s >> 4) * tabR * DK + c]);
         }
         *reinterpret_cast<frag *>(blk + L::oK + ((size_t)f * 64 + lane) * 16) = a;
     }
@@ -342,13 +425,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             const int r = 16 * R + rl, s = 16 * R + sl;
             float aA = 0.f, aP = 0.f;
             if (sl <= rl && r < n) {
-                const size_t br = ((size_t)(t0 + r) * H + h) * DK, bs = ((size_t)(t0 + s) * H + h) * DK;
+                const size_t br_ = ((size_t)(t0 + r) * H + h) * DK, bs = ((size_t)(t0 + s) * H + h) * DK;
                 for (int c = 0; c < DK; ++c) {
                     float d = 0.f;
                     for (int x = s + 1; x <= r; ++x) d += la[((size_t)(t0 + x) * H + h) * DK + c];
                     const float e = __expf(d) * Ld<In>::one(k + bs + c);
-                    aA += Ld<In>::one(b + br + c) * Ld<In>::one(k + br + c) * e;
-                    aP += Ld<In>::one(q + br + c) * e;
+                    aA += Ld<In>::one(b + br_ + c) * Ld<In>::one(k + br_ + c) * e;
+                    aP += Ld<In>::one(q + br_ + c) * e;
                 }
             }
             sA[r * LDA + s] = sl < rl ? aA : 0.f;
@@ -397,95 +480,111 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         __syncthreads();
     }
 
-    // ---- stage 6: W = T E (E_s = E^_s e^{ref_R(s)}); pack -W, P, T ----
-    constexpr int NWT = (4 * NCT + 3) / 4;
-    f4 wacc[NWT];
+    // ---- stage 6: W = T E (E = stored E-side operand x e^{ref}); pack -W, P, T ----
+    // wave wv takes output column tiles nt = wv, wv+4, ...; T fragments are
+    // shared across them, E column fragments across the row tiles
+    constexpr int NWT = (NCT + 3) / 4;
+    frag tf[4][NSB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+            if (sb <= (16 * mt + 15) / KB) tf[mt][sb] = lds_row_frag<Op>(sT + (16 * mt + m16) * LDT, sb * KB, g4);
+    f4 wacc[NWT][4];
 #pragma unroll
     for (int qq = 0; qq < NWT; ++qq) {
-        const int f = wv + 4 * qq;
-        wacc[qq] = f4zero();
-        if (f >= 4 * NCT) continue;
-        const int mt = f / NCT, nt = f % NCT;
-        const int sbmax = (16 * mt + 15) / KB;
-        for (int sb = 0; sb <= sbmax; ++sb) {
-            frag a, bb;
+        const int nt = wv + 4 * qq;
+        if (nt >= NCT) continue;
+        const int c = 16 * nt + m16;
+        frag eb[NSB];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
             for (int i4 = 0; i4 < NE; ++i4) {
                 const int s = sb * KB + kofs(g4, i4);
-                a[i4] = sT[(16 * mt + m16) * LDT + s];
-                const int c = 16 * nt + m16;
-                bb[i4] = (Op)((float)sE[s * LDE + c] * tExpRef[(s >> 4) * DK + c]);
+                eb[sb][i4] = (Op)((float)sE[s * LDE + c] * tExpRef[(s >> 4) * tabR * DK + c]);
             }
-            wacc[qq] = M::mma(a, bb, wacc[qq]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f4 acc = f4zero();
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+                if (sb <= (16 * mt + 15) / KB) acc = M::mma(tf[mt][sb], eb[sb], acc);
+            wacc[qq][mt] = acc;
         }
     }
     // P and T fragments
     for (int f = wv; f < 4 * NSB; f += 4) {
         const int mt = f / NSB, sb = f % NSB;
-        frag a, c;
-#pragma unroll
-        for (int i4 = 0; i4 < NE; ++i4) {
-            const int s = sb * KB + kofs(g4, i4);
-            a[i4] = sP[(16 * mt + m16) * LDT + s];
-            c[i4] = sT[(16 * mt + m16) * LDT + s];
-        }
-        *reinterpret_cast<frag *>(blk + L::oP + ((size_t)f * 64 + lane) * 16) = a;
-        *reinterpret_cast<frag *>(blk + L::oT + ((size_t)f * 64 + lane) * 16) = c;
+        *reinterpret_cast<frag *>(blk + L::oP + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sP + (16 * mt + m16) * LDT, sb * KB, g4);
+        *reinterpret_cast<frag *>(blk + L::oT + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sT + (16 * mt + m16) * LDT, sb * KB, g4);
     }
-    __syncthreads();   // every read of E^ done
+    __syncthreads();   // every read of the E-side operand done
 #pragma unroll
     for (int qq = 0; qq < NWT; ++qq) {
-        const int f = wv + 4 * qq;
-        if (f >= 4 * NCT) continue;
-        const int mt = f / NCT, nt = f % NCT;
+        const int nt = wv + 4 * qq;
+        if (nt >= NCT) continue;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            sW[(16 * mt + 4 * g4 + ii) * LDE + 16 * nt + m16] = (Op)(-wacc[qq][ii]);
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                sW[(16 * mt + 4 * g4 + ii) * LDE + 16 * nt + m16] = (Op)(-wacc[qq][mt][ii]);
     }
     __syncthreads();
     for (int f = wv; f < 4 * NKB; f += 4) {
         const int mt = f / NKB, kb = f % NKB;
-        frag a;
-#pragma unroll
-        for (int i4 = 0; i4 < NE; ++i4) a[i4] = sW[(16 * mt + m16) * LDE + kb * KB + kofs(g4, i4)];
-        *reinterpret_cast<frag *>(blk + L::oW + ((size_t)f * 64 + lane) * 16) = a;
+        *reinterpret_cast<frag *>(blk + L::oW + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sW + (16 * mt + m16) * LDE, kb * KB, g4);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Sequential state pass.
 //
-// Workgroup = (chain = sequence*H + head, 16-column slice of dv); wave w owns
-// rows 16w..16w+15 of each chunk's Delta and O, and state tiles
-// [w*TPW, (w+1)*TPW) (16 key channels each). Per chunk, two barriers:
-//   1: state operand tiles and U = w*v (hi + lo f16) ready in LDS
-//      Delta_w = T_w U - W_w S,  O_w = Q+_w S          (MFMA)
-//   2: Delta tiles ready in LDS
-//      O_w += P_w Delta,  S_tile = gamma * S_tile + Khat^T_tile Delta
-// The next chunk's operand fragments and v/w tile are loaded into registers
-// while the current chunk computes.
+// Workgroup = (chain = sequence*H + head, 16-column slice of dv), 8 waves in
+// two roles:
+//  * state waves 0..3 carry the recurrence. Wave w owns rows 16w..16w+15 of
+//    each chunk's Delta and state tiles [w*TPW, (w+1)*TPW) (16 key channels
+//    each), fp32 in registers:
+//        Delta_w = T_w U - W_w S;   S_tile <- gamma * S_tile + Khat^T_tile Delta
+//  * output waves 4..7 stage U = w*v (hi + lo f16) into LDS and compute
+//        O_w = Q+_w S + P_w Delta
+//    off the serial path.
+// Per chunk, two barriers: (1) state tiles and U in LDS, (2) Delta in LDS.
+// Each role loads its operand fragments two chunks ahead into a ring of
+// three register sets; the loads are unconditional (clamped chunk index) so
+// the compiler waits only for the chunk at hand. A compute unit streams
+// operand bytes at ~60 B/cycle, so the loads are placed where each role would
+// otherwise wait at a barrier: the state waves issue half after writing
+// Delta and half after the state update, the output waves right after
+// barrier (1). The output tile goes through LDS and leaves as one 16-byte
+// store per thread.
 //
 // Workgroups are numbered so that the slices of one chain land on the same
 // XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), where they
 // share that XCD's L2 for the chain's operand blocks.
-template <typename Op, int DK> struct PassFrags {
+template <typename Op, int DK> struct StateFrags {
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
     static constexpr int TPW = (L::NCT + 3) / 4;
-    frag nW[L::NKB], Qp[L::NKB], Ti[L::NSB], Pm[L::NSB], Kh[TPW][L::NSB];
+    frag nW[L::NKB], Ti[L::NSB], Kh[TPW][L::NSB];
     f4 gam[TPW];
-    __device__ __forceinline__ void load(const uint8_t *blk, int wv, int lane) {
+    // first half: what the Delta step needs (T fragments above the diagonal are zero and skipped)
+    __device__ __forceinline__ void load_a(const uint8_t *blk, int wv, int lane) {
 #pragma unroll
-        for (int kb = 0; kb < L::NKB; ++kb) {
+        for (int kb = 0; kb < L::NKB; ++kb)
             nW[kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
-            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
-        }
+        const int sbmax = (16 * wv + 15) / M::KB;
 #pragma unroll
-        for (int sb = 0; sb < L::NSB; ++sb) {
-            Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
-            Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
-        }
+        for (int sb = 0; sb < L::NSB; ++sb)
+            if (sb <= sbmax)
+                Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
+    }
+    // second half: what the state update needs
+    __device__ __forceinline__ void load_b(const uint8_t *blk, int wv, int lane) {
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int ct = wv * TPW + u;
@@ -499,8 +598,25 @@ template <typename Op, int DK> struct PassFrags {
     }
 };
 
-// v and w for one chunk and column slice: thread t holds row t/4, columns
-// 4*(t%4)..+3 of both.
+template <typename Op, int DK> struct OutFrags {
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    frag Qp[L::NKB], Pm[L::NSB];
+    __device__ __forceinline__ void load(const uint8_t *blk, int wo, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wo * L::NKB + kb) * 64 + lane) * 16);
+        const int sbmax = (16 * wo + 15) / M::KB;   // P is lower triangular
+#pragma unroll
+        for (int sb = 0; sb < L::NSB; ++sb)
+            if (sb <= sbmax)
+                Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)(wo * L::NSB + sb) * 64 + lane) * 16);
+    }
+};
+
+// v and w for one chunk and column slice: output-wave thread t (0..255)
+// holds row t/4, columns 4*(t%4)..+3 of both.
 template <typename In> struct UVTile {
     In v[4], w[4];
     // `off` always addresses a valid row; `ok` false zeroes the values after
@@ -526,8 +642,31 @@ template <typename In> __device__ __forceinline__ float in2f(In x);
 template <> __device__ __forceinline__ float in2f<uint16_t>(uint16_t x) { return bf16f(x); }
 template <> __device__ __forceinline__ float in2f<float>(float x) { return x; }
 
+template <typename Op> __device__ __forceinline__ typename Mma<Op>::frag lds_bfrag(const Op *base, int lane)
+{
+    // B fragment of a KB-deep block from KB/16 consecutive accumulator-layout tiles
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    typename Mma<Op>::frag f;
+#pragma unroll
+    for (int p = 0; p < Mma<Op>::KB / 16; ++p) {
+        const op4 x = *reinterpret_cast<const op4 *>(base + (p * 64 + lane) * 4);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) f[4 * p + ii] = x[ii];
+    }
+    return f;
+}
+
+template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, int lane, const f4 &x)
+{
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    op4 y;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) y[ii] = (Op)x[ii];
+    *reinterpret_cast<op4 *>(dst + lane * 4) = y;
+}
+
 template <typename In, typename Op, int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_pass_kernel(
+__global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
     const uint8_t *__restrict__ ops)
@@ -535,15 +674,18 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
-    using F = PassFrags<Op, DK>;
+    using SF = StateFrags<Op, DK>;
+    using OF = OutFrags<Op, DK>;
     constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
-    constexpr int TPW = F::TPW;
+    constexpr int TPW = SF::TPW;
     constexpr int TPK = KB / 16;              // accumulator tiles per k-block
     constexpr int NSL = DV / 16;              // column slices
 
     __shared__ __attribute__((aligned(16))) Op sS[NCT * 64 * 4];        // state operand tiles
     __shared__ __attribute__((aligned(16))) Op sD[4 * 64 * 4];          // Delta tiles
     __shared__ __attribute__((aligned(16))) Op sU[2 * NSB * 64 * NE];   // U hi / lo B-fragments
+    constexpr int LDO = 20;                                              // o staging row stride (floats)
+    __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];      // o tiles
 
     // XCD-aware numbering: slices of chain c sit on XCD c % 8
     const int Lid = blockIdx.x;
@@ -557,155 +699,146 @@ __global__ __launch_bounds__(256) void chunk_pass_kernel(
     const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
     const int col = 16 * js + m16;
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
-
-    f4 Sr[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int ct = wv * TPW + u;
-        Sr[u] = f4zero();
-        if (ct < NCT) {
-            if (S0) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Sr[u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col];
-            }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sS[(ct * 64 + lane) * 4 + ii] = (Op)Sr[u][ii];
-        }
-    }
-
     const int tb = sq.t0(i), te = sq.t1(i);
     const int cbeg = sq.m.chunk0(i);
     const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
-    const int sbmax = (16 * wv + 15) / KB;
-    // v / w tile coordinates of this thread
-    const int ur = t >> 2, uc = 4 * (t & 3);
-    const size_t uoff0 = (size_t)h * DV + 16 * js + uc;
-    // where this thread's 4 U values go in the B-fragment layout
-    const int usb = ur / KB, usl = ur % KB;
-    const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
+    auto blk_of = [&](int c) { return ops + ((size_t)(cbeg + min(c, nch - 1)) * H + h) * L::bytes; };
 
-    auto blk_of = [&](int c) { return ops + ((size_t)(cbeg + c) * H + h) * L::bytes; };
-    auto uv_ok = [&](int c) { return tb + 64 * c + ur < te; };
-    auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
-
-    F fa, fb;
-    UVTile<In> ua, ub;
-    if (nch > 0) {
-        fa.load(blk_of(0), wv, lane);
-        ua.load(v, w, uv_off(0), uv_ok(0));
-    }
-
-    // One chunk. The next chunk's loads are issued unconditionally (the index
-    // is clamped, re-reading the last chunk at the end) so that the compiler
-    // can count them and only wait for the current chunk's data. LAST marks
-    // the final, possibly partial, chunk: only there are o stores guarded.
-    auto step = [&](auto last_tag, int c, F &cur, F &nxt, UVTile<In> &ucur, UVTile<In> &unxt) {
-        constexpr bool LAST = decltype(last_tag)::value;
-        const int tok = tb + 64 * c;
-        const int n = min(64, te - tok);
-        const int cn = min(c + 1, nch - 1);
-        nxt.load(blk_of(cn), wv, lane);
-        unxt.load(v, w, uv_off(cn), uv_ok(cn));
-        // U = w * v as hi + lo operand-precision parts, into B-fragment order
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float uu = in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]);
-            const Op hi = (Op)uu;
-            const int ln = (uc + e) + 16 * ug;
-            sU[((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
-            sU[((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
-        }
-        __syncthreads();   // (1) state tiles and U ready
-
-        f4 acc = f4zero(), oacc = f4zero();
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-            if (sb > sbmax) break;
-            const frag uh = *reinterpret_cast<const frag *>(&sU[((0 * NSB + sb) * 64 + lane) * NE]);
-            const frag ul = *reinterpret_cast<const frag *>(&sU[((1 * NSB + sb) * 64 + lane) * NE]);
-            acc = M::mma(cur.Ti[sb], uh, acc);
-            acc = M::mma(cur.Ti[sb], ul, acc);
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            frag sbf;
-#pragma unroll
-            for (int p = 0; p < TPK; ++p) {
-                typedef Op op4 __attribute__((ext_vector_type(4)));
-                const op4 x = *reinterpret_cast<const op4 *>(&sS[((kb * TPK + p) * 64 + lane) * 4]);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) sbf[4 * p + ii] = x[ii];
-            }
-            acc = M::mma(cur.nW[kb], sbf, acc);
-            oacc = M::mma(cur.Qp[kb], sbf, oacc);
-        }
-        {
-            typedef Op op4 __attribute__((ext_vector_type(4)));
-            op4 x;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) x[ii] = (Op)acc[ii];
-            *reinterpret_cast<op4 *>(&sD[(wv * 64 + lane) * 4]) = x;
-        }
-        __syncthreads();   // (2) Delta tiles ready
-
-        frag Db[NSB];
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-            for (int p = 0; p < TPK; ++p) {
-                typedef Op op4 __attribute__((ext_vector_type(4)));
-                const op4 x = *reinterpret_cast<const op4 *>(&sD[((sb * TPK + p) * 64 + lane) * 4]);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Db[sb][4 * p + ii] = x[ii];
-            }
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-            if (sb > sbmax) break;
-            oacc = M::mma(cur.Pm[sb], Db[sb], oacc);
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int r = 16 * wv + 4 * g4 + ii;
-            if (!LAST || r < n) o[((size_t)(tok + r) * H + h) * DV + col] = oacc[ii];
-        }
+    if (wv < 4) {
+        // ------------------------------------------------ state waves
+        f4 Sr[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int ct = wv * TPW + u;
-            if (NCT % 4 != 0 && ct >= NCT) continue;
-            f4 s = Sr[u] * cur.gam[u];
+            Sr[u] = f4zero();
+            if (ct < NCT) {
+                if (S0) {
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[sb], s);
-            Sr[u] = s;
-            typedef Op op4 __attribute__((ext_vector_type(4)));
-            op4 x;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) x[ii] = (Op)s[ii];
-            *reinterpret_cast<op4 *>(&sS[(ct * 64 + lane) * 4]) = x;
+                    for (int ii = 0; ii < 4; ++ii)
+                        Sr[u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col];
+                }
+                lds_tile_store<Op>(sS + ct * 256, lane, Sr[u]);
+            }
         }
-    };
-
-    using NotLast = std::integral_constant<bool, false>;
-    using Last = std::integral_constant<bool, true>;
-    int c = 0;
-    for (; c + 2 < nch; c += 2) {
-        step(NotLast{}, c, fa, fb, ua, ub);
-        step(NotLast{}, c + 1, fb, fa, ub, ua);
-    }
-    if (c + 1 < nch) {
-        step(NotLast{}, c, fa, fb, ua, ub);
-        step(Last{}, c + 1, fb, fa, ub, ua);
-    } else if (c < nch) {
-        step(Last{}, c, fa, fb, ua, ub);
-    }
-
-    if (ST) {
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int ct = wv * TPW + u;
-            if (ct >= NCT) continue;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col] = Sr[u][ii];
+        const int sbmax = (16 * wv + 15) / KB;
+        SF f0, f1, f2;
+        if (nch > 0) {
+            f0.load_a(blk_of(0), wv, lane);
+            f0.load_b(blk_of(0), wv, lane);
+            f1.load_a(blk_of(1), wv, lane);
+            f1.load_b(blk_of(1), wv, lane);
         }
+        // The prefetch of chunk c+2 is split over the two windows in which
+        // the state waves would otherwise wait for the output waves.
+        auto step = [&](int c, SF &cur, SF &pre) {
+            __syncthreads();   // (1) state tiles and U ready
+            f4 acc = f4zero(), accw = f4zero();
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                if (sb > sbmax) break;
+                const frag uh = *reinterpret_cast<const frag *>(&sU[((0 * NSB + sb) * 64 + lane) * NE]);
+                const frag ul = *reinterpret_cast<const frag *>(&sU[((1 * NSB + sb) * 64 + lane) * NE]);
+                acc = M::mma(cur.Ti[sb], uh, acc);
+                acc = M::mma(cur.Ti[sb], ul, acc);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                accw = M::mma(cur.nW[kb], lds_bfrag<Op>(sS + kb * TPK * 256, lane), accw);
+            lds_tile_store<Op>(sD + wv * 256, lane, acc + accw);
+            pre.load_a(blk_of(c + 2), wv, lane);
+            __syncthreads();   // (2) Delta tiles ready
+            frag Db[NSB];
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) Db[sb] = lds_bfrag<Op>(sD + sb * TPK * 256, lane);
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (NCT % 4 != 0 && ct >= NCT) continue;
+                f4 s = Sr[u] * cur.gam[u];
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[sb], s);
+                Sr[u] = s;
+                lds_tile_store<Op>(sS + ct * 256, lane, s);
+            }
+            pre.load_b(blk_of(c + 2), wv, lane);
+        };
+        for (int c = 0; c < nch; c += 3) {
+            step(c, f0, f2);
+            if (c + 1 < nch) step(c + 1, f1, f0);
+            if (c + 2 < nch) step(c + 2, f2, f1);
+        }
+        __syncthreads();   // final: pairs with the output waves' last o tile
+        if (ST) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (ct >= NCT) continue;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col] = Sr[u][ii];
+            }
+        }
+    } else {
+        // ------------------------------------------------ output waves
+        const int wo = wv - 4, to = t - 256;
+        const int sbmax = (16 * wo + 15) / KB;
+        // v / w tile coordinates of this thread and where its U values go
+        const int ur = to >> 2, uc = 4 * (to & 3);
+        const size_t uoff0 = (size_t)h * DV + 16 * js + uc;
+        const int usb = ur / KB, usl = ur % KB;
+        const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
+        auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
+        auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
+        OF g0, g1, g2;
+        UVTile<In> u0, u1, u2;
+        if (nch > 0) {
+            g0.load(blk_of(0), wo, lane);
+            u0.load(v, w, uv_off(0), uv_ok(0));
+            g1.load(blk_of(1), wo, lane);
+            u1.load(v, w, uv_off(1), uv_ok(1));
+        }
+        // o tiles go through LDS (double-buffered) and leave as one 16-byte
+        // store per thread after the next barrier
+        auto store_o = [&](int c) {
+            const int tok = tb + 64 * c, n = min(64, te - tok);
+            const int row = to >> 2, q4 = to & 3;
+            if (row < n)
+                *reinterpret_cast<f4 *>(o + ((size_t)(tok + row) * H + h) * DV + 16 * js + 4 * q4) =
+                    *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
+        };
+        auto step = [&](int c, OF &cur, OF &pre, UVTile<In> &ucur, UVTile<In> &upre) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float uu = in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]);
+                const Op hi = (Op)uu;
+                const int ln = (uc + e) + 16 * ug;
+                sU[((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
+                sU[((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+            }
+            __syncthreads();   // (1)
+            pre.load(blk_of(c + 2), wo, lane);
+            upre.load(v, w, uv_off(c + 2), uv_ok(c + 2));
+            if (c > 0) store_o(c - 1);
+            f4 oacc = f4zero();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                oacc = M::mma(cur.Qp[kb], lds_bfrag<Op>(sS + kb * TPK * 256, lane), oacc);
+            __syncthreads();   // (2)
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                if (sb > sbmax) break;
+                oacc = M::mma(cur.Pm[sb], lds_bfrag<Op>(sD + sb * TPK * 256, lane), oacc);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + m16] = oacc[ii];
+        };
+        for (int c = 0; c < nch; c += 3) {
+            step(c, g0, g2, u0, u2);
+            if (c + 1 < nch) step(c + 1, g1, g0, u1, u0);
+            if (c + 2 < nch) step(c + 2, g2, g1, u2, u1);
+        }
+        __syncthreads();   // final
+        if (nch > 0) store_o(nch - 1);
     }
 }
 
@@ -767,7 +900,7 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     const long long chains = (long long)a.N * a.H;
     const long long pass_grid = 8LL * (DV / 16) * ((chains + 7) / 8);
     if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3((unsigned)pass_grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3((unsigned)pass_grid), dim3(512), 0, st,
                        (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
                        (const uint8_t *)ops);
     prof_after(st);

@@ -31,6 +31,16 @@ __device__ __forceinline__ float bf16f(uint16_t x) { return __uint_as_float((uin
 
 template <typename In> struct Ld;
 template <> struct Ld<uint16_t> {
+    // a pair of consecutive elements kept packed until use
+    typedef uint32_t raw2;
+    static __device__ __forceinline__ raw2 ldraw2(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+    static __device__ __forceinline__ f2 cvt2(raw2 u) {
+        f2 r;
+        r[0] = __uint_as_float(u << 16);
+        r[1] = __uint_as_float(u & 0xFFFF0000u);
+        return r;
+    }
+    static __device__ __forceinline__ raw2 zero2() { return 0u; }
     // two consecutive elements
     static __device__ __forceinline__ f2 two(const uint16_t *p) {
         uint32_t u = *reinterpret_cast<const uint32_t *>(p);
@@ -42,6 +52,10 @@ template <> struct Ld<uint16_t> {
     static __device__ __forceinline__ float one(const uint16_t *p) { return bf16f(*p); }
 };
 template <> struct Ld<float> {
+    typedef f2 raw2;
+    static __device__ __forceinline__ raw2 ldraw2(const float *p) { return *reinterpret_cast<const f2 *>(p); }
+    static __device__ __forceinline__ f2 cvt2(raw2 u) { return u; }
+    static __device__ __forceinline__ raw2 zero2() { f2 z = {0.f, 0.f}; return z; }
     static __device__ __forceinline__ f2 two(const float *p) { return *reinterpret_cast<const f2 *>(p); }
     static __device__ __forceinline__ float one(const float *p) { return *p; }
 };
@@ -81,6 +95,23 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ f4 f4zero() { f4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// Fragment whose contraction runs along a row of a row-major LDS tile:
+// element i is rowp[kbase + kofs(g, i)], read as NE/4 runs of 4 elements
+// (8-byte reads for f16, 16-byte for fp32; the caller keeps them aligned).
+template <typename Op>
+__device__ __forceinline__ typename Mma<Op>::frag lds_row_frag(const Op *rowp, int kbase, int g4)
+{
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    typename Mma<Op>::frag f;
+#pragma unroll
+    for (int p = 0; p < Mma<Op>::NE / 4; ++p) {
+        const op4 x = *reinterpret_cast<const op4 *>(rowp + kbase + 16 * p + 4 * g4);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) f[4 * p + ii] = x[ii];
+    }
+    return f;
+}
 
 // ---- chunk bookkeeping -------------------------------------------------------
 // Sequences are token ranges [cu[i], cu[i+1]); each is cut into 64-token
