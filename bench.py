@@ -205,8 +205,8 @@ def main():
     ap.add_argument('--steps', type=int, default=20)
     ap.add_argument('--warmup', type=int, default=3)
     ap.add_argument('--decode-steps', type=int, default=1000)
-    ap.add_argument('--cpu-sample-tokens', type=int, default=16384)
-    ap.add_argument('--cpu-decode-steps', type=int, default=10)
+    ap.add_argument('--cpu-sample-tokens', type=int, default=65536)
+    ap.add_argument('--cpu-decode-steps', type=int, default=100)
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--no-decode', action='store_true')
     ap.add_argument('--copy-calibration-mib', type=int, default=0,

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 namespace {
@@ -35,7 +36,20 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
-constexpr int kEventsPerCall = 6;   // at most three kernels per call
+// Events created up front per recorded call; the pool grows past this on
+// demand (a segmented prefill launches two kernels per segment), up to a cap.
+constexpr size_t kEventsPerCall = 64;
+constexpr size_t kMaxProfEvents = 1u << 17;
+
+bool prof_grow(size_t n)
+{
+    while (g_prof.ev.size() < n) {
+        hipEvent_t e = nullptr;
+        if (g_prof.ev.size() >= kMaxProfEvents || hipEventCreate(&e) != hipSuccess) return false;
+        g_prof.ev.push_back(e);
+    }
+    return true;
+}
 
 // Marks the start of a library call: decides whether its kernels are timed.
 void prof_call()
@@ -54,7 +68,7 @@ namespace gdn2 {
 
 void prof_before(const char *kernel, hipStream_t st)
 {
-    if (!g_prof.active || g_prof.used + 2 > g_prof.ev.size()) return;
+    if (!g_prof.active || !prof_grow(g_prof.used + 2)) return;
     (void)hipEventRecord(g_prof.ev[g_prof.used], st);
     g_prof.recs.push_back({kernel, g_prof.used});
     g_prof.used += 1;
@@ -75,13 +89,9 @@ int gdn2_profile_begin(int max_calls)
 {
     if (max_calls < 1 || max_calls > 4096) return GDN2_ERR_INVALID;
     g_prof.release();
-    g_prof.ev.resize((size_t)max_calls * kEventsPerCall);
-    for (size_t i = 0; i < g_prof.ev.size(); ++i) {
-        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-            g_prof.ev.resize(i);
-            g_prof.release();
-            return GDN2_ERR_HIP;
-        }
+    if (!prof_grow(std::min((size_t)max_calls * kEventsPerCall, kMaxProfEvents))) {
+        g_prof.release();
+        return GDN2_ERR_HIP;
     }
     g_prof.max_calls = max_calls;
     g_prof.on = true;

@@ -39,6 +39,9 @@
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
+#include <algorithm>
+#include <atomic>
+
 #include <type_traits>
 
 namespace gdn2 {
@@ -123,7 +126,7 @@ struct Seqs {
 template <typename In, typename Op, int DK>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ la,
-    const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops)
+    const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops, int *__restrict__ prog, int nprog)
 {
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
@@ -145,13 +148,19 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     __shared__ float sTab[19 * DK];
     __shared__ int sFlag[5];                              // [0,4): exact diagonal blocks; [4]: slow chunk
 
-    const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    // Chunks are dealt last to first, all heads of a chunk together, so the
+    // blocks the pass reads first are the ones written last (the most likely
+    // to still sit in the last-level cache).
+    const int t = threadIdx.x;
+    const int h = (int)(blockIdx.x % (unsigned)H), j = sq.max_chunks - 1 - (int)(blockIdx.x / (unsigned)H);
     const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    if (blockIdx.x == 0)
+        for (int x = t; x < nprog; x += 256) prog[x] = 0;
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
     const int i = sq.m.seq_of(j);
     const int t0 = sq.t0(i) + 64 * (j - sq.m.chunk0(i));
     const int n = min(64, sq.t1(i) - t0);
-    uint8_t *blk = ops + ((size_t)j * H + h) * L::bytes;
+    uint8_t *blk = ops + ((size_t)h * sq.max_chunks + j) * L::bytes;
 
     // tables (rows of DK floats): [0,4) Q+/E scale per row block; [4,8) Khat
     // scale per row block; [8,11) e^{ref_R - ref_{S+1}} for (R,S) = (2,0),
@@ -619,9 +628,13 @@ template <typename Op, int DK> struct OutFrags {
 // holds row t/4, columns 4*(t%4)..+3 of both.
 template <typename In> struct UVTile {
     In v[4], w[4];
-    // `off` always addresses a valid row; `ok` false zeroes the values after
-    // the load (no branch, so the load count per iteration stays fixed)
-    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, bool ok) {
+    bool ok;
+    // `off` always addresses a valid row; `ok` false stands for a row past
+    // the end and zeroes the product where it is used, not here: a select on
+    // the loaded values would make the wave wait for this load (and every
+    // load issued before it) at once.
+    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, bool ok_) {
+        ok = ok_;
         if constexpr (sizeof(In) == 2) {
             uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
             uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
@@ -633,8 +646,6 @@ template <typename In> struct UVTile {
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] = ok ? v[e] : (In)0; w[e] = ok ? w[e] : (In)0; }
     }
 };
 
@@ -665,11 +676,61 @@ template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, i
     *reinterpret_cast<op4 *>(dst + lane * 4) = y;
 }
 
+// L2 prefetch workgroups. A pass workgroup holds a bounded number of
+// cache-line requests in flight, so its step time grows with the latency of
+// the level its operands come from. When the chip has workgroup slots to
+// spare, each chain gets `npf` extra workgroups on the same XCD that read
+// the chain's upcoming operand blocks and v / w rows a few chunks ahead of
+// the pass, so that the pass finds them in that XCD's L2. They read the
+// chain's progress counter (chunks finished by its first slice) to stay
+// between 3 and 3 + kPfWindow chunks ahead; every wait is bounded, and the
+// results of the pass never depend on them.
+static constexpr int kPfWindow = 5;
+static constexpr int kPfMaxSleeps = 64;
+
+template <typename In, int DV, size_t BYTES>
+__device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
+                                              int chain, int h, int H, int pf, int npf, int nch, int tb, int te)
+{
+    constexpr int NL = (int)(BYTES / 128);                        // block lines
+    constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
+    constexpr int RL = (RB + 127) / 128;                          // lines per row
+    constexpr int PL = NL + 2 * 64 * RL;                          // lines per chunk
+    const int t = threadIdx.x;
+    uint32_t sink = 0;
+    for (int c = 0; c < nch; ++c) {
+        int done = 0;
+        for (int s = 0;; ++s) {
+            done = __builtin_amdgcn_readfirstlane(__hip_atomic_load(prog + chain, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT));
+            if (c <= done + 3 + kPfWindow || s >= kPfMaxSleeps) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        c = max(c, done + 3);
+        if (c >= nch) break;
+        const uint8_t *blk = blk0 + (size_t)c * BYTES;
+        for (int l = t * npf + pf; l < PL; l += npf * 512) {
+            const uint8_t *a;
+            if (l < NL) {
+                a = blk + (size_t)l * 128;
+            } else {
+                const int k = l - NL, which = k / (64 * RL), r = (k / RL) % 64, part = k % RL;
+                const int tok = min(tb + 64 * c + r, te - 1);
+                a = reinterpret_cast<const uint8_t *>(which ? w : v) + ((size_t)tok * H + h) * RB +
+                    min(part * 128, RB - 4);
+            }
+            sink ^= *reinterpret_cast<const uint32_t *>(a);
+        }
+    }
+    // keep the loads: the condition never holds for a launched grid
+    if (sink == 0x9e3779b9u && npf == 0) *const_cast<int *>(prog + chain) = (int)sink;
+}
+
 template <typename In, typename Op, int DK, int DV>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
-    const uint8_t *__restrict__ ops)
+    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf)
 {
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
@@ -680,6 +741,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     constexpr int TPW = SF::TPW;
     constexpr int TPK = KB / 16;              // accumulator tiles per k-block
     constexpr int NSL = DV / 16;              // column slices
+    constexpr int PD = 2;                     // prefetch distance (register ring of 3)
 
     __shared__ __attribute__((aligned(16))) Op sS[NCT * 64 * 4];        // state operand tiles
     __shared__ __attribute__((aligned(16))) Op sD[4 * 64 * 4];          // Delta tiles
@@ -687,10 +749,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     constexpr int LDO = 20;                                              // o staging row stride (floats)
     __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];      // o tiles
 
-    // XCD-aware numbering: slices of chain c sit on XCD c % 8
+    // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
+    // sit on XCD c % 8
     const int Lid = blockIdx.x;
-    const int kq = Lid >> 3, js = kq % NSL;
-    const int chain = (kq / NSL) * 8 + (Lid & 7);
+    const int kq = Lid >> 3, role = kq % (NSL + npf), js = role;
+    const int chain = (kq / (NSL + npf)) * 8 + (Lid & 7);
     const int chains = sq.m.N * H;
     if (chain >= chains) return;
     const int i = chain / H, h = chain % H;
@@ -702,7 +765,13 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const int tb = sq.t0(i), te = sq.t1(i);
     const int cbeg = sq.m.chunk0(i);
     const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
-    auto blk_of = [&](int c) { return ops + ((size_t)(cbeg + min(c, nch - 1)) * H + h) * L::bytes; };
+    auto blk_of = [&](int c) { return ops + ((size_t)h * sq.max_chunks + cbeg + min(c, nch - 1)) * L::bytes; };
+    if (role >= NSL) {
+        pass_prefetch<In, DV, L::bytes>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain, h,
+                                        H, role - NSL, npf, nch, tb, te);
+        return;
+    }
+    const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
 
     if (wv < 4) {
         // ------------------------------------------------ state waves
@@ -745,7 +814,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             for (int kb = 0; kb < NKB; ++kb)
                 accw = M::mma(cur.nW[kb], lds_bfrag<Op>(sS + kb * TPK * 256, lane), accw);
             lds_tile_store<Op>(sD + wv * 256, lane, acc + accw);
-            pre.load_a(blk_of(c + 2), wv, lane);
+            pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready
             frag Db[NSB];
 #pragma unroll
@@ -760,13 +829,24 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 Sr[u] = s;
                 lds_tile_store<Op>(sS + ct * 256, lane, s);
             }
-            pre.load_b(blk_of(c + 2), wv, lane);
+            pre.load_b(blk_of(c + PD), wv, lane);
+            // A device-scope store is written through to memory and, since
+            // stores and loads retire in order, would hold up this wave's
+            // later operand waits; the prefetch workgroups sit on the same
+            // XCD and read the counter from the shared L2.
+            if (report) __hip_atomic_store(prog + chain, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
-        for (int c = 0; c < nch; c += 3) {
+        // Full rounds of three steps carry no branches, so the register ring
+        // needs no merge copies (a copy of a register with a load in flight
+        // waits for that load and every load issued before it).
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
             step(c, f0, f2);
-            if (c + 1 < nch) step(c + 1, f1, f0);
-            if (c + 2 < nch) step(c + 2, f2, f1);
+            step(c + 1, f1, f0);
+            step(c + 2, f2, f1);
         }
+        if (c < nch) step(c, f0, f2);
+        if (c + 1 < nch) step(c + 1, f1, f0);
         __syncthreads();   // final: pairs with the output waves' last o tile
         if (ST) {
 #pragma unroll
@@ -809,15 +889,15 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         auto step = [&](int c, OF &cur, OF &pre, UVTile<In> &ucur, UVTile<In> &upre) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float uu = in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]);
+                const float uu = ucur.ok ? in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]) : 0.f;
                 const Op hi = (Op)uu;
                 const int ln = (uc + e) + 16 * ug;
                 sU[((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
                 sU[((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
             }
             __syncthreads();   // (1)
-            pre.load(blk_of(c + 2), wo, lane);
-            upre.load(v, w, uv_off(c + 2), uv_ok(c + 2));
+            pre.load(blk_of(c + PD), wo, lane);
+            upre.load(v, w, uv_off(c + PD), uv_ok(c + PD));
             if (c > 0) store_o(c - 1);
             f4 oacc = f4zero();
 #pragma unroll
@@ -832,11 +912,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + m16] = oacc[ii];
         };
-        for (int c = 0; c < nch; c += 3) {
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
             step(c, g0, g2, u0, u2);
-            if (c + 1 < nch) step(c + 1, g1, g0, u1, u0);
-            if (c + 2 < nch) step(c + 2, g2, g1, u2, u1);
+            step(c + 1, g1, g0, u1, u0);
+            step(c + 2, g2, g1, u2, u1);
         }
+        if (c < nch) step(c, g0, g2, u0, u2);
+        if (c + 1 < nch) step(c + 1, g1, g0, u1, u0);
         __syncthreads();   // final
         if (nch > 0) store_o(nch - 1);
     }
@@ -861,12 +944,34 @@ bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varl
     if (!bb) return false;
     const long long per = ((long long)T + 63) / 64;
     const long long mc = varlen ? per + N : per * B;
-    if (mc > 0x7fffffffLL) return false;
+    if (mc * H > 0x7fffffffLL) return false;
+    const long long chains = (long long)(varlen ? N : B) * H;
     p->max_chunks = (int)mc;
     p->plan_bytes = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
+    p->prog_bytes = ((size_t)chains * 4 + 255) / 256 * 256;
     p->block_bytes = bb;
-    p->total_bytes = p->plan_bytes + (size_t)mc * H * bb;
+    p->total_bytes = p->plan_bytes + p->prog_bytes + (size_t)mc * H * bb;
     return true;
+}
+
+static constexpr int kMaxPrefetchWgs = 6;
+
+// compute units of the current device, queried once per device
+static hipError_t device_cus(int *cus)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cached[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return hipSuccess;
 }
 
 template <typename In, typename Op, int DK, int DV>
@@ -888,21 +993,31 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    uint8_t *ops = ws + p.plan_bytes;
+    int *prog = (int *)(ws + p.plan_bytes);
+    uint8_t *ops = ws + p.plan_bytes + p.prog_bytes;
+    const long long chains = (long long)a.N * a.H;
     if (p.max_chunks > 0) {
         prof_before("gdn2_chunk_prep", st);
-        hipLaunchKernelGGL((chunk_prep_kernel<In, Op, DK>), dim3(p.max_chunks, a.H), dim3(256), 0, st,
-                           (const In *)a.q, (const In *)a.k, a.log_alpha, (const In *)a.b, sq, a.H, ops);
+        hipLaunchKernelGGL((chunk_prep_kernel<In, Op, DK>), dim3((unsigned)((long long)p.max_chunks * a.H)), dim3(256),
+                           0, st, (const In *)a.q, (const In *)a.k, a.log_alpha, (const In *)a.b, sq, a.H, ops,
+                           prog, (int)chains);
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    prof_before("gdn2_chunk_pass", st);
-    const long long chains = (long long)a.N * a.H;
-    const long long pass_grid = 8LL * (DV / 16) * ((chains + 7) / 8);
+    // prefetch workgroups only where the whole grid stays resident at one
+    // workgroup per compute unit
+    constexpr int NSL = DV / 16;
+    const long long groups = (chains + 7) / 8;
+    int cus = 0;
+    if ((err = device_cus(&cus)) != hipSuccess) return err;
+    int npf = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - NSL);
+    if (npf < 2 || p.max_chunks == 0) npf = 0;
+    const long long pass_grid = 8LL * (NSL + npf) * groups;
     if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    prof_before("gdn2_chunk_pass", st);
     hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3((unsigned)pass_grid), dim3(512), 0, st,
                        (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
-                       (const uint8_t *)ops);
+                       (const uint8_t *)ops, prog, npf);
     prof_after(st);
     return hipGetLastError();
 }

@@ -30,11 +30,14 @@ struct ChunkArgs {
 };
 
 // Workspace layout for one call (all offsets 256-byte aligned):
-//   [0, plan_bytes)            int32 chunk offsets co[N+1] (varlen only)
-//   [plan_bytes, ...)          per (chunk, head) operand blocks
+//   [0, plan_bytes)                      int32 chunk offsets co[N+1] (varlen only)
+//   [plan_bytes, +prog_bytes)            int32 per-chain progress of the pass
+//   [plan_bytes + prog_bytes, ...)       operand blocks, head-major:
+//                                        block (h, j) at (h * max_chunks + j)
 struct ChunkPlan {
     int max_chunks;              // grid bound on chunk ids
     size_t plan_bytes;           // bytes reserved for co[]
+    size_t prog_bytes;           // bytes reserved for the progress counters
     size_t block_bytes;          // bytes per (chunk, head) operand block
     size_t total_bytes;
 };

@@ -37,7 +37,7 @@ def run_prefill(p: gi.Prefill, S0=True, **kw):
     cu = dev(p.cu_seqlens, torch.int32) if p.varlen else None
     o, ST = gdn2.chunk_fwd(q, k, v, la, b, w, s0, cu, **kw)
     torch.cuda.synchronize()
-    return o.reshape(-1, p.H, p.dv).cpu().numpy(), ST.cpu().numpy()
+    return o.reshape(-1, p.H, p.dv).cpu().numpy(), None if ST is None else ST.cpu().numpy()
 
 
 def oracle_prefill(p: gi.Prefill, seqs=None):

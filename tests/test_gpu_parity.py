@@ -112,6 +112,22 @@ def test_edit_modes(mode):
     assert_close(ST, ST_ref, 'f32', 'mode erase S_T (absolute)')
 
 
+@pytest.mark.parametrize('dt,d,B,H,T', [('bf16', 128, 2, 1, 8401), ('f32', 64, 1, 2, 9000),
+                                         ('bf16', 64, 3, 2, 8192 + 129)])
+def test_long_uniform_few_chains(dt, d, B, H, T):
+    """Uniform batches with few chains and more than 128 chunks: the pass runs
+    with its L2 prefetch workgroups; ragged tail."""
+    p = gi.prefill(950 + T, [T] * B, H=H, dk=d, dv=d, dtype=dt, s0_std=0.05, uniform=True)
+    check_prefill(p, f'long uniform {dt} B={B} H={H} T={T}')
+
+
+def test_long_no_s0_no_final_state():
+    p = gi.prefill(990, [8500], H=1, dk=128, dv=128, dtype='bf16', s0_std=0.0, uniform=True)
+    o, _ = run_prefill(p, output_final_state=False)
+    o_ref, _ = oracle_prefill(p)
+    assert_close(o, o_ref, p.dtype, 'long no S0 o')
+
+
 # ------------------------------------------------------------------ consistency
 
 def test_deterministic_and_overwrites_outputs():
