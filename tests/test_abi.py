@@ -52,13 +52,16 @@ WS = gdn2.lib().gdn2_chunk_fwd_workspace_bytes
 
 def test_workspace_bytes():
     # (B, T, N, H, dk, dv, dtype, varlen)
-    one = WS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0)
+    # layout: [chunk offsets (varlen)] [progress counters, 4 B per chain]
+    # [operand blocks], each part rounded up to 256 bytes
+    one = WS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) - 256   # one (chunk, head) block
     assert one > 0 and one % 256 == 0
-    assert WS(1, 65, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) == 2 * one
-    assert WS(4, 64, 4, 1, 128, 128, gdn2.GDN2_BF16, 0) == 4 * one
-    assert WS(1, 64, 1, 3, 128, 128, gdn2.GDN2_BF16, 0) == 3 * one
+    assert WS(1, 65, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) == 256 + 2 * one
+    assert WS(4, 64, 4, 1, 128, 128, gdn2.GDN2_BF16, 0) == 256 + 4 * one
+    assert WS(1, 64, 1, 3, 128, 128, gdn2.GDN2_BF16, 0) == 256 + 3 * one
+    assert WS(1, 64, 1, 100, 128, 128, gdn2.GDN2_BF16, 0) == 512 + 100 * one
     # varlen reserves the chunk-offset table and one extra chunk per sequence
-    assert WS(1, 64, 2, 1, 128, 128, gdn2.GDN2_BF16, 1) == 256 + 3 * one
+    assert WS(1, 64, 2, 1, 128, 128, gdn2.GDN2_BF16, 1) == 256 + 256 + 3 * one
     assert WS(1, 4096, 1, 16, 128, 128, gdn2.GDN2_F32, 0) > WS(1, 4096, 1, 16, 128, 128, gdn2.GDN2_BF16, 0)
     # invalid or unsupported sizes give 0
     assert WS(0, 64, 0, 1, 128, 128, gdn2.GDN2_BF16, 0) == 0
