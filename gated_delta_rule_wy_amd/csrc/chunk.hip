@@ -681,12 +681,19 @@ template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, i
 // the level its operands come from. When the chip has workgroup slots to
 // spare, each chain gets `npf` extra workgroups on the same XCD that read
 // the chain's upcoming operand blocks and v / w rows a few chunks ahead of
-// the pass, so that the pass finds them in that XCD's L2. They read the
-// chain's progress counter (chunks finished by its first slice) to stay
-// between 3 and 3 + kPfWindow chunks ahead; every wait is bounded, and the
-// results of the pass never depend on them.
-static constexpr int kPfWindow = 5;
+// the pass, so that the pass finds them in that XCD's L2. Wave k of such a
+// workgroup takes chunks k, k + 8, ...: it reads the chain's progress
+// counter (chunks finished by the pass's first slice), waits while it is
+// more than 3 + kPfWindow chunks ahead, skips chunks closer than 3, and
+// reads one dword per line of its share of the chunk straight into an LDS
+// scratch area that nothing reads (so no register waits for a line; the
+// counter read waits only for this wave's reads of 8 chunks before). Every
+// loop and wait is bounded, and the pass never waits for these workgroups.
+static constexpr int kPfWindow = 8;
 static constexpr int kPfMaxSleeps = 64;
+
+typedef const __attribute__((address_space(1))) void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
 
 template <typename In, int DV, size_t BYTES>
 __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
@@ -696,34 +703,36 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
     constexpr int RL = (RB + 127) / 128;                          // lines per row
     constexpr int PL = NL + 2 * 64 * RL;                          // lines per chunk
-    const int t = threadIdx.x;
-    uint32_t sink = 0;
-    for (int c = 0; c < nch; ++c) {
-        int done = 0;
-        for (int s = 0;; ++s) {
-            done = __builtin_amdgcn_readfirstlane(__hip_atomic_load(prog + chain, __ATOMIC_RELAXED,
-                                                                    __HIP_MEMORY_SCOPE_AGENT));
-            if (c <= done + 3 + kPfWindow || s >= kPfMaxSleeps) break;
-            __builtin_amdgcn_s_sleep(8);
+    constexpr int NW = 8;                                         // waves
+    __shared__ uint32_t sSink[NW * 64];
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    lptr_t scratch = (lptr_t)(sSink + wv * 64);
+    auto done = [&]() {
+        return __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(prog + chain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    };
+    for (int c = wv; c < nch; c += NW) {
+        int d = done();
+        for (int s = 0; c > d + 3 + kPfWindow && s < kPfMaxSleeps; ++s) {
+            __builtin_amdgcn_s_sleep(4);
+            d = done();
         }
-        c = max(c, done + 3);
+        while (c < d + 3) c += NW;
         if (c >= nch) break;
-        const uint8_t *blk = blk0 + (size_t)c * BYTES;
-        for (int l = t * npf + pf; l < PL; l += npf * 512) {
+        for (int l = pf + npf * lane; l < PL; l += npf * 64) {
             const uint8_t *a;
             if (l < NL) {
-                a = blk + (size_t)l * 128;
+                a = blk0 + (size_t)c * BYTES + (size_t)l * 128;
             } else {
-                const int k = l - NL, which = k / (64 * RL), r = (k / RL) % 64, part = k % RL;
-                const int tok = min(tb + 64 * c + r, te - 1);
+                const int k = l - NL, which = k / (64 * RL), row = (k / RL) % 64, part = k % RL;
+                const int tok = min(tb + 64 * c + row, te - 1);
                 a = reinterpret_cast<const uint8_t *>(which ? w : v) + ((size_t)tok * H + h) * RB +
                     min(part * 128, RB - 4);
             }
-            sink ^= *reinterpret_cast<const uint32_t *>(a);
+            __builtin_amdgcn_global_load_lds((gptr_t)a, scratch, 4, 0, 0);
         }
     }
-    // keep the loads: the condition never holds for a launched grid
-    if (sink == 0x9e3779b9u && npf == 0) *const_cast<int *>(prog + chain) = (int)sink;
+    __syncthreads();   // drains the line reads before the workgroup ends
 }
 
 template <typename In, typename Op, int DK, int DV>
@@ -954,7 +963,7 @@ bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varl
     return true;
 }
 
-static constexpr int kMaxPrefetchWgs = 6;
+static constexpr int kMaxPrefetchWgs = 8;
 
 // compute units of the current device, queried once per device
 static hipError_t device_cus(int *cus)
