@@ -735,7 +735,7 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     __syncthreads();   // drains the line reads before the workgroup ends
 }
 
-template <typename In, typename Op, int DK, int DV>
+template <typename In, typename Op, int DK, int DV, int NC>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
@@ -749,14 +749,16 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
     constexpr int TPW = SF::TPW;
     constexpr int TPK = KB / 16;              // accumulator tiles per k-block
-    constexpr int NSL = DV / 16;              // column slices
+    constexpr int NSL = DV / (16 * NC);       // column slices (workgroups per chain)
     constexpr int PD = 2;                     // prefetch distance (register ring of 3)
+    static_assert(NSL >= 1 && NSL * 16 * NC == DV, "slice width must divide dv");
 
-    __shared__ __attribute__((aligned(16))) Op sS[NCT * 64 * 4];        // state operand tiles
-    __shared__ __attribute__((aligned(16))) Op sD[4 * 64 * 4];          // Delta tiles
-    __shared__ __attribute__((aligned(16))) Op sU[2 * NSB * 64 * NE];   // U hi / lo B-fragments
-    constexpr int LDO = 20;                                              // o staging row stride (floats)
-    __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];      // o tiles
+    // per 16-column tile q of the slice
+    __shared__ __attribute__((aligned(16))) Op sS[NC][NCT * 64 * 4];        // state operand tiles
+    __shared__ __attribute__((aligned(16))) Op sD[NC][4 * 64 * 4];          // Delta tiles
+    __shared__ __attribute__((aligned(16))) Op sU[NC][2 * NSB * 64 * NE];   // U hi / lo B-fragments
+    constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
+    __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];          // o tiles
 
     // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
     // sit on XCD c % 8
@@ -769,7 +771,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 
     const int t = threadIdx.x;
     const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
-    const int col = 16 * js + m16;
+    const int col0 = 16 * NC * js;            // first value column of the slice
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
     const int tb = sq.t0(i), te = sq.t1(i);
     const int cbeg = sq.m.chunk0(i);
@@ -784,20 +786,22 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 
     if (wv < 4) {
         // ------------------------------------------------ state waves
-        f4 Sr[TPW];
+        f4 Sr[NC][TPW];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int ct = wv * TPW + u;
-            Sr[u] = f4zero();
-            if (ct < NCT) {
-                if (S0) {
+        for (int q = 0; q < NC; ++q)
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        Sr[u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col];
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                Sr[q][u] = f4zero();
+                if (ct < NCT) {
+                    if (S0) {
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            Sr[q][u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16];
+                    }
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
-                lds_tile_store<Op>(sS + ct * 256, lane, Sr[u]);
             }
-        }
         const int sbmax = (16 * wv + 15) / KB;
         SF f0, f1, f2;
         if (nch > 0) {
@@ -810,33 +814,46 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         // the state waves would otherwise wait for the output waves.
         auto step = [&](int c, SF &cur, SF &pre) {
             __syncthreads();   // (1) state tiles and U ready
-            f4 acc = f4zero(), accw = f4zero();
+            f4 acc[NC], accw[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) { acc[q] = f4zero(); accw[q] = f4zero(); }
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 if (sb > sbmax) break;
-                const frag uh = *reinterpret_cast<const frag *>(&sU[((0 * NSB + sb) * 64 + lane) * NE]);
-                const frag ul = *reinterpret_cast<const frag *>(&sU[((1 * NSB + sb) * 64 + lane) * NE]);
-                acc = M::mma(cur.Ti[sb], uh, acc);
-                acc = M::mma(cur.Ti[sb], ul, acc);
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
+                    const frag ul = *reinterpret_cast<const frag *>(&sU[q][((1 * NSB + sb) * 64 + lane) * NE]);
+                    acc[q] = M::mma(cur.Ti[sb], uh, acc[q]);
+                    acc[q] = M::mma(cur.Ti[sb], ul, acc[q]);
+                }
             }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                accw = M::mma(cur.nW[kb], lds_bfrag<Op>(sS + kb * TPK * 256, lane), accw);
-            lds_tile_store<Op>(sD + wv * 256, lane, acc + accw);
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    accw[q] = M::mma(cur.nW[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), accw[q]);
+#pragma unroll
+            for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sD[q] + wv * 256, lane, acc[q] + accw[q]);
             pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready
-            frag Db[NSB];
+            frag Db[NC][NSB];
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) Db[sb] = lds_bfrag<Op>(sD + sb * TPK * 256, lane);
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) Db[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int ct = wv * TPW + u;
                 if (NCT % 4 != 0 && ct >= NCT) continue;
-                f4 s = Sr[u] * cur.gam[u];
 #pragma unroll
-                for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[sb], s);
-                Sr[u] = s;
-                lds_tile_store<Op>(sS + ct * 256, lane, s);
+                for (int q = 0; q < NC; ++q) {
+                    f4 s = Sr[q][u] * cur.gam[u];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                    Sr[q][u] = s;
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
+                }
             }
             pre.load_b(blk_of(c + PD), wv, lane);
             // A device-scope store is written through to memory and, since
@@ -859,67 +876,89 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         __syncthreads();   // final: pairs with the output waves' last o tile
         if (ST) {
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int ct = wv * TPW + u;
-                if (ct >= NCT) continue;
+            for (int q = 0; q < NC; ++q)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-                    ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col] = Sr[u][ii];
-            }
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (ct >= NCT) continue;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = Sr[q][u][ii];
+                }
         }
     } else {
         // ------------------------------------------------ output waves
         const int wo = wv - 4, to = t - 256;
         const int sbmax = (16 * wo + 15) / KB;
-        // v / w tile coordinates of this thread and where its U values go
+        // v / w tile coordinates of this thread (per column tile) and where its U values go
         const int ur = to >> 2, uc = 4 * (to & 3);
-        const size_t uoff0 = (size_t)h * DV + 16 * js + uc;
+        const size_t uoff0 = (size_t)h * DV + col0 + uc;
         const int usb = ur / KB, usl = ur % KB;
         const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
         auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
         auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
+        struct UV { UVTile<In> q[NC]; };
+        auto uv_load = [&](UV &u, int c) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q) u.q[q].load(v, w, uv_off(c) + 16 * q, uv_ok(c));
+        };
         OF g0, g1, g2;
-        UVTile<In> u0, u1, u2;
+        UV u0, u1, u2;
         if (nch > 0) {
             g0.load(blk_of(0), wo, lane);
-            u0.load(v, w, uv_off(0), uv_ok(0));
+            uv_load(u0, 0);
             g1.load(blk_of(1), wo, lane);
-            u1.load(v, w, uv_off(1), uv_ok(1));
+            uv_load(u1, 1);
         }
-        // o tiles go through LDS (double-buffered) and leave as one 16-byte
-        // store per thread after the next barrier
+        // o tiles go through LDS (double-buffered) and leave as 16-byte
+        // stores (NC per thread) after the next barrier
         auto store_o = [&](int c) {
             const int tok = tb + 64 * c, n = min(64, te - tok);
-            const int row = to >> 2, q4 = to & 3;
-            if (row < n)
-                *reinterpret_cast<f4 *>(o + ((size_t)(tok + row) * H + h) * DV + 16 * js + 4 * q4) =
-                    *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
-        };
-        auto step = [&](int c, OF &cur, OF &pre, UVTile<In> &ucur, UVTile<In> &upre) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float uu = ucur.ok ? in2f<In>(ucur.w[e]) * in2f<In>(ucur.v[e]) : 0.f;
-                const Op hi = (Op)uu;
-                const int ln = (uc + e) + 16 * ug;
-                sU[((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
-                sU[((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+            for (int q = 0; q < NC; ++q) {
+                const int x = to + 256 * q, row = x / (4 * NC), q4 = x % (4 * NC);
+                if (row < n)
+                    *reinterpret_cast<f4 *>(o + ((size_t)(tok + row) * H + h) * DV + col0 + 4 * q4) =
+                        *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
             }
+        };
+        auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &upre) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const UVTile<In> &uq = ucur.q[q];
+                    const float uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                    const Op hi = (Op)uu;
+                    const int ln = (uc + e) + 16 * ug;
+                    sU[q][((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
+                    sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+                }
             __syncthreads();   // (1)
             pre.load(blk_of(c + PD), wo, lane);
-            upre.load(v, w, uv_off(c + PD), uv_ok(c + PD));
+            uv_load(upre, c + PD);
             if (c > 0) store_o(c - 1);
-            f4 oacc = f4zero();
+            f4 oacc[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) oacc[q] = f4zero();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                oacc = M::mma(cur.Qp[kb], lds_bfrag<Op>(sS + kb * TPK * 256, lane), oacc);
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    oacc[q] = M::mma(cur.Qp[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), oacc[q]);
             __syncthreads();   // (2)
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 if (sb > sbmax) break;
-                oacc = M::mma(cur.Pm[sb], lds_bfrag<Op>(sD + sb * TPK * 256, lane), oacc);
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    oacc[q] = M::mma(cur.Pm[sb], lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane), oacc[q]);
             }
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + m16] = oacc[ii];
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + 16 * q + m16] = oacc[q][ii];
         };
         int c = 0;
         for (; c + 3 <= nch; c += 3) {
@@ -1013,20 +1052,35 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    // prefetch workgroups only where the whole grid stays resident at one
-    // workgroup per compute unit
-    constexpr int NSL = DV / 16;
-    const long long groups = (chains + 7) / 8;
+    // One 16-column tile per workgroup with L2 prefetch workgroups where the
+    // grid stays resident at one workgroup per compute unit; two tiles per
+    // workgroup where one tile would oversubscribe the chip (half the
+    // workgroups, each streaming the same operand blocks once for twice the
+    // columns), with prefetch workgroups if the halved grid leaves room.
     int cus = 0;
     if ((err = device_cus(&cus)) != hipSuccess) return err;
-    int npf = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - NSL);
-    if (npf < 2 || p.max_chunks == 0) npf = 0;
-    const long long pass_grid = 8LL * (NSL + npf) * groups;
+    const long long groups = (chains + 7) / 8;
+    auto npf_for = [&](int nsl) {
+        int n = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - nsl);
+        return (n < 2 || p.max_chunks == 0) ? 0 : n;
+    };
+    constexpr int NSL1 = DV / 16;
+    const bool two = (DV / 16) % 2 == 0 && 8LL * NSL1 * groups > cus;
+    const int nsl = two ? NSL1 / 2 : NSL1;
+    const int npf = npf_for(nsl);
+    const long long pass_grid = 8LL * (nsl + npf) * groups;
     if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_before("gdn2_chunk_pass", st);
-    hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV>), dim3((unsigned)pass_grid), dim3(512), 0, st,
-                       (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
-                       (const uint8_t *)ops, prog, npf);
+    if (two) {
+        if constexpr ((DV / 16) % 2 == 0)
+            hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV, 2>), dim3((unsigned)pass_grid), dim3(512), 0, st,
+                               (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
+                               (const uint8_t *)ops, prog, npf);
+    } else {
+        hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV, 1>), dim3((unsigned)pass_grid), dim3(512), 0, st,
+                           (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
+                           (const uint8_t *)ops, prog, npf);
+    }
     prof_after(st);
     return hipGetLastError();
 }

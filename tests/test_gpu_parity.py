@@ -128,6 +128,15 @@ def test_long_no_s0_no_final_state():
     assert_close(o, o_ref, p.dtype, 'long no S0 o')
 
 
+@pytest.mark.parametrize('dt,dk,dv', [('bf16', 128, 128), ('bf16', 32, 64), ('f32', 64, 32), ('f32', 16, 128)])
+def test_many_chains_two_tile_slices(dt, dk, dv):
+    """Enough (sequence, head) chains that one 16-column tile per workgroup
+    would oversubscribe the chip: the pass takes two tiles per workgroup."""
+    lens = [130, 64, 1, 200, 77] * 8
+    p = gi.prefill(970 + dk + dv, lens, H=8, dk=dk, dv=dv, dtype=dt, s0_std=0.05, uniform=False)
+    check_prefill(p, f'two-tile {dt} dk={dk} dv={dv}')
+
+
 # ------------------------------------------------------------------ consistency
 
 def test_deterministic_and_overwrites_outputs():
