@@ -58,9 +58,18 @@ template <typename Op, int DK> struct Blk {
     static constexpr size_t oW = 0;                          // -W   [4][NKB] frags
     static constexpr size_t oQ = oW + 4 * NKB * FRAG;        // Q+   [4][NKB]
     static constexpr size_t oK = oQ + 4 * NKB * FRAG;        // Khat^T [NCT][NSB]
-    static constexpr size_t oP = oK + NCT * NSB * FRAG;      // P    [4][NSB]
-    static constexpr size_t oT = oP + 4 * NSB * FRAG;        // T    [4][NSB]
-    static constexpr size_t oG = oT + 4 * NSB * FRAG;        // gamma float[DK]
+    // P and T are lower triangular: only the k-blocks sb <= sbmax(mt) of row
+    // tile mt are stored, in row-tile order (tpos)
+    static constexpr __host__ __device__ int sbmax(int mt) { return (16 * mt + 15) / KB; }
+    static constexpr __host__ __device__ int tpos(int mt, int sb) {
+        int p = sb;
+        for (int m = 0; m < mt; ++m) p += sbmax(m) + 1;
+        return p;
+    }
+    static constexpr int NTRI = tpos(3, sbmax(3)) + 1;   // stored fragments of P (and of T)
+    static constexpr size_t oP = oK + NCT * NSB * FRAG;      // P    [NTRI]
+    static constexpr size_t oT = oP + NTRI * FRAG;           // T    [NTRI]
+    static constexpr size_t oG = oT + NTRI * FRAG;           // gamma float[DK]
     static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
 };
 
@@ -522,12 +531,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             wacc[qq][mt] = acc;
         }
     }
-    // P and T fragments
+    // P and T fragments (the nonzero k-blocks only)
     for (int f = wv; f < 4 * NSB; f += 4) {
         const int mt = f / NSB, sb = f % NSB;
-        *reinterpret_cast<frag *>(blk + L::oP + ((size_t)f * 64 + lane) * 16) =
+        if (sb > L::sbmax(mt)) continue;
+        const int pos = L::tpos(mt, sb);
+        *reinterpret_cast<frag *>(blk + L::oP + ((size_t)pos * 64 + lane) * 16) =
             lds_row_frag<Op>(sP + (16 * mt + m16) * LDT, sb * KB, g4);
-        *reinterpret_cast<frag *>(blk + L::oT + ((size_t)f * 64 + lane) * 16) =
+        *reinterpret_cast<frag *>(blk + L::oT + ((size_t)pos * 64 + lane) * 16) =
             lds_row_frag<Op>(sT + (16 * mt + m16) * LDT, sb * KB, g4);
     }
     __syncthreads();   // every read of the E-side operand done
@@ -590,7 +601,7 @@ template <typename Op, int DK> struct StateFrags {
 #pragma unroll
         for (int sb = 0; sb < L::NSB; ++sb)
             if (sb <= sbmax)
-                Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)(wv * L::NSB + sb) * 64 + lane) * 16);
+                Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)L::tpos(wv, sb) * 64 + lane) * 16);
     }
     // second half: what the state update needs
     __device__ __forceinline__ void load_b(const uint8_t *blk, int wv, int lane) {
@@ -620,7 +631,7 @@ template <typename Op, int DK> struct OutFrags {
 #pragma unroll
         for (int sb = 0; sb < L::NSB; ++sb)
             if (sb <= sbmax)
-                Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)(wo * L::NSB + sb) * 64 + lane) * 16);
+                Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)L::tpos(wo, sb) * 64 + lane) * 16);
     }
 };
 

@@ -17,7 +17,7 @@ namespace gdn2 {
 
 template <int DK, int DV> struct DecodeShape {
     static constexpr int COLG = DV / 4;                                  // column groups
-    static constexpr int ROWG = (DK < 256 / COLG) ? DK : 256 / COLG;     // row groups
+    static constexpr int ROWG = (DK < 512 / COLG) ? DK : 512 / COLG;     // row groups (512 threads: 6.8 vs 6.6 TB/s at 256)
     static constexpr int RPT = DK / ROWG;                                // rows per thread
     static constexpr int NT = COLG * ROWG;                               // threads
 };
@@ -86,10 +86,14 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const f4 delta = u - E;
     if (rg == 0)
         *reinterpret_cast<f4 *>(o + (size_t)nh * DV + 4 * cg) = R + delta * KQ;
+    // The new state is written with non-temporal stores (measured: 6.6 vs
+    // 6.2 TB/s for the 256 x 16 x 128 x 128 state; non-temporal loads gain
+    // as much alone, but the two together lose).
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int c = rg + r * ROWG;
-        *reinterpret_cast<f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg) = sv[r] + delta * s_k[c];
+        __builtin_nontemporal_store(sv[r] + delta * s_k[c],
+                                    reinterpret_cast<f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg));
     }
 }
 
