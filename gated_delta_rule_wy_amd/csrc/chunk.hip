@@ -61,10 +61,10 @@ template <typename Op, int DK> struct Blk {
     // P and T are lower triangular: only the k-blocks sb <= sbmax(mt) of row
     // tile mt are stored, in row-tile order (tpos)
     static constexpr __host__ __device__ int sbmax(int mt) { return (16 * mt + 15) / KB; }
+    // closed form (a loop over a runtime mt would stay a loop in the pass)
+    static_assert(KB == 32 || KB == 16, "k-block of 16 or 32 rows");
     static constexpr __host__ __device__ int tpos(int mt, int sb) {
-        int p = sb;
-        for (int m = 0; m < mt; ++m) p += sbmax(m) + 1;
-        return p;
+        return (KB == 32 ? (mt < 2 ? mt : 2 * mt - 2) : mt * (mt + 1) / 2) + sb;
     }
     static constexpr int NTRI = tpos(3, sbmax(3)) + 1;   // stored fragments of P (and of T)
     static constexpr size_t oP = oK + NCT * NSB * FRAG;      // P    [NTRI]
@@ -797,6 +797,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 
     if (wv < 4) {
         // ------------------------------------------------ state waves
+        // the serial chain runs here: these waves win issue ties on their SIMD
+        __builtin_amdgcn_s_setprio(3);
         f4 Sr[NC][TPW];
 #pragma unroll
         for (int q = 0; q < NC; ++q)
@@ -1013,7 +1015,7 @@ bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varl
     return true;
 }
 
-static constexpr int kMaxPrefetchWgs = 8;
+static constexpr int kMaxPrefetchWgs = 4;   // more gave no gain, and a full chip leaves no slack
 
 // compute units of the current device, queried once per device
 static hipError_t device_cus(int *cus)
