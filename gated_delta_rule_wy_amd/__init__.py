@@ -24,10 +24,12 @@ LIB_PATH = os.path.join(_HERE, 'libgdn2.so')
 
 GDN2_OK, GDN2_ERR_INVALID, GDN2_ERR_UNSUPPORTED, GDN2_ERR_WORKSPACE, GDN2_ERR_HIP = range(5)
 GDN2_F32, GDN2_BF16 = 0, 1
+GDN2_GATES_PER_CHANNEL, GDN2_GATE_B_PER_HEAD, GDN2_GATE_W_PER_HEAD, GDN2_GATE_ALPHA_PER_HEAD = 0, 1, 2, 4
 CHUNK = 64
 
 EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
-           'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_decode_step',
+           'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_gates',
+           'gdn2_decode_step', 'gdn2_decode_step_gates',
            'gdn2_profile_begin', 'gdn2_profile_end', 'gdn2_profile_kernel')
 
 
@@ -52,8 +54,12 @@ def _load() -> ctypes.CDLL:
     lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn2_chunk_fwd.argtypes = [vp] * 10 + [i] * 8 + [vp, sz]
     lib.gdn2_chunk_fwd.restype = i
+    lib.gdn2_chunk_fwd_gates.argtypes = [vp] * 6 + [i] + [vp] * 4 + [i] * 8 + [vp, sz]
+    lib.gdn2_chunk_fwd_gates.restype = i
     lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 6
     lib.gdn2_decode_step.restype = i
+    lib.gdn2_decode_step_gates.argtypes = [vp] * 6 + [i] + [vp] * 2 + [i] * 6
+    lib.gdn2_decode_step_gates.restype = i
     lib.gdn2_profile_begin.argtypes = [i]
     lib.gdn2_profile_begin.restype = i
     lib.gdn2_profile_end.argtypes = []
@@ -134,6 +140,20 @@ def profile_end() -> dict:
     return out
 
 
+def _gate_layout(lead, H, dk, dv, b, w, log_alpha, dt, dev) -> int:
+    """Gate layout bits from the gate shapes: a gate without the channel axis
+    ([..., H]) holds one value per token-head (KDA / Gated DeltaNet forms)."""
+    gates = 0
+    for name, t, d, bit, tdt in (('b', b, dk, GDN2_GATE_B_PER_HEAD, dt), ('w', w, dv, GDN2_GATE_W_PER_HEAD, dt),
+                                 ('log_alpha', log_alpha, dk, GDN2_GATE_ALPHA_PER_HEAD, torch.float32)):
+        if t.dim() == len(lead) + 1:
+            _check(t, name, (*lead, H), tdt, dev)
+            gates |= bit
+        else:
+            _check(t, name, (*lead, H, d), tdt, dev)
+    return gates
+
+
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
               b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
@@ -143,16 +163,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     fp32); log_alpha: [B, T, H, dk] fp32. With ``cu_seqlens`` (int32 [N+1] on
     the device) B must be 1 and the sequences are packed along T. S0: [N, H,
     dk, dv] fp32 or None (zeros). Returns (o [B, T, H, dv] fp32, S_T [N, H, dk,
-    dv] fp32 or None)."""
+    dv] fp32 or None). b, w and log_alpha may instead be [B, T, H], one gate
+    per token-head (KDA: b = w = beta; Gated DeltaNet: also a scalar decay)."""
     if q.dim() != 4:
         raise ValueError('q must be [B, T, H, dk]')
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
-    for name, t, d in (('q', q, dk), ('k', k, dk), ('b', b, dk), ('v', v, dv), ('w', w, dv)):
+    for name, t, d in (('q', q, dk), ('k', k, dk), ('v', v, dv)):
         _check(t, name, (B, T, H, d), dt, dev)
-    _check(log_alpha, 'log_alpha', (B, T, H, dk), torch.float32, dev)
+    gates = _gate_layout((B, T), H, dk, dv, b, w, log_alpha, dt, dev)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
             raise ValueError('cu_seqlens must be a 1-D int32 tensor on the same device')
@@ -180,12 +201,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     set_stream()
-    st = _lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                             _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
-                             B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace),
-                             workspace.numel() * workspace.element_size())
+    st = _lib.gdn2_chunk_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
+                                   _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
+                                   B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size())
     if st != GDN2_OK:
-        raise Gdn2Error(st, 'gdn2_chunk_fwd')
+        raise Gdn2Error(st, 'gdn2_chunk_fwd_gates')
     return out, ST
 
 
@@ -193,24 +214,25 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
                 b: torch.Tensor, w: torch.Tensor, S: torch.Tensor, *,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One token per sequence. q, k, b: [N, H, dk]; v, w: [N, H, dv]; log_alpha
-    [N, H, dk] fp32; S: [N, H, dk, dv] fp32, updated in place. Returns o [N, H, dv] fp32."""
+    [N, H, dk] fp32; S: [N, H, dk, dv] fp32, updated in place. Returns o [N, H, dv] fp32.
+    b, w and log_alpha may instead be [N, H] (one gate per sequence-head)."""
     if q.dim() != 3:
         raise ValueError('q must be [N, H, dk]')
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
-    for name, t, d in (('q', q, dk), ('k', k, dk), ('b', b, dk), ('v', v, dv), ('w', w, dv)):
+    for name, t, d in (('q', q, dk), ('k', k, dk), ('v', v, dv)):
         _check(t, name, (N, H, d), dt, dev)
-    _check(log_alpha, 'log_alpha', (N, H, dk), torch.float32, dev)
+    gates = _gate_layout((N,), H, dk, dv, b, w, log_alpha, dt, dev)
     _check(S, 'S', (N, H, dk, dv), torch.float32, dev)
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     else:
         _check(out, 'out', (N, H, dv), torch.float32, dev)
     set_stream()
-    st = _lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                               _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
+    st = _lib.gdn2_decode_step_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
+                                     _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
     if st != GDN2_OK:
-        raise Gdn2Error(st, 'gdn2_decode_step')
+        raise Gdn2Error(st, 'gdn2_decode_step_gates')
     return out

@@ -179,6 +179,17 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                    gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
                    size_t workspace_bytes)
 {
+    return gdn2_chunk_fwd_gates(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, S0, o, ST, cu_seqlens, B, T,
+                                N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes);
+}
+
+int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
+                         const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                         size_t workspace_bytes)
+{
+    if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     gdn2::ChunkPlan plan;
     const int varlen = cu_seqlens != nullptr;
     int st = chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan);
@@ -199,6 +210,7 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
     a.ST = ST;
     a.cu_seqlens = cu_seqlens;
     a.B = B; a.T = T; a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.gates = gates;
     a.bf16 = in_dtype == GDN2_BF16;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
@@ -211,6 +223,15 @@ int gdn2_decode_step(const void *q, const void *k, const void *v, const float *l
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
                      int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
 {
+    return gdn2_decode_step_gates(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, S, o, N, H, dk, dv, in_dtype,
+                                  out_dtype);
+}
+
+int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
+                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+{
+    if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
     if (in_dtype != GDN2_F32 && in_dtype != GDN2_BF16) return GDN2_ERR_INVALID;
     if (out_dtype != GDN2_F32) return out_dtype == GDN2_BF16 ? GDN2_ERR_UNSUPPORTED : GDN2_ERR_INVALID;
@@ -225,6 +246,7 @@ int gdn2_decode_step(const void *q, const void *k, const void *v, const float *l
     a.S = S;
     a.o = o;
     a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.gates = gates;
     a.bf16 = in_dtype == GDN2_BF16;
     prof_call();
     if (gdn2::launch_decode(a, g_stream) != hipSuccess) return GDN2_ERR_HIP;

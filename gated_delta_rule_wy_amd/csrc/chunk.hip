@@ -117,6 +117,7 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(const int32_t *__restr
 struct Seqs {
     SeqMap m;
     int Ttot, max_chunks;
+    int gates;   // kGateB / kGateW / kGateAlpha: per token-head instead of per channel
     __device__ __forceinline__ int t0(int i) const { return clampi(m.tok0(i), 0, Ttot); }
     __device__ __forceinline__ int t1(int i) const { return clampi(m.tok1(i), t0(i), Ttot); }
 };
@@ -192,9 +193,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
             const bool ok = r < n;
-            const size_t off = ((size_t)(t0 + min(r, n - 1)) * H + h) * DK + c0;
-            const f2 x = *reinterpret_cast<const f2 *>(la + off);
-            const raw2 kk = Ld<In>::ldraw2(k + off), bb = Ld<In>::ldraw2(b + off), qq = Ld<In>::ldraw2(q + off);
+            const size_t th = (size_t)(t0 + min(r, n - 1)) * H + h, off = th * DK + c0;
+            f2 x;
+            if (sq.gates & kGateAlpha) { const float a1 = la[th]; x[0] = a1; x[1] = a1; }
+            else x = *reinterpret_cast<const f2 *>(la + off);
+            const raw2 bb = (sq.gates & kGateB) ? Ld<In>::splat2(b + th) : Ld<In>::ldraw2(b + off);
+            const raw2 kk = Ld<In>::ldraw2(k + off), qq = Ld<In>::ldraw2(q + off);
             const f2 z = {0.f, 0.f};
             lv[u] = ok ? x : z;
             kr[u] = ok ? kk : Ld<In>::zero2();
@@ -444,11 +448,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             float aA = 0.f, aP = 0.f;
             if (sl <= rl && r < n) {
                 const size_t br_ = ((size_t)(t0 + r) * H + h) * DK, bs = ((size_t)(t0 + s) * H + h) * DK;
+                const bool asc = sq.gates & kGateAlpha, bsc = sq.gates & kGateB;
                 for (int c = 0; c < DK; ++c) {
                     float d = 0.f;
-                    for (int x = s + 1; x <= r; ++x) d += la[((size_t)(t0 + x) * H + h) * DK + c];
+                    for (int x = s + 1; x <= r; ++x) {
+                        const size_t th = (size_t)(t0 + x) * H + h;
+                        d += la[asc ? th : th * DK + c];
+                    }
                     const float e = __expf(d) * Ld<In>::one(k + bs + c);
-                    aA += Ld<In>::one(b + br_ + c) * Ld<In>::one(k + br_ + c) * e;
+                    const float bv = Ld<In>::one(b + (bsc ? (size_t)(t0 + r) * H + h : br_ + c));
+                    aA += bv * Ld<In>::one(k + br_ + c) * e;
                     aP += Ld<In>::one(q + br_ + c) * e;
                 }
             }
@@ -644,16 +653,25 @@ template <typename In> struct UVTile {
     // the end and zeroes the product where it is used, not here: a select on
     // the loaded values would make the wave wait for this load (and every
     // load issued before it) at once.
-    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, bool ok_) {
+    // `woff` addresses w when it holds one gate per token-head (`wsc`)
+    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, size_t woff, bool wsc, bool ok_) {
         ok = ok_;
         if constexpr (sizeof(In) == 2) {
             uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
-            uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
             v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
-            w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
+            if (wsc) {
+                const In x = wp[woff];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = x;
+            } else {
+                uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
+                w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
+            }
         } else {
             const f4 a = *reinterpret_cast<const f4 *>(vp + off);
-            const f4 b = *reinterpret_cast<const f4 *>(wp + off);
+            f4 b;
+            if (wsc) { const float x = wp[woff]; b[0] = x; b[1] = x; b[2] = x; b[3] = x; }
+            else b = *reinterpret_cast<const f4 *>(wp + off);
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
         }
@@ -708,12 +726,14 @@ typedef __attribute__((address_space(3))) void *lptr_t;
 
 template <typename In, int DV, size_t BYTES>
 __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
-                                              int chain, int h, int H, int pf, int npf, int nch, int tb, int te)
+                                              int chain, int h, int H, int pf, int npf, int nch, int tb, int te,
+                                              int gates)
 {
     constexpr int NL = (int)(BYTES / 128);                        // block lines
     constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
     constexpr int RL = (RB + 127) / 128;                          // lines per row
-    constexpr int PL = NL + 2 * 64 * RL;                          // lines per chunk
+    // lines per chunk: the block, then the v rows and (per-channel gates) the w rows
+    const int PL = NL + ((gates & kGateW) ? 1 : 2) * 64 * RL;
     constexpr int NW = 8;                                         // waves
     __shared__ uint32_t sSink[NW * 64];
     const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
@@ -790,7 +810,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     auto blk_of = [&](int c) { return ops + ((size_t)h * sq.max_chunks + cbeg + min(c, nch - 1)) * L::bytes; };
     if (role >= NSL) {
         pass_prefetch<In, DV, L::bytes>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain, h,
-                                        H, role - NSL, npf, nch, tb, te);
+                                        H, role - NSL, npf, nch, tb, te, sq.gates);
         return;
     }
     const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
@@ -910,10 +930,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
         auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
         auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
+        auto w_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H + h; };
+        const bool wsc = sq.gates & kGateW;
         struct UV { UVTile<In> q[NC]; };
         auto uv_load = [&](UV &u, int c) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q) u.q[q].load(v, w, uv_off(c) + 16 * q, uv_ok(c));
+            for (int q = 0; q < NC; ++q) u.q[q].load(v, w, uv_off(c) + 16 * q, w_off(c), wsc, uv_ok(c));
         };
         OF g0, g1, g2;
         UV u0, u1, u2;
@@ -1046,6 +1068,7 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     sq.m.T = a.T;
     sq.Ttot = a.cu_seqlens ? a.T : a.B * a.T;
     sq.max_chunks = p.max_chunks;
+    sq.gates = a.gates;
     hipError_t err = hipSuccess;
     if (a.cu_seqlens) {
         prof_before("gdn2_chunk_plan", st);

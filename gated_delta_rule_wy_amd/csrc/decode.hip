@@ -26,7 +26,7 @@ template <typename In, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
     const float *__restrict__ la, const In *__restrict__ b, const In *__restrict__ w,
-    float *__restrict__ S, float *__restrict__ o)
+    float *__restrict__ S, float *__restrict__ o, int gates)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int COLG = Sh::COLG, ROWG = Sh::ROWG, RPT = Sh::RPT, NT = Sh::NT;
@@ -44,19 +44,21 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     for (int r = 0; r < RPT; ++r)
         sv[r] = *reinterpret_cast<const f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg);
 
+    // gates: one value per channel, or per (sequence, head) where the bit is set
+    const bool asc = gates & kGateAlpha, bsc = gates & kGateB, wsc = gates & kGateW;
     float kq = 0.f;
     for (int c = t; c < DK; c += NT) {
         const size_t i = (size_t)nh * DK + c;
         const float kc = Ld<In>::one(k + i), qc = Ld<In>::one(q + i);
-        s_a[c] = __expf(la[i]);
+        s_a[c] = __expf(la[asc ? (size_t)nh : i]);
         s_k[c] = kc;
         s_q[c] = qc;
-        s_bk[c] = Ld<In>::one(b + i) * kc;
+        s_bk[c] = Ld<In>::one(b + (bsc ? (size_t)nh : i)) * kc;
         kq += kc * qc;
     }
     for (int j = t; j < DV; j += NT) {
         const size_t i = (size_t)nh * DV + j;
-        s_u[j] = Ld<In>::one(w + i) * Ld<In>::one(v + i);
+        s_u[j] = Ld<In>::one(w + (wsc ? (size_t)nh : i)) * Ld<In>::one(v + i);
     }
     // k.q: wave reduction, then across waves
 #pragma unroll
@@ -104,7 +106,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st)
     prof_before("gdn2_decode", st);
     hipLaunchKernelGGL((decode_kernel<In, DK, DV>), dim3(a.N * a.H), dim3(NT), 0, st,
                        (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
-                       (const In *)a.b, (const In *)a.w, a.S, (float *)a.o);
+                       (const In *)a.b, (const In *)a.w, a.S, (float *)a.o, a.gates);
     prof_after(st);
     return hipGetLastError();
 }

@@ -41,6 +41,8 @@ template <> struct Ld<uint16_t> {
         return r;
     }
     static __device__ __forceinline__ raw2 zero2() { return 0u; }
+    // one element, twice
+    static __device__ __forceinline__ raw2 splat2(const uint16_t *p) { const uint32_t x = *p; return x | (x << 16); }
     // two consecutive elements
     static __device__ __forceinline__ f2 two(const uint16_t *p) {
         uint32_t u = *reinterpret_cast<const uint32_t *>(p);
@@ -56,6 +58,7 @@ template <> struct Ld<float> {
     static __device__ __forceinline__ raw2 ldraw2(const float *p) { return *reinterpret_cast<const f2 *>(p); }
     static __device__ __forceinline__ f2 cvt2(raw2 u) { return u; }
     static __device__ __forceinline__ raw2 zero2() { f2 z = {0.f, 0.f}; return z; }
+    static __device__ __forceinline__ raw2 splat2(const float *p) { const float x = *p; f2 r = {x, x}; return r; }
     static __device__ __forceinline__ f2 two(const float *p) { return *reinterpret_cast<const f2 *>(p); }
     static __device__ __forceinline__ float one(const float *p) { return *p; }
 };

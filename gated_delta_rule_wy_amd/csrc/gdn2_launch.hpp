@@ -7,12 +7,16 @@
 
 namespace gdn2 {
 
+// Gate layouts (bit set = one value per token and head instead of one per channel)
+enum : int { kGateB = 1, kGateW = 2, kGateAlpha = 4 };
+
 struct DecodeArgs {
     const void *q, *k, *v, *b, *w;
     const float *log_alpha;
     float *S;
     void *o;
     int N, H, dk, dv;
+    int gates;
     bool bf16;
 };
 
@@ -24,6 +28,7 @@ struct ChunkArgs {
     float *ST;
     const int32_t *cu_seqlens;   // device, or null for uniform batches
     int B, T, N, H, dk, dv;
+    int gates;
     bool bf16;
     void *workspace;
     size_t workspace_bytes;

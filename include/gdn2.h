@@ -54,6 +54,23 @@ typedef enum {
     GDN2_BF16 = 1
 } gdn2_dtype;
 
+/*
+ * Gate layouts for the *_gates entry points. A set bit means that gate holds
+ * one value per token and head ([tokens, H], or [N, H] for a decode step)
+ * instead of one per channel; the value applies to every channel. Kimi Delta
+ * Attention is the erase and write gates collapsed to one scalar beta per
+ * token-head (pass GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD with b == w),
+ * and Gated DeltaNet additionally has a scalar decay (also set
+ * GDN2_GATE_ALPHA_PER_HEAD): the special cases that Gated DeltaNet-2 reduces
+ * to (snilld.dk, section "Hvad Gated DeltaNet-2 ændrer").
+ */
+typedef enum {
+    GDN2_GATES_PER_CHANNEL = 0,
+    GDN2_GATE_B_PER_HEAD = 1,
+    GDN2_GATE_W_PER_HEAD = 2,
+    GDN2_GATE_ALPHA_PER_HEAD = 4
+} gdn2_gate_layout;
+
 /* Set the HIP stream (a hipStream_t) used by this thread's later calls.
  * NULL selects the default stream. Always returns GDN2_OK. */
 int gdn2_set_stream(void *hip_stream);
@@ -101,6 +118,20 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                    size_t workspace_bytes);
 
 /*
+ * gdn2_chunk_fwd with the gate layouts given by `gates` (gdn2_gate_layout
+ * bits): b is [tokens, H] when GDN2_GATE_B_PER_HEAD is set, w is [tokens, H]
+ * with GDN2_GATE_W_PER_HEAD and log_alpha is [tokens, H] with
+ * GDN2_GATE_ALPHA_PER_HEAD; the other arguments, the workspace size and the
+ * errors are those of gdn2_chunk_fwd. Unknown bits give GDN2_ERR_INVALID.
+ * gdn2_chunk_fwd is this call with gates = GDN2_GATES_PER_CHANNEL.
+ */
+int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
+                         const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                         size_t workspace_bytes);
+
+/*
  * One recurrent decode step for N independent sequences (the same update
  * and readout for a single token; constant-size state, aifetchly, "Gated
  * DeltaNet-2 Guide", section "3. Chunkwise Parallel Algorithm ...": O(1)
@@ -117,6 +148,15 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
 int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
                      int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+
+/*
+ * gdn2_decode_step with the gate layouts given by `gates`: b, w and
+ * log_alpha are [N, H] where their bit is set. Unknown bits give
+ * GDN2_ERR_INVALID.
+ */
+int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
+                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
 
 /*
  * Per-kernel timing, for measurement tools (not needed for computing).

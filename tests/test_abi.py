@@ -133,6 +133,30 @@ def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
 
 
+@pytest.mark.parametrize('gates', [8, 16, -1])
+def test_gate_layout_rejects_unknown_bits(gates):
+    P = 0x10000
+    vp = ctypes.c_void_p
+    lib = gdn2.lib()
+    st = lib.gdn2_chunk_fwd_gates(vp(P), vp(P), vp(P), vp(P), vp(P), vp(P), gates, None, vp(P), vp(P), None,
+                                  1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, gdn2.GDN2_F32, vp(P), 1 << 30)
+    assert st == gdn2.GDN2_ERR_INVALID
+    st = lib.gdn2_decode_step_gates(vp(P), vp(P), vp(P), vp(P), vp(P), vp(P), gates, vp(P), vp(P),
+                                    4, 2, 128, 128, gdn2.GDN2_BF16, gdn2.GDN2_F32)
+    assert st == gdn2.GDN2_ERR_INVALID
+
+
+def test_gate_layout_valid_bits_pass_validation():
+    """Known layouts pass host validation (a bad dk then decides the status, so nothing launches)."""
+    P = 0x10000
+    vp = ctypes.c_void_p
+    lib = gdn2.lib()
+    for gates in range(8):
+        st = lib.gdn2_chunk_fwd_gates(vp(P), vp(P), vp(P), vp(P), vp(P), vp(P), gates, None, vp(P), vp(P),
+                                      None, 1, 64, 1, 1, 48, 128, gdn2.GDN2_BF16, gdn2.GDN2_F32, vp(P), 1 << 30)
+        assert st == gdn2.GDN2_ERR_UNSUPPORTED
+
+
 def test_python_binding_validates_before_calling():
     import torch
     x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
