@@ -122,6 +122,36 @@ def bench_prefill(args, torch, gdn2, gi):
         'kernels_ms': {k: round(v, 5) for k, v in avg.items()},
     }
 
+    # The same workload with gates of one value per token-head: the Kimi Delta
+    # Attention form (erase and write gate = one beta) and the Gated DeltaNet
+    # form (also one decay), the cases Gated DeltaNet-2 reduces to. The gate
+    # values are the per-channel gates' first channel; only the timing is used.
+    forms = {}
+    b1 = b[..., 0].contiguous()
+    la1 = la[..., 0].contiguous()
+    o1 = torch.empty_like(o)       # keeps o for the parity sample below
+    ST1 = torch.empty_like(ST)
+    for fname, (fb, fw, fla) in (('kda', (b1, b1, la)), ('gdn', (b1, b1, la1))):
+        frun = lambda: gdn2.chunk_fwd(q, k, v, fla, fb, fw, S0, out=o1, final_state=ST1, workspace=ws)
+        for _ in range(args.warmup):
+            frun()
+        torch.cuda.synchronize()
+        gdn2.profile_begin(args.steps)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            frun()
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - t0) * 1e3 / args.steps
+        fprof = gdn2.profile_end()
+        la_b = dk * 4 if fla is la else 4
+        fbytes = TH * (2 * dk * in_b + in_b + la_b) + TH * (dv * in_b + in_b + dv * 4) + 2 * B * H * dk * dv * 4
+        forms[fname] = {'ms_per_step': round(fms, 4), 'value': B * T / (fms * 1e-3), 'unit': 'tokens/s',
+                        'alg_bytes_per_step': int(fbytes),
+                        'step_roofline_frac': round(fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        'kernels_ms': {kk: round(vv[1] / vv[0], 5) for kk, vv in fprof.items() if vv[0]}}
+        log(f'[bench] prefill, {fname} gates: {fms:.3f} ms/step')
+    res['gate_forms'] = forms
+
     if not args.no_cpu_baseline:
         import oracle
         n_s = args.cpu_sample_tokens
@@ -140,7 +170,7 @@ def bench_prefill(args, torch, gdn2, gi):
         res['parity_sample'] = {'max_abs_err_over_rms': float(np.max(np.abs(o_gpu - o_ref)) / rms),
                                 'tokens': n_s}
         log(f'[bench] oracle {n_s} tokens in {dt:.1f}s; parity {res["parity_sample"]}')
-    del q, k, v, b, w, la, o, ws
+    del q, k, v, b, w, la, o, ws, b1, la1, o1, ST1
     torch.cuda.empty_cache()
     return res
 
@@ -248,6 +278,7 @@ def main():
         out['cpu_baseline'] = pre['cpu_baseline']
     out['step_roofline'] = pre['step_roofline']
     out['kernels_ms'] = pre['kernels_ms']
+    out['gate_forms'] = pre['gate_forms']
     if 'parity_sample' in pre:
         out['parity_sample'] = pre['parity_sample']
     if not args.no_decode:

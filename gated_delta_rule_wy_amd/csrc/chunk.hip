@@ -133,7 +133,7 @@ struct Seqs {
 // is used, with the exact pairwise path for diagonal blocks that need it.
 // All global loads are issued up front and unconditionally (rows past the
 // chunk's end are clamped and zeroed), so the wave waits once.
-template <typename In, typename Op, int DK>
+template <typename In, typename Op, int DK, int G>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ la,
     const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops, int *__restrict__ prog, int nprog)
@@ -186,7 +186,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     float *sMid = sRef + 5 * DK;        // [4][DK]
     float *sG0 = sMid + 4 * DK;         // [DK]: g at the chunk's first row
     f2 gg[RPG];
-    raw2 kr[RPG], br[RPG], qr[RPG];
+    // raw k, b, q of the thread's rows; rows past the chunk's end are zeroed
+    // where the values are used (rowf), not here, so no load waits early
+    constexpr bool BSC = (G & kGateB) != 0;   // b: one value per token-head
+    raw2 kr[RPG], qr[RPG];
+    typename std::conditional<BSC, In, raw2>::type br[RPG];
+    auto bf2 = [&](int u) {
+        if constexpr (BSC) { const float x = in2f<In>(br[u]); f2 r = {x, x}; return r; }
+        else return Ld<In>::cvt2(br[u]);
+    };
+    auto rowf = [&](int u) { return r0 + u < n ? 1.f : 0.f; };
     {
         f2 lv[RPG];
 #pragma unroll
@@ -194,16 +203,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             const int r = r0 + u;
             const bool ok = r < n;
             const size_t th = (size_t)(t0 + min(r, n - 1)) * H + h, off = th * DK + c0;
+            // G (compile time): which gates hold one value per token-head
             f2 x;
-            if (sq.gates & kGateAlpha) { const float a1 = la[th]; x[0] = a1; x[1] = a1; }
+            if constexpr ((G & kGateAlpha) != 0) { const float a1 = la[th]; x[0] = a1; x[1] = a1; }
             else x = *reinterpret_cast<const f2 *>(la + off);
-            const raw2 bb = (sq.gates & kGateB) ? Ld<In>::splat2(b + th) : Ld<In>::ldraw2(b + off);
-            const raw2 kk = Ld<In>::ldraw2(k + off), qq = Ld<In>::ldraw2(q + off);
+            if constexpr (BSC) br[u] = b[th];
+            else br[u] = Ld<In>::ldraw2(b + off);
+            kr[u] = Ld<In>::ldraw2(k + off);
+            qr[u] = Ld<In>::ldraw2(q + off);
             const f2 z = {0.f, 0.f};
             lv[u] = ok ? x : z;
-            kr[u] = ok ? kk : Ld<In>::zero2();
-            br[u] = ok ? bb : Ld<In>::zero2();
-            qr[u] = ok ? qq : Ld<In>::zero2();
         }
         f2 run = {0.f, 0.f};
 #pragma unroll
@@ -246,7 +255,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             f2 e1, e2;
             e1[0] = __expf(gg[u][0] - mid[0]); e1[1] = __expf(gg[u][1] - mid[1]);
             e2[0] = __expf(mid[0] - gg[u][0]); e2[1] = __expf(mid[1] - gg[u][1]);
-            const f2 kv = Ld<In>::cvt2(kr[u]), bv = Ld<In>::cvt2(br[u]), qv = Ld<In>::cvt2(qr[u]);
+            const float rf = rowf(u);
+            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
             const f2 eh = bv * kv * e1, qh = qv * e1, kb_ = kv * e2;
             sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
             sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
@@ -299,7 +309,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
-            const f2 kv = Ld<In>::cvt2(kr[u]), bv = Ld<In>::cvt2(br[u]), qv = Ld<In>::cvt2(qr[u]);
+            const float rf = rowf(u);
+            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
             const f2 eh = bv * kv * e1[u], qh = qv * e1[u], kb_ = kv * e2[u];
             sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
             sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
@@ -448,7 +459,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             float aA = 0.f, aP = 0.f;
             if (sl <= rl && r < n) {
                 const size_t br_ = ((size_t)(t0 + r) * H + h) * DK, bs = ((size_t)(t0 + s) * H + h) * DK;
-                const bool asc = sq.gates & kGateAlpha, bsc = sq.gates & kGateB;
+                constexpr bool asc = (G & kGateAlpha) != 0, bsc = (G & kGateB) != 0;
                 for (int c = 0; c < DK; ++c) {
                     float d = 0.f;
                     for (int x = s + 1; x <= r; ++x) {
@@ -653,13 +664,14 @@ template <typename In> struct UVTile {
     // the end and zeroes the product where it is used, not here: a select on
     // the loaded values would make the wave wait for this load (and every
     // load issued before it) at once.
-    // `woff` addresses w when it holds one gate per token-head (`wsc`)
-    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, size_t woff, bool wsc, bool ok_) {
+    // `woff` addresses w when it holds one gate per token-head (WSC)
+    template <bool WSC>
+    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, size_t woff, bool ok_) {
         ok = ok_;
         if constexpr (sizeof(In) == 2) {
             uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
             v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
-            if (wsc) {
+            if constexpr (WSC) {
                 const In x = wp[woff];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] = x;
@@ -670,7 +682,7 @@ template <typename In> struct UVTile {
         } else {
             const f4 a = *reinterpret_cast<const f4 *>(vp + off);
             f4 b;
-            if (wsc) { const float x = wp[woff]; b[0] = x; b[1] = x; b[2] = x; b[3] = x; }
+            if constexpr (WSC) { const float x = wp[woff]; b[0] = x; b[1] = x; b[2] = x; b[3] = x; }
             else b = *reinterpret_cast<const f4 *>(wp + off);
 #pragma unroll
             for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
@@ -678,9 +690,6 @@ template <typename In> struct UVTile {
     }
 };
 
-template <typename In> __device__ __forceinline__ float in2f(In x);
-template <> __device__ __forceinline__ float in2f<uint16_t>(uint16_t x) { return bf16f(x); }
-template <> __device__ __forceinline__ float in2f<float>(float x) { return x; }
 
 template <typename Op> __device__ __forceinline__ typename Mma<Op>::frag lds_bfrag(const Op *base, int lane)
 {
@@ -766,7 +775,7 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     __syncthreads();   // drains the line reads before the workgroup ends
 }
 
-template <typename In, typename Op, int DK, int DV, int NC>
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
@@ -931,11 +940,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
         auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
         auto w_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H + h; };
-        const bool wsc = sq.gates & kGateW;
         struct UV { UVTile<In> q[NC]; };
         auto uv_load = [&](UV &u, int c) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q) u.q[q].load(v, w, uv_off(c) + 16 * q, w_off(c), wsc, uv_ok(c));
+            for (int q = 0; q < NC; ++q) u.q[q].template load<WSC>(v, w, uv_off(c) + 16 * q, w_off(c), uv_ok(c));
         };
         OF g0, g1, g2;
         UV u0, u1, u2;
@@ -1082,9 +1090,17 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     const long long chains = (long long)a.N * a.H;
     if (p.max_chunks > 0) {
         prof_before("gdn2_chunk_prep", st);
-        hipLaunchKernelGGL((chunk_prep_kernel<In, Op, DK>), dim3((unsigned)((long long)p.max_chunks * a.H)), dim3(256),
-                           0, st, (const In *)a.q, (const In *)a.k, a.log_alpha, (const In *)a.b, sq, a.H, ops,
-                           prog, (int)chains);
+        const dim3 pg((unsigned)((long long)p.max_chunks * a.H));
+        auto prep = [&](auto kern) {
+            hipLaunchKernelGGL(kern, pg, dim3(256), 0, st, (const In *)a.q, (const In *)a.k, a.log_alpha,
+                               (const In *)a.b, sq, a.H, ops, prog, (int)chains);
+        };
+        switch (a.gates & (kGateB | kGateAlpha)) {
+        case 0: prep(chunk_prep_kernel<In, Op, DK, 0>); break;
+        case kGateB: prep(chunk_prep_kernel<In, Op, DK, kGateB>); break;
+        case kGateAlpha: prep(chunk_prep_kernel<In, Op, DK, kGateAlpha>); break;
+        default: prep(chunk_prep_kernel<In, Op, DK, kGateB | kGateAlpha>); break;
+        }
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -1107,15 +1123,19 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     const long long pass_grid = 8LL * (nsl + npf) * groups;
     if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_before("gdn2_chunk_pass", st);
+    auto pass = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)pass_grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
+                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf);
+    };
+    const bool wsc = a.gates & kGateW;
     if (two) {
-        if constexpr ((DV / 16) % 2 == 0)
-            hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV, 2>), dim3((unsigned)pass_grid), dim3(512), 0, st,
-                               (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
-                               (const uint8_t *)ops, prog, npf);
+        if constexpr ((DV / 16) % 2 == 0) {
+            if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 2, true>);
+            else pass(chunk_pass_kernel<In, Op, DK, DV, 2, false>);
+        }
     } else {
-        hipLaunchKernelGGL((chunk_pass_kernel<In, Op, DK, DV, 1>), dim3((unsigned)pass_grid), dim3(512), 0, st,
-                           (const In *)a.v, (const In *)a.w, a.S0, (float *)a.o, a.ST, sq, a.H,
-                           (const uint8_t *)ops, prog, npf);
+        if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 1, true>);
+        else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false>);
     }
     prof_after(st);
     return hipGetLastError();

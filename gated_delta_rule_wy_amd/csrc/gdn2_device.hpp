@@ -28,6 +28,10 @@ __device__ __forceinline__ int kofs(int g, int i) { return 16 * (i >> 2) + 4 * g
 
 // ---- input element loads (bf16 bit patterns or fp32) -----------------------
 __device__ __forceinline__ float bf16f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+// one input element (bf16 bit pattern or fp32) as float
+template <typename In> __device__ __forceinline__ float in2f(In x);
+template <> __device__ __forceinline__ float in2f<uint16_t>(uint16_t x) { return bf16f(x); }
+template <> __device__ __forceinline__ float in2f<float>(float x) { return x; }
 
 template <typename In> struct Ld;
 template <> struct Ld<uint16_t> {
