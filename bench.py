@@ -131,7 +131,7 @@ def bench_prefill(args, torch, gdn2, gi):
     la1 = la[..., 0].contiguous()
     o1 = torch.empty_like(o)       # keeps o for the parity sample below
     ST1 = torch.empty_like(ST)
-    for fname, (fb, fw, fla) in (('kda', (b1, b1, la)), ('gdn', (b1, b1, la1))):
+    for fname, (fb, fw, fla) in (() if args.no_gate_forms else (('kda', (b1, b1, la)), ('gdn', (b1, b1, la1)))):
         frun = lambda: gdn2.chunk_fwd(q, k, v, fla, fb, fw, S0, out=o1, final_state=ST1, workspace=ws)
         for _ in range(args.warmup):
             frun()
@@ -239,6 +239,8 @@ def main():
     ap.add_argument('--cpu-decode-steps', type=int, default=100)
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--no-decode', action='store_true')
+    ap.add_argument('--no-gate-forms', action='store_true',
+                    help='skip the scalar-gate (KDA, Gated DeltaNet) prefill timings')
     ap.add_argument('--copy-calibration-mib', type=int, default=0,
                     help='only run a plain device copy of this many MiB (x3), to calibrate '
                          'the FETCH_SIZE / WRITE_SIZE counters; prints nothing else')
