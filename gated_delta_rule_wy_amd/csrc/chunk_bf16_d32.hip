@@ -1,0 +1,6 @@
+// Prefill kernels for bf16 inputs and d_k = 32.
+#include "chunk_impl.hpp"
+
+namespace gdn2 {
+template hipError_t dispatch_dv<uint16_t, _Float16, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+}

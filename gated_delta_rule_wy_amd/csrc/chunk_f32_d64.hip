@@ -1,0 +1,6 @@
+// Prefill kernels for fp32 inputs and d_k = 64.
+#include "chunk_impl.hpp"
+
+namespace gdn2 {
+template hipError_t dispatch_dv<float, float, 64>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+}

@@ -1,0 +1,1094 @@
+// Chunkwise (C = 64) WY-form prefill of the Gated Delta Rule-2 on gfx950.
+//
+// Per head and chunk of n <= 64 tokens starting from state S0 (dk x dv), with
+// g_r = sum_{s<=r} log alpha_s per key channel and u_r = w_r * v_r, the
+// token recurrence (snilld.dk, "Hvad Gated DeltaNet-2 ændrer", update
+// equation) unrolls to the chunk form ("Hvad betyder det for træning og
+// inferens": chunkwise WY form with the cumulative channel-wise decay folded
+// into the rank-one erase factors):
+//   A_rs  = sum_c b_rc k_rc k_sc e^{g_rc - g_sc}   (s < r)      Gram / erase
+//   T     = (I + A)^{-1}                                         unit lower
+//   W     = T E,   E_r = b_r * k_r * e^{g_r}                    WY factor
+//   Delta = T U - W S0                                           corrected writes
+//   P_rs  = sum_c q_rc k_sc e^{g_rc - g_sc}        (s <= r)
+//   O     = Q+ S0 + P Delta,   Q+_r = q_r * e^{g_r}
+//   S_n   = Diag(e^{g_n}) S0 + Khat^T Delta,   Khat_s = k_s * e^{g_n - g_s}
+//
+// Two kernels:
+//  * chunk_prep: one workgroup per (chunk, head), all chunks in parallel.
+//    Builds A and P on the matrix cores, inverts I + A in LDS, forms W, and
+//    writes -W, Q+, Khat^T, P, T (as ready-to-use MFMA A-fragments) and
+//    gamma = e^{g_n} to the workspace.
+//  * chunk_pass: one workgroup per (sequence, head, 16-column slice of dv);
+//    walks the sequence's chunks in order with its slice of the state in
+//    registers (fp32). Value columns of S evolve independently because the
+//    transition acts on the key axis only, which is what allows the slicing.
+//
+// Decay factoring. Exponent differences g_r - g_s (s <= r) are <= 0, but
+// the products above are formed as (row factor) x (column factor).
+//  * When the chunk's decay spread is moderate (half spread <= Lim::chunk,
+//    every chunk of ordinary gating), all factors are taken around one
+//    per-channel midpoint and stay within e^{+-Lim::chunk}.
+//  * Otherwise row block R (rows 16R..16R+15) uses ref_R = g_{16R-1}
+//    (0 for R = 0): off-diagonal blocks S < R use
+//    e^{g_r - ref_R} * e^{ref_R - ref_{S+1}} * e^{ref_{S+1} - g_s}, every
+//    factor <= 1, so nothing overflows whatever the decay; diagonal blocks
+//    take factors around the block's middle row, bounded by e^{Lim::v}, and
+//    a block whose decay spread exceeds that is computed exactly (pairwise
+//    exponents) on the vector ALUs instead.
+#pragma once
+
+#include "gdn2_device.hpp"
+#include "gdn2_launch.hpp"
+
+#include <algorithm>
+#include <atomic>
+
+#include <type_traits>
+
+namespace gdn2 {
+
+// Operand block written by chunk_prep for one (chunk, head); every fragment
+// is 64 lanes x 16 bytes in the lane order the consumer loads it.
+template <typename Op, int DK> struct Blk {
+    using M = Mma<Op>;
+    static constexpr int KB = M::KB, NE = M::NE;
+    static constexpr int NKB = DK / KB;   // k-blocks over key channels
+    static constexpr int NSB = 64 / KB;   // k-blocks over chunk rows
+    static constexpr int NCT = DK / 16;   // 16-row tiles over key channels
+    static constexpr size_t FRAG = 64 * 16;
+    static constexpr size_t oW = 0;                          // -W   [4][NKB] frags
+    static constexpr size_t oQ = oW + 4 * NKB * FRAG;        // Q+   [4][NKB]
+    static constexpr size_t oK = oQ + 4 * NKB * FRAG;        // Khat^T [NCT][NSB]
+    // P and T are lower triangular: only the k-blocks sb <= sbmax(mt) of row
+    // tile mt are stored, in row-tile order (tpos)
+    static constexpr __host__ __device__ int sbmax(int mt) { return (16 * mt + 15) / KB; }
+    // closed form (a loop over a runtime mt would stay a loop in the pass)
+    static_assert(KB == 32 || KB == 16, "k-block of 16 or 32 rows");
+    static constexpr __host__ __device__ int tpos(int mt, int sb) {
+        return (KB == 32 ? (mt < 2 ? mt : 2 * mt - 2) : mt * (mt + 1) / 2) + sb;
+    }
+    static constexpr int NTRI = tpos(3, sbmax(3)) + 1;   // stored fragments of P (and of T)
+    static constexpr size_t oP = oK + NCT * NSB * FRAG;      // P    [NTRI]
+    static constexpr size_t oT = oP + NTRI * FRAG;           // T    [NTRI]
+    static constexpr size_t oG = oT + NTRI * FRAG;           // gamma float[DK]
+    static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
+};
+
+// Bounds on decay-factor exponents: `v` for the diagonal blocks of the
+// per-block factoring, `chunk` for the half spread of the chunk-wide one.
+template <typename Op> struct Lim;
+template <> struct Lim<_Float16> { static constexpr float v = 8.0f, chunk = 6.0f; };
+template <> struct Lim<float> { static constexpr float v = 60.0f, chunk = 40.0f; };
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// ---------------------------------------------------------------------------
+
+// Token range and chunk ids with the host-unchecked preconditions made safe:
+// offsets are clamped into [0, Ttot] and chunk ids capped at max_chunks.
+struct Seqs {
+    SeqMap m;
+    int Ttot, max_chunks;
+    int gates;   // kGateB / kGateW / kGateAlpha: per token-head instead of per channel
+    __device__ __forceinline__ int t0(int i) const { return clampi(m.tok0(i), 0, Ttot); }
+    __device__ __forceinline__ int t1(int i) const { return clampi(m.tok1(i), t0(i), Ttot); }
+};
+
+// ---------------------------------------------------------------------------
+// Chunk preparation, one workgroup (4 waves) per (chunk, head).
+//
+// Fast path (the chunk's decay spread is moderate): every exponent is taken
+// around one per-channel midpoint m = (g_first + g_last) / 2, so
+//   E^m_r = b_r k_r e^{g_r - m},  Q^m_r = q_r e^{g_r - m},  K^m_s = k_s e^{m - g_s}
+// are bounded by e^{LIMC} and A = E^m K^mT, P = Q^m K^mT need no per-tile
+// scaling. Otherwise the per-block factoring described at the top of the file
+// is used, with the exact pairwise path for diagonal blocks that need it.
+// All global loads are issued up front and unconditionally (rows past the
+// chunk's end are clamped and zeroed), so the wave waits once.
+template <typename In, typename Op, int DK, int G>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ la,
+    const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops, int *__restrict__ prog, int nprog)
+{
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    using raw2 = typename Ld<In>::raw2;
+    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
+    constexpr int LDE = DK + 4;                 // row stride of the [64][DK] tiles
+    constexpr int LDT = 64 + 4;                 // row stride of the [64][64] tiles
+    constexpr int REG = 64 * (LDE > LDT ? LDE : LDT);
+    constexpr int LDA = 65;
+    constexpr int CP = DK / 2, NRG = 256 / CP, RPG = 64 / NRG;
+    constexpr float LIM = Lim<Op>::v;
+    constexpr float LIMC = Lim<Op>::chunk;
+
+    __shared__ __attribute__((aligned(16))) Op sE[REG];   // E-side operand; later -W staging
+    __shared__ __attribute__((aligned(16))) Op sQ[REG];   // Q-side operand; later P
+    __shared__ __attribute__((aligned(16))) Op sK[REG];   // K-side operand; later T
+    __shared__ float sA[64 * LDA];                        // A (fp32); early: cumsum scratch
+    __shared__ float sTab[19 * DK];
+    __shared__ int sFlag[5];                              // [0,4): exact diagonal blocks; [4]: slow chunk
+
+    // Chunks are dealt last to first, all heads of a chunk together, so the
+    // blocks the pass reads first are the ones written last (the most likely
+    // to still sit in the last-level cache).
+    const int t = threadIdx.x;
+    const int h = (int)(blockIdx.x % (unsigned)H), j = sq.max_chunks - 1 - (int)(blockIdx.x / (unsigned)H);
+    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    if (blockIdx.x == 0)
+        for (int x = t; x < nprog; x += 256) prog[x] = 0;
+    if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
+    const int i = sq.m.seq_of(j);
+    const int t0 = sq.t0(i) + 64 * (j - sq.m.chunk0(i));
+    const int n = min(64, sq.t1(i) - t0);
+    uint8_t *blk = ops + ((size_t)h * sq.max_chunks + j) * L::bytes;
+
+    // tables (rows of DK floats): [0,4) Q+/E scale per row block; [4,8) Khat
+    // scale per row block; [8,11) e^{ref_R - ref_{S+1}} for (R,S) = (2,0),
+    // (3,0), (3,1); [11,15) e^{ref_R - mid_R}; [15,19) e^{mid_R - ref_{R+1}}.
+    // The fast path uses rows 0 and 4 for every block.
+    float *tExpRef = sTab, *tExpKh = sTab + 4 * DK, *tDec = sTab + 8 * DK;
+    float *tDiagE = sTab + 11 * DK, *tDiagK = sTab + 15 * DK;
+
+    // ---- stage 1: all loads, cumulative log-decay g, references ----
+    const int cp = t % CP, rg = t / CP, c0 = 2 * cp, r0 = rg * RPG;
+    float *sPart = sA;                  // [NRG][DK]
+    float *sRef = sA + NRG * DK;        // [5][DK]: ref_0..ref_4 (ref_4 = g_n)
+    float *sMid = sRef + 5 * DK;        // [4][DK]
+    float *sG0 = sMid + 4 * DK;         // [DK]: g at the chunk's first row
+    f2 gg[RPG];
+    // raw k, b, q of the thread's rows; rows past the chunk's end are zeroed
+    // where the values are used (rowf), not here, so no load waits early
+    constexpr bool BSC = (G & kGateB) != 0;   // b: one value per token-head
+    raw2 kr[RPG], qr[RPG];
+    typename std::conditional<BSC, In, raw2>::type br[RPG];
+    auto bf2 = [&](int u) {
+        if constexpr (BSC) { const float x = in2f<In>(br[u]); f2 r = {x, x}; return r; }
+        else return Ld<In>::cvt2(br[u]);
+    };
+    auto rowf = [&](int u) { return r0 + u < n ? 1.f : 0.f; };
+    {
+        f2 lv[RPG];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int r = r0 + u;
+            const bool ok = r < n;
+            const size_t th = (size_t)(t0 + min(r, n - 1)) * H + h, off = th * DK + c0;
+            // G (compile time): which gates hold one value per token-head
+            f2 x;
+            if constexpr ((G & kGateAlpha) != 0) { const float a1 = la[th]; x[0] = a1; x[1] = a1; }
+            else x = *reinterpret_cast<const f2 *>(la + off);
+            if constexpr (BSC) br[u] = b[th];
+            else br[u] = Ld<In>::ldraw2(b + off);
+            kr[u] = Ld<In>::ldraw2(k + off);
+            qr[u] = Ld<In>::ldraw2(q + off);
+            const f2 z = {0.f, 0.f};
+            lv[u] = ok ? x : z;
+        }
+        f2 run = {0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) { run += lv[u]; gg[u] = run; }
+        *reinterpret_cast<f2 *>(sPart + rg * DK + c0) = run;
+    }
+    if (t < 5) sFlag[t] = 0;
+    __syncthreads();
+    {
+        f2 pre = {0.f, 0.f};
+        for (int q2 = 0; q2 < rg; ++q2) pre += *reinterpret_cast<const f2 *>(sPart + q2 * DK + c0);
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            gg[u] += pre;
+            const int r = r0 + u;
+            if ((r & 15) == 15) *reinterpret_cast<f2 *>(sRef + ((r + 1) >> 4) * DK + c0) = gg[u];
+            if ((r & 15) == 7) *reinterpret_cast<f2 *>(sMid + (r >> 4) * DK + c0) = gg[u];
+            if (r == 0) *reinterpret_cast<f2 *>(sG0 + c0) = gg[u];
+        }
+        if (rg == 0) { sRef[c0] = 0.f; sRef[c0 + 1] = 0.f; }
+    }
+    __syncthreads();
+    for (int c = t; c < DK; c += 256)
+        if (0.5f * (sG0[c] - sRef[4 * DK + c]) > LIMC) atomicOr(&sFlag[4], 1);
+    __syncthreads();
+    const bool fast = sFlag[4] == 0;
+
+    // ---- stage 2: decay factors, gamma, scaled operands in LDS ----
+    if (t < DK) reinterpret_cast<float *>(blk + L::oG)[t] = __expf(sRef[4 * DK + t]);
+    if (fast) {
+        for (int c = t; c < DK; c += 256) {
+            const float gn = sRef[4 * DK + c], mid = 0.5f * (sG0[c] + gn);
+            tExpRef[c] = __expf(mid);
+            tExpKh[c] = __expf(gn - mid);
+        }
+        const f2 mid = 0.5f * (*reinterpret_cast<const f2 *>(sG0 + c0) + *reinterpret_cast<const f2 *>(sRef + 4 * DK + c0));
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int r = r0 + u;
+            f2 e1, e2;
+            e1[0] = __expf(gg[u][0] - mid[0]); e1[1] = __expf(gg[u][1] - mid[1]);
+            e2[0] = __expf(mid[0] - gg[u][0]); e2[1] = __expf(mid[1] - gg[u][1]);
+            const float rf = rowf(u);
+            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
+            const f2 eh = bv * kv * e1, qh = qv * e1, kb_ = kv * e2;
+            sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
+            sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
+            sK[r * LDE + c0] = (Op)kb_[0]; sK[r * LDE + c0 + 1] = (Op)kb_[1];
+        }
+    } else {
+        for (int idx = t; idx < 4 * DK; idx += 256) {
+            const int R = idx / DK, c = idx % DK;
+            const float rR = sRef[R * DK + c], rR1 = sRef[(R + 1) * DK + c];
+            const float mid = sMid[R * DK + c], gn = sRef[4 * DK + c];
+            tExpRef[R * DK + c] = __expf(rR);
+            tExpKh[R * DK + c] = __expf(gn - rR1);
+            const float de = rR - mid, dq = mid - rR1;
+            tDiagE[R * DK + c] = __expf(de);
+            tDiagK[R * DK + c] = __expf(dq);
+            if (fmaxf(de, dq) > LIM) atomicOr(&sFlag[R], 1);
+            if (R < 3) {
+                const int Rr = R == 0 ? 2 : 3, Ss = R == 2 ? 1 : 0;
+                tDec[R * DK + c] = __expf(sRef[Rr * DK + c] - sRef[(Ss + 1) * DK + c]);
+            }
+        }
+        // e1_r = e^{g_r - ref_R} forward, e2_r = e^{ref_{R+1} - g_r} backward,
+        // as running products of alpha within the 16-row block
+        f2 al[RPG], e1[RPG], e2[RPG];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const f2 gprev = u ? gg[u - 1] : gg[0];
+            al[u][0] = __expf(u ? gg[u][0] - gprev[0] : 0.f);
+            al[u][1] = __expf(u ? gg[u][1] - gprev[1] : 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int r = r0 + u;
+            if (u == 0 || (r & 15) == 0) {
+                const float *ref = sRef + (r >> 4) * DK + c0;
+                e1[u][0] = __expf(gg[u][0] - ref[0]);
+                e1[u][1] = __expf(gg[u][1] - ref[1]);
+            } else e1[u] = e1[u - 1] * al[u];
+        }
+#pragma unroll
+        for (int u = RPG - 1; u >= 0; --u) {
+            const int r = r0 + u;
+            if ((r & 15) == 15) { e2[u][0] = 1.f; e2[u][1] = 1.f; }
+            else if (u == RPG - 1) {
+                const float *ref = sRef + ((r >> 4) + 1) * DK + c0;
+                e2[u][0] = __expf(ref[0] - gg[u][0]);
+                e2[u][1] = __expf(ref[1] - gg[u][1]);
+            } else e2[u] = e2[u + 1] * al[u + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int r = r0 + u;
+            const float rf = rowf(u);
+            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
+            const f2 eh = bv * kv * e1[u], qh = qv * e1[u], kb_ = kv * e2[u];
+            sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
+            sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
+            sK[r * LDE + c0] = (Op)kb_[0]; sK[r * LDE + c0 + 1] = (Op)kb_[1];
+        }
+    }
+    __syncthreads();
+    // Q+ / E scale of row block R, Khat scale of row block S
+    const int tabR = fast ? 0 : 1;   // table row step per block
+
+    // ---- stage 3: A and P blocks on the matrix cores; pack Q+ and Khat^T ----
+    for (int idx = t; idx < 6 * 256; idx += 256) {   // strictly-upper blocks of A
+        const int bi = idx >> 8, e = idx & 255;
+        const int R = bi < 3 ? 0 : (bi < 5 ? 1 : 2);
+        const int S = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
+        sA[(16 * R + (e >> 4)) * LDA + 16 * S + (e & 15)] = 0.f;
+    }
+    const bool any_slow = !fast && (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]);
+    f4 pacc[5];
+    int ptile[5];
+    if (fast) {
+        // waves 0,1 build A, waves 2,3 build P; wave parity picks the row
+        // blocks {0,3} or {1,2}, five 16x16 blocks each
+        const int kind = wv >> 1, par = wv & 1;
+        const Op *src = kind ? sQ : sE;
+#pragma unroll
+        for (int qq = 0; qq < 5; ++qq) {
+            const int R = par ? (qq < 2 ? 1 : 2) : (qq == 0 ? 0 : 3);
+            const int S = par ? (qq < 2 ? qq : qq - 2) : (qq == 0 ? 0 : qq - 1);
+            f4 acc = f4zero();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = M::mma(lds_row_frag<Op>(src + (16 * R + m16) * LDE, kb * KB, g4),
+                             lds_row_frag<Op>(sK + (16 * S + m16) * LDE, kb * KB, g4), acc);
+            if (kind == 0) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    sA[(16 * R + rr) * LDA + 16 * S + m16] = (R > S || rr > m16) ? acc[ii] : 0.f;
+                }
+                ptile[qq] = -1;
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    acc[ii] = (R > S || rr >= m16) ? acc[ii] : 0.f;
+                }
+                ptile[qq] = (R * (R + 1)) / 2 + S;
+            }
+            pacc[qq] = acc;
+        }
+    } else {
+        // wave wv takes jobs wv + 4*qq: ids 0..9 are the A blocks, 10..19 the P blocks
+#pragma unroll
+        for (int qq = 0; qq < 5; ++qq) {
+            const int jb = wv + 4 * qq;
+            const int kind = jb / 10, tile = jb % 10;
+            const int R = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int S = tile - (R * (R + 1)) / 2;
+            ptile[qq] = -1;
+            pacc[qq] = f4zero();
+            if (R == S && sFlag[R]) continue;   // exact path below
+            const Op *src = kind ? sQ : sE;
+            f4 acc = f4zero();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                frag a, bb;
+#pragma unroll
+                for (int i4 = 0; i4 < NE; ++i4) {
+                    const int ch = kb * KB + kofs(g4, i4);
+                    float av = (float)src[(16 * R + m16) * LDE + ch];
+                    float bvv = (float)sK[(16 * S + m16) * LDE + ch];
+                    if (R == S) { av *= tDiagE[R * DK + ch]; bvv *= tDiagK[R * DK + ch]; }
+                    else if (R > S + 1) bvv *= tDec[(R == 2 ? 0 : (S == 0 ? 1 : 2)) * DK + ch];
+                    a[i4] = (Op)av;
+                    bb[i4] = (Op)bvv;
+                }
+                acc = M::mma(a, bb, acc);
+            }
+            if (kind == 0) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    sA[(16 * R + rr) * LDA + 16 * S + m16] = (R > S || rr > m16) ? acc[ii] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int rr = 4 * g4 + ii;
+                    acc[ii] = (R > S || rr >= m16) ? acc[ii] : 0.f;
+                }
+                pacc[qq] = acc;
+                ptile[qq] = tile;
+            }
+        }
+    }
+    // Q+ fragments: rows 16 mt + m, channels kb*KB + kofs, scaled to e^{g_r}
+    for (int f = wv; f < 4 * NKB; f += 4) {
+        const int mt = f / NKB, kb = f % NKB;
+        const frag x = lds_row_frag<Op>(sQ + (16 * mt + m16) * LDE, kb * KB, g4);
+        const float *sc = tExpRef + mt * tabR * DK + kb * KB;
+        frag a;
+#pragma unroll
+        for (int i4 = 0; i4 < NE; ++i4) a[i4] = (Op)((float)x[i4] * sc[kofs(g4, i4)]);
+        *reinterpret_cast<frag *>(blk + L::oQ + ((size_t)f * 64 + lane) * 16) = a;
+    }
+    // Khat^T fragments: rows = channel 16 ct + m, contraction = chunk rows
+    for (int f = wv; f < NCT * NSB; f += 4) {
+        const int ct = f / NSB, sb = f % NSB;
+        const int c = 16 * ct + m16;
+        frag a;
+#pragma unroll
+        for (int i4 = 0; i4 < NE; ++i4) {
+            const int s = sb * KB + kofs(g4, i4);
+            a[i4] = (Op)((float)sK[s * LDE + c] * tExpKh[(s >> 4) * tabR * DK + c]);
+        }
+        *reinterpret_cast<frag *>(blk + L::oK + ((size_t)f * 64 + lane) * 16) = a;
+    }
+    __syncthreads();
+
+    // ---- stage 4: P into LDS (over Q^), exact diagonal blocks if needed ----
+    Op *sP = sQ, *sT = sK, *sW = sE;
+    for (int idx = t; idx < 6 * 256; idx += 256) {
+        const int bi = idx >> 8, e = idx & 255;
+        const int R = bi < 3 ? 0 : (bi < 5 ? 1 : 2);
+        const int S = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
+        sP[(16 * R + (e >> 4)) * LDT + 16 * S + (e & 15)] = (Op)0.f;
+        sT[(16 * R + (e >> 4)) * LDT + 16 * S + (e & 15)] = (Op)0.f;
+    }
+#pragma unroll
+    for (int s3 = 0; s3 < 5; ++s3) {
+        if (ptile[s3] < 0) continue;
+        const int tile = ptile[s3];
+        const int R = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+        const int S = tile - (R * (R + 1)) / 2;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            sP[(16 * R + 4 * g4 + ii) * LDT + 16 * S + m16] = (Op)pacc[s3][ii];
+    }
+    if (any_slow) {
+        // exact pairwise exponents for flagged diagonal blocks (strong decay)
+        for (int R = 0; R < 4; ++R) {
+            if (!sFlag[R]) continue;
+            const int rl = t >> 4, sl = t & 15;
+            const int r = 16 * R + rl, s = 16 * R + sl;
+            float aA = 0.f, aP = 0.f;
+            if (sl <= rl && r < n) {
+                const size_t br_ = ((size_t)(t0 + r) * H + h) * DK, bs = ((size_t)(t0 + s) * H + h) * DK;
+                constexpr bool asc = (G & kGateAlpha) != 0, bsc = (G & kGateB) != 0;
+                for (int c = 0; c < DK; ++c) {
+                    float d = 0.f;
+                    for (int x = s + 1; x <= r; ++x) {
+                        const size_t th = (size_t)(t0 + x) * H + h;
+                        d += la[asc ? th : th * DK + c];
+                    }
+                    const float e = __expf(d) * Ld<In>::one(k + bs + c);
+                    const float bv = Ld<In>::one(b + (bsc ? (size_t)(t0 + r) * H + h : br_ + c));
+                    aA += bv * Ld<In>::one(k + br_ + c) * e;
+                    aP += Ld<In>::one(q + br_ + c) * e;
+                }
+            }
+            sA[r * LDA + s] = sl < rl ? aA : 0.f;
+            sP[r * LDT + s] = (Op)aP;
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 5: T = (I + A)^{-1}, block forward substitution ----
+    {
+        const int R = wv;
+        if (lane < 16) {
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < r; ++s) acc -= sA[(16 * R + r) * LDA + 16 * R + s] * x[s];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[(16 * R + r) * LDT + 16 * R + lane] = (Op)x[r];
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        if (wv < 4 - d) {
+            const int S = wv, R = S + d;
+            f4 y = f4zero();
+            for (int J = S; J < R; ++J) {
+                f4 a, bb;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    a[ii] = sA[(16 * R + m16) * LDA + 16 * J + 4 * g4 + ii];
+                    bb[ii] = (float)sT[(16 * J + 4 * g4 + ii) * LDT + 16 * S + m16];
+                }
+                y = M::mma16(a, bb, y);
+            }
+            f4 a;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) a[ii] = (float)sT[(16 * R + m16) * LDT + 16 * R + 4 * g4 + ii];
+            const f4 z = M::mma16(a, y, f4zero());
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sT[(16 * R + 4 * g4 + ii) * LDT + 16 * S + m16] = (Op)(-z[ii]);
+        }
+        __syncthreads();
+    }
+
+    // ---- stage 6: W = T E (E = stored E-side operand x e^{ref}); pack -W, P, T ----
+    // wave wv takes output column tiles nt = wv, wv+4, ...; T fragments are
+    // shared across them, E column fragments across the row tiles
+    constexpr int NWT = (NCT + 3) / 4;
+    frag tf[4][NSB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+            if (sb <= (16 * mt + 15) / KB) tf[mt][sb] = lds_row_frag<Op>(sT + (16 * mt + m16) * LDT, sb * KB, g4);
+    f4 wacc[NWT][4];
+#pragma unroll
+    for (int qq = 0; qq < NWT; ++qq) {
+        const int nt = wv + 4 * qq;
+        if (nt >= NCT) continue;
+        const int c = 16 * nt + m16;
+        frag eb[NSB];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int i4 = 0; i4 < NE; ++i4) {
+                const int s = sb * KB + kofs(g4, i4);
+                eb[sb][i4] = (Op)((float)sE[s * LDE + c] * tExpRef[(s >> 4) * tabR * DK + c]);
+            }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f4 acc = f4zero();
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+                if (sb <= (16 * mt + 15) / KB) acc = M::mma(tf[mt][sb], eb[sb], acc);
+            wacc[qq][mt] = acc;
+        }
+    }
+    // P and T fragments (the nonzero k-blocks only)
+    for (int f = wv; f < 4 * NSB; f += 4) {
+        const int mt = f / NSB, sb = f % NSB;
+        if (sb > L::sbmax(mt)) continue;
+        const int pos = L::tpos(mt, sb);
+        *reinterpret_cast<frag *>(blk + L::oP + ((size_t)pos * 64 + lane) * 16) =
+            lds_row_frag<Op>(sP + (16 * mt + m16) * LDT, sb * KB, g4);
+        *reinterpret_cast<frag *>(blk + L::oT + ((size_t)pos * 64 + lane) * 16) =
+            lds_row_frag<Op>(sT + (16 * mt + m16) * LDT, sb * KB, g4);
+    }
+    __syncthreads();   // every read of the E-side operand done
+#pragma unroll
+    for (int qq = 0; qq < NWT; ++qq) {
+        const int nt = wv + 4 * qq;
+        if (nt >= NCT) continue;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                sW[(16 * mt + 4 * g4 + ii) * LDE + 16 * nt + m16] = (Op)(-wacc[qq][mt][ii]);
+    }
+    __syncthreads();
+    for (int f = wv; f < 4 * NKB; f += 4) {
+        const int mt = f / NKB, kb = f % NKB;
+        *reinterpret_cast<frag *>(blk + L::oW + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sW + (16 * mt + m16) * LDE, kb * KB, g4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential state pass.
+//
+// Workgroup = (chain = sequence*H + head, 16-column slice of dv), 8 waves in
+// two roles:
+//  * state waves 0..3 carry the recurrence. Wave w owns rows 16w..16w+15 of
+//    each chunk's Delta and state tiles [w*TPW, (w+1)*TPW) (16 key channels
+//    each), fp32 in registers:
+//        Delta_w = T_w U - W_w S;   S_tile <- gamma * S_tile + Khat^T_tile Delta
+//  * output waves 4..7 stage U = w*v (hi + lo f16) into LDS and compute
+//        O_w = Q+_w S + P_w Delta
+//    off the serial path.
+// Per chunk, two barriers: (1) state tiles and U in LDS, (2) Delta in LDS.
+// Each role loads its operand fragments two chunks ahead into a ring of
+// three register sets; the loads are unconditional (clamped chunk index) so
+// the compiler waits only for the chunk at hand. A compute unit streams
+// operand bytes at ~60 B/cycle, so the loads are placed where each role would
+// otherwise wait at a barrier: the state waves issue half after writing
+// Delta and half after the state update, the output waves right after
+// barrier (1). The output tile goes through LDS and leaves as one 16-byte
+// store per thread.
+//
+// Workgroups are numbered so that the slices of one chain land on the same
+// XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), where they
+// share that XCD's L2 for the chain's operand blocks.
+template <typename Op, int DK> struct StateFrags {
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    static constexpr int TPW = (L::NCT + 3) / 4;
+    frag nW[L::NKB], Ti[L::NSB], Kh[TPW][L::NSB];
+    f4 gam[TPW];
+    // first half: what the Delta step needs (T fragments above the diagonal are zero and skipped)
+    __device__ __forceinline__ void load_a(const uint8_t *blk, int wv, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+            nW[kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
+        const int sbmax = (16 * wv + 15) / M::KB;
+#pragma unroll
+        for (int sb = 0; sb < L::NSB; ++sb)
+            if (sb <= sbmax)
+                Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)L::tpos(wv, sb) * 64 + lane) * 16);
+    }
+    // second half: what the state update needs
+    __device__ __forceinline__ void load_b(const uint8_t *blk, int wv, int lane) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int ct = wv * TPW + u;
+            if (L::NCT % 4 == 0 || ct < L::NCT) {   // static when all waves own tiles
+                gam[u] = *reinterpret_cast<const f4 *>(blk + L::oG + (size_t)(16 * ct + 4 * (lane >> 4)) * 4);
+#pragma unroll
+                for (int sb = 0; sb < L::NSB; ++sb)
+                    Kh[u][sb] = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)(ct * L::NSB + sb) * 64 + lane) * 16);
+            }
+        }
+    }
+};
+
+template <typename Op, int DK> struct OutFrags {
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    frag Qp[L::NKB], Pm[L::NSB];
+    __device__ __forceinline__ void load(const uint8_t *blk, int wo, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wo * L::NKB + kb) * 64 + lane) * 16);
+        const int sbmax = (16 * wo + 15) / M::KB;   // P is lower triangular
+#pragma unroll
+        for (int sb = 0; sb < L::NSB; ++sb)
+            if (sb <= sbmax)
+                Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)L::tpos(wo, sb) * 64 + lane) * 16);
+    }
+};
+
+// v and w for one chunk and column slice: output-wave thread t (0..255)
+// holds row t/4, columns 4*(t%4)..+3 of both.
+template <typename In> struct UVTile {
+    In v[4], w[4];
+    bool ok;
+    // `off` always addresses a valid row; `ok` false stands for a row past
+    // the end and zeroes the product where it is used, not here: a select on
+    // the loaded values would make the wave wait for this load (and every
+    // load issued before it) at once.
+    // `woff` addresses w when it holds one gate per token-head (WSC)
+    template <bool WSC>
+    __device__ __forceinline__ void load(const In *vp, const In *wp, size_t off, size_t woff, bool ok_) {
+        ok = ok_;
+        if constexpr (sizeof(In) == 2) {
+            uint2 a = *reinterpret_cast<const uint2 *>(vp + off);
+            v[0] = (In)(a.x & 0xFFFF); v[1] = (In)(a.x >> 16); v[2] = (In)(a.y & 0xFFFF); v[3] = (In)(a.y >> 16);
+            if constexpr (WSC) {
+                const In x = wp[woff];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = x;
+            } else {
+                uint2 b = *reinterpret_cast<const uint2 *>(wp + off);
+                w[0] = (In)(b.x & 0xFFFF); w[1] = (In)(b.x >> 16); w[2] = (In)(b.y & 0xFFFF); w[3] = (In)(b.y >> 16);
+            }
+        } else {
+            const f4 a = *reinterpret_cast<const f4 *>(vp + off);
+            f4 b;
+            if constexpr (WSC) { const float x = wp[woff]; b[0] = x; b[1] = x; b[2] = x; b[3] = x; }
+            else b = *reinterpret_cast<const f4 *>(wp + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = a[e]; w[e] = b[e]; }
+        }
+    }
+};
+
+
+template <typename Op> __device__ __forceinline__ typename Mma<Op>::frag lds_bfrag(const Op *base, int lane)
+{
+    // B fragment of a KB-deep block from KB/16 consecutive accumulator-layout tiles
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    typename Mma<Op>::frag f;
+#pragma unroll
+    for (int p = 0; p < Mma<Op>::KB / 16; ++p) {
+        const op4 x = *reinterpret_cast<const op4 *>(base + (p * 64 + lane) * 4);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) f[4 * p + ii] = x[ii];
+    }
+    return f;
+}
+
+template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, int lane, const f4 &x)
+{
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    op4 y;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) y[ii] = (Op)x[ii];
+    *reinterpret_cast<op4 *>(dst + lane * 4) = y;
+}
+
+// L2 prefetch workgroups. A pass workgroup holds a bounded number of
+// cache-line requests in flight, so its step time grows with the latency of
+// the level its operands come from. When the chip has workgroup slots to
+// spare, each chain gets `npf` extra workgroups on the same XCD that read
+// the chain's upcoming operand blocks and v / w rows a few chunks ahead of
+// the pass, so that the pass finds them in that XCD's L2. Wave k of such a
+// workgroup takes chunks k, k + 8, ...: it reads the chain's progress
+// counter (chunks finished by the pass's first slice), waits while it is
+// more than 3 + kPfWindow chunks ahead, skips chunks closer than 3, and
+// reads one dword per line of its share of the chunk straight into an LDS
+// scratch area that nothing reads (so no register waits for a line; the
+// counter read waits only for this wave's reads of 8 chunks before). Every
+// loop and wait is bounded, and the pass never waits for these workgroups.
+static constexpr int kPfWindow = 8;
+static constexpr int kPfMaxSleeps = 64;
+
+typedef const __attribute__((address_space(1))) void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+
+template <typename In, int DV, size_t BYTES>
+__device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
+                                              int chain, int h, int H, int pf, int npf, int nch, int tb, int te,
+                                              int gates)
+{
+    constexpr int NL = (int)(BYTES / 128);                        // block lines
+    constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
+    constexpr int RL = (RB + 127) / 128;                          // lines per row
+    // lines per chunk: the block, then the v rows and (per-channel gates) the w rows
+    const int PL = NL + ((gates & kGateW) ? 1 : 2) * 64 * RL;
+    constexpr int NW = 8;                                         // waves
+    __shared__ uint32_t sSink[NW * 64];
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    lptr_t scratch = (lptr_t)(sSink + wv * 64);
+    auto done = [&]() {
+        return __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(prog + chain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    };
+    for (int c = wv; c < nch; c += NW) {
+        int d = done();
+        for (int s = 0; c > d + 3 + kPfWindow && s < kPfMaxSleeps; ++s) {
+            __builtin_amdgcn_s_sleep(4);
+            d = done();
+        }
+        while (c < d + 3) c += NW;
+        if (c >= nch) break;
+        for (int l = pf + npf * lane; l < PL; l += npf * 64) {
+            const uint8_t *a;
+            if (l < NL) {
+                a = blk0 + (size_t)c * BYTES + (size_t)l * 128;
+            } else {
+                const int k = l - NL, which = k / (64 * RL), row = (k / RL) % 64, part = k % RL;
+                const int tok = min(tb + 64 * c + row, te - 1);
+                a = reinterpret_cast<const uint8_t *>(which ? w : v) + ((size_t)tok * H + h) * RB +
+                    min(part * 128, RB - 4);
+            }
+            __builtin_amdgcn_global_load_lds((gptr_t)a, scratch, 4, 0, 0);
+        }
+    }
+    __syncthreads();   // drains the line reads before the workgroup ends
+}
+
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC>
+__global__ __launch_bounds__(512) void chunk_pass_kernel(
+    const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
+    float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
+    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf)
+{
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    using SF = StateFrags<Op, DK>;
+    using OF = OutFrags<Op, DK>;
+    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
+    constexpr int TPW = SF::TPW;
+    constexpr int TPK = KB / 16;              // accumulator tiles per k-block
+    constexpr int NSL = DV / (16 * NC);       // column slices (workgroups per chain)
+    constexpr int PD = 2;                     // prefetch distance (register ring of 3)
+    static_assert(NSL >= 1 && NSL * 16 * NC == DV, "slice width must divide dv");
+
+    // per 16-column tile q of the slice
+    __shared__ __attribute__((aligned(16))) Op sS[NC][NCT * 64 * 4];        // state operand tiles
+    __shared__ __attribute__((aligned(16))) Op sD[NC][4 * 64 * 4];          // Delta tiles
+    __shared__ __attribute__((aligned(16))) Op sU[NC][2 * NSB * 64 * NE];   // U hi / lo B-fragments
+    constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
+    __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];          // o tiles
+
+    // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
+    // sit on XCD c % 8
+    const int Lid = blockIdx.x;
+    const int kq = Lid >> 3, role = kq % (NSL + npf), js = role;
+    const int chain = (kq / (NSL + npf)) * 8 + (Lid & 7);
+    const int chains = sq.m.N * H;
+    if (chain >= chains) return;
+    const int i = chain / H, h = chain % H;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int col0 = 16 * NC * js;            // first value column of the slice
+    const size_t sbase = ((size_t)i * H + h) * DK * DV;
+    const int tb = sq.t0(i), te = sq.t1(i);
+    const int cbeg = sq.m.chunk0(i);
+    const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
+    auto blk_of = [&](int c) { return ops + ((size_t)h * sq.max_chunks + cbeg + min(c, nch - 1)) * L::bytes; };
+    if (role >= NSL) {
+        pass_prefetch<In, DV, L::bytes>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain, h,
+                                        H, role - NSL, npf, nch, tb, te, sq.gates);
+        return;
+    }
+    const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
+
+    if (wv < 4) {
+        // ------------------------------------------------ state waves
+        // the serial chain runs here: these waves win issue ties on their SIMD
+        __builtin_amdgcn_s_setprio(3);
+        f4 Sr[NC][TPW];
+#pragma unroll
+        for (int q = 0; q < NC; ++q)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                Sr[q][u] = f4zero();
+                if (ct < NCT) {
+                    if (S0) {
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            Sr[q][u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16];
+                    }
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
+                }
+            }
+        const int sbmax = (16 * wv + 15) / KB;
+        SF f0, f1, f2;
+        if (nch > 0) {
+            f0.load_a(blk_of(0), wv, lane);
+            f0.load_b(blk_of(0), wv, lane);
+            f1.load_a(blk_of(1), wv, lane);
+            f1.load_b(blk_of(1), wv, lane);
+        }
+        // The prefetch of chunk c+2 is split over the two windows in which
+        // the state waves would otherwise wait for the output waves.
+        auto step = [&](int c, SF &cur, SF &pre) {
+            __syncthreads();   // (1) state tiles and U ready
+            f4 acc[NC], accw[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) { acc[q] = f4zero(); accw[q] = f4zero(); }
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                if (sb > sbmax) break;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
+                    const frag ul = *reinterpret_cast<const frag *>(&sU[q][((1 * NSB + sb) * 64 + lane) * NE]);
+                    acc[q] = M::mma(cur.Ti[sb], uh, acc[q]);
+                    acc[q] = M::mma(cur.Ti[sb], ul, acc[q]);
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    accw[q] = M::mma(cur.nW[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), accw[q]);
+#pragma unroll
+            for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sD[q] + wv * 256, lane, acc[q] + accw[q]);
+            pre.load_a(blk_of(c + PD), wv, lane);
+            __syncthreads();   // (2) Delta tiles ready
+            frag Db[NC][NSB];
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) Db[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    f4 s = Sr[q][u] * cur.gam[u];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                    Sr[q][u] = s;
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
+                }
+            }
+            pre.load_b(blk_of(c + PD), wv, lane);
+            // A device-scope store is written through to memory and, since
+            // stores and loads retire in order, would hold up this wave's
+            // later operand waits; the prefetch workgroups sit on the same
+            // XCD and read the counter from the shared L2.
+            if (report) __hip_atomic_store(prog + chain, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
+        // Full rounds of three steps carry no branches, so the register ring
+        // needs no merge copies (a copy of a register with a load in flight
+        // waits for that load and every load issued before it).
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
+            step(c, f0, f2);
+            step(c + 1, f1, f0);
+            step(c + 2, f2, f1);
+        }
+        if (c < nch) step(c, f0, f2);
+        if (c + 1 < nch) step(c + 1, f1, f0);
+        __syncthreads();   // final: pairs with the output waves' last o tile
+        if (ST) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (ct >= NCT) continue;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = Sr[q][u][ii];
+                }
+        }
+    } else {
+        // ------------------------------------------------ output waves
+        const int wo = wv - 4, to = t - 256;
+        const int sbmax = (16 * wo + 15) / KB;
+        // v / w tile coordinates of this thread (per column tile) and where its U values go
+        const int ur = to >> 2, uc = 4 * (to & 3);
+        const size_t uoff0 = (size_t)h * DV + col0 + uc;
+        const int usb = ur / KB, usl = ur % KB;
+        const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
+        auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
+        auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
+        auto w_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H + h; };
+        struct UV { UVTile<In> q[NC]; };
+        auto uv_load = [&](UV &u, int c) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q) u.q[q].template load<WSC>(v, w, uv_off(c) + 16 * q, w_off(c), uv_ok(c));
+        };
+        OF g0, g1, g2;
+        UV u0, u1, u2;
+        if (nch > 0) {
+            g0.load(blk_of(0), wo, lane);
+            uv_load(u0, 0);
+            g1.load(blk_of(1), wo, lane);
+            uv_load(u1, 1);
+        }
+        // o tiles go through LDS (double-buffered) and leave as 16-byte
+        // stores (NC per thread) after the next barrier
+        auto store_o = [&](int c) {
+            const int tok = tb + 64 * c, n = min(64, te - tok);
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const int x = to + 256 * q, row = x / (4 * NC), q4 = x % (4 * NC);
+                if (row < n)
+                    *reinterpret_cast<f4 *>(o + ((size_t)(tok + row) * H + h) * DV + col0 + 4 * q4) =
+                        *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
+            }
+        };
+        auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &upre) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const UVTile<In> &uq = ucur.q[q];
+                    const float uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                    const Op hi = (Op)uu;
+                    const int ln = (uc + e) + 16 * ug;
+                    sU[q][((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
+                    sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+                }
+            __syncthreads();   // (1)
+            pre.load(blk_of(c + PD), wo, lane);
+            uv_load(upre, c + PD);
+            if (c > 0) store_o(c - 1);
+            f4 oacc[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) oacc[q] = f4zero();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    oacc[q] = M::mma(cur.Qp[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), oacc[q]);
+            __syncthreads();   // (2)
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                if (sb > sbmax) break;
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    oacc[q] = M::mma(cur.Pm[sb], lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane), oacc[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + 16 * q + m16] = oacc[q][ii];
+        };
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
+            step(c, g0, g2, u0, u2);
+            step(c + 1, g1, g0, u1, u0);
+            step(c + 2, g2, g1, u2, u1);
+        }
+        if (c < nch) step(c, g0, g2, u0, u2);
+        if (c + 1 < nch) step(c + 1, g1, g0, u1, u0);
+        __syncthreads();   // final
+        if (nch > 0) store_o(nch - 1);
+    }
+}
+
+
+static constexpr int kMaxPrefetchWgs = 4;   // more gave no gain, and a full chip leaves no slack
+
+// compute units of the current device, queried once per device
+static hipError_t device_cus(int *cus)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cached[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return hipSuccess;
+}
+
+template <typename In, typename Op, int DK, int DV>
+static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st)
+{
+    uint8_t *ws = (uint8_t *)a.workspace;
+    Seqs sq;
+    sq.m.cu = a.cu_seqlens;
+    sq.m.co = a.cu_seqlens ? (const int32_t *)ws : nullptr;
+    sq.m.N = a.N;
+    sq.m.T = a.T;
+    sq.Ttot = a.cu_seqlens ? a.T : a.B * a.T;
+    sq.max_chunks = p.max_chunks;
+    sq.gates = a.gates;
+    hipError_t err = hipSuccess;
+    int *prog = (int *)(ws + p.plan_bytes);
+    uint8_t *ops = ws + p.plan_bytes + p.prog_bytes;
+    const long long chains = (long long)a.N * a.H;
+    if (p.max_chunks > 0) {
+        prof_before("gdn2_chunk_prep", st);
+        const dim3 pg((unsigned)((long long)p.max_chunks * a.H));
+        auto prep = [&](auto kern) {
+            hipLaunchKernelGGL(kern, pg, dim3(256), 0, st, (const In *)a.q, (const In *)a.k, a.log_alpha,
+                               (const In *)a.b, sq, a.H, ops, prog, (int)chains);
+        };
+        switch (a.gates & (kGateB | kGateAlpha)) {
+        case 0: prep(chunk_prep_kernel<In, Op, DK, 0>); break;
+        case kGateB: prep(chunk_prep_kernel<In, Op, DK, kGateB>); break;
+        case kGateAlpha: prep(chunk_prep_kernel<In, Op, DK, kGateAlpha>); break;
+        default: prep(chunk_prep_kernel<In, Op, DK, kGateB | kGateAlpha>); break;
+        }
+        prof_after(st);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    // One 16-column tile per workgroup with L2 prefetch workgroups where the
+    // grid stays resident at one workgroup per compute unit; two tiles per
+    // workgroup where one tile would oversubscribe the chip (half the
+    // workgroups, each streaming the same operand blocks once for twice the
+    // columns), with prefetch workgroups if the halved grid leaves room.
+    int cus = 0;
+    if ((err = device_cus(&cus)) != hipSuccess) return err;
+    const long long groups = (chains + 7) / 8;
+    auto npf_for = [&](int nsl) {
+        int n = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - nsl);
+        return (n < 2 || p.max_chunks == 0) ? 0 : n;
+    };
+    constexpr int NSL1 = DV / 16;
+    const bool two = (DV / 16) % 2 == 0 && 8LL * NSL1 * groups > cus;
+    const int nsl = two ? NSL1 / 2 : NSL1;
+    const int npf = npf_for(nsl);
+    const long long pass_grid = 8LL * (nsl + npf) * groups;
+    if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    prof_before("gdn2_chunk_pass", st);
+    auto pass = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)pass_grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
+                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf);
+    };
+    const bool wsc = a.gates & kGateW;
+    if (two) {
+        if constexpr ((DV / 16) % 2 == 0) {
+            if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 2, true>);
+            else pass(chunk_pass_kernel<In, Op, DK, DV, 2, false>);
+        }
+    } else {
+        if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 1, true>);
+        else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false>);
+    }
+    prof_after(st);
+    return hipGetLastError();
+}
+
+template <typename In, typename Op, int DK>
+hipError_t dispatch_dv(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st)
+{
+    switch (a.dv) {
+    case 16: return launch_t<In, Op, DK, 16>(a, p, st);
+    case 32: return launch_t<In, Op, DK, 32>(a, p, st);
+    case 64: return launch_t<In, Op, DK, 64>(a, p, st);
+    case 128: return launch_t<In, Op, DK, 128>(a, p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace gdn2
