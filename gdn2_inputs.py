@@ -215,3 +215,145 @@ def workload(name: str, threads: int = 8) -> Prefill:
                        collapsed=c['collapsed'], uniform=False, threads=threads)
     return prefill(c['seed'], [c['T']] * c['B'], c['H'], c['dk'], c['dv'], c['dtype'],
                    c['s0_std'], uniform=True, threads=threads)
+
+
+# ---- inputs for the fused prologue (ShortConv, L2 norm, sigmoid gates) ----
+# Raw inputs are what the projections would hand the mixer: q, k, v before
+# the short convolution and the gate logits before the sigmoid.
+#
+# Recipe:
+# * per (sequence i, 1024-token block j) stream ``default_rng([seed, i, j, 3])``
+#   drawing, each ``[block_len, H, d]``: q_raw, k_raw, v_raw ~ N(0, 1),
+#   x_alpha ~ N(-3, 1) (log_alpha = -softplus(x_alpha), float32), b and w
+#   logits ~ N(0, 1);
+# * convolution taps ~ U(-1/2, 1/2) ``[H*d, 4]`` and biases ~ U(-1/2, 1/2)
+#   ``[H*d]`` for q, k, v in that order from ``default_rng([seed, 2**23])``
+#   (the default initialisation bound of a one-channel, kernel-4 convolution);
+# * convolution history (three raw inputs before each sequence's start, oldest
+#   first) ~ N(0, 1) ``[H, 3, d]`` per sequence, q, k, v in that order, from
+#   ``default_rng([seed, i, 2**24])``;
+# * bf16 workloads round the raw inputs, logits and history to bf16 (taps,
+#   biases and log_alpha stay float32).
+# Decode: the step-s stream ``default_rng([seed, 2**25, s])`` draws q_raw,
+# k_raw, v_raw, x_alpha, b and w logits ``[N, H, d]``; the resident state
+# and the history come from ``default_rng([seed, 2**25, 0])``.
+
+CONV_K = 4
+
+
+@dataclasses.dataclass
+class PrologueBatch:
+    q_raw: np.ndarray             # [tokens, H, dk]
+    k_raw: np.ndarray
+    v_raw: np.ndarray             # [tokens, H, dv]
+    log_alpha: np.ndarray         # [tokens, H, dk] float32
+    b_logit: np.ndarray           # [tokens, H, dk]
+    w_logit: np.ndarray           # [tokens, H, dv]
+    conv_w: dict                  # 'q','k','v' -> [H*d, 4] float32
+    conv_b: Optional[dict]        # 'q','k','v' -> [H*d] float32, or None
+    conv_in: Optional[dict]       # 'q','k','v' -> [N, H, 3, d], or None (zeros)
+    S0: Optional[np.ndarray]
+    cu_seqlens: np.ndarray
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+    varlen: bool
+
+    @property
+    def N(self) -> int:
+        return len(self.cu_seqlens) - 1
+
+    @property
+    def tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def conv_params(seed: int, H: int, dk: int, dv: int, bias: bool = True):
+    rng = np.random.default_rng([seed, 2 ** 23])
+    f = np.float32
+    w = {n: rng.uniform(-0.5, 0.5, (H * d, CONV_K)).astype(f) for n, d in (('q', dk), ('k', dk), ('v', dv))}
+    b = {n: rng.uniform(-0.5, 0.5, H * d).astype(f) for n, d in (('q', dk), ('k', dk), ('v', dv))}
+    return w, (b if bias else None)
+
+
+def _conv_history(seed, i, H, dk, dv, dtype):
+    rng = np.random.default_rng([seed, i, 2 ** 24])
+    f = np.float32
+    h = {n: rng.standard_normal((H, CONV_K - 1, d), dtype=f) for n, d in (('q', dk), ('k', dk), ('v', dv))}
+    if dtype == 'bf16':
+        h = {n: bf16_round(a) for n, a in h.items()}
+    return h
+
+
+def prologue_prefill(seed: int, lengths, H: int, dk: int, dv: int, dtype: str = 'bf16',
+                     s0_std: float = 0.0, uniform: bool = True, conv_bias: bool = True,
+                     conv_history: bool = False, threads: int = 8) -> PrologueBatch:
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    total = int(cu[-1])
+    names = (('q', dk), ('k', dk), ('v', dv), ('la', dk), ('xb', dk), ('xw', dv))
+    out = {name: np.empty((total, H, d), np.float32) for name, d in names}
+    jobs = []
+    for i, L in enumerate(lengths):
+        for j in range(0, (L + BLOCK - 1) // BLOCK):
+            jobs.append((i, j, int(cu[i]) + j * BLOCK, min(BLOCK, L - j * BLOCK)))
+
+    def run(job):
+        i, j, t0, n = job
+        rng = np.random.default_rng([seed, i, j, 3])
+        f = np.float32
+        arrs = {name: rng.standard_normal((n, H, d), dtype=f) for name, d in names}
+        arrs['la'] = -_softplus(arrs['la'] - f(3.0))
+        if dtype == 'bf16':
+            for name in ('q', 'k', 'v', 'xb', 'xw'):
+                arrs[name] = bf16_round(arrs[name])
+        for name, a in arrs.items():
+            out[name][t0:t0 + n] = a
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(run, jobs))
+    cw, cb = conv_params(seed, H, dk, dv, conv_bias)
+    conv_in = None
+    if conv_history:
+        hs = [_conv_history(seed, i, H, dk, dv, dtype) for i in range(len(lengths))]
+        conv_in = {n: np.stack([h[n] for h in hs]) for n in ('q', 'k', 'v')}
+    S0 = None
+    if s0_std > 0:
+        S0 = np.empty((len(lengths), H, dk, dv), np.float32)
+        for i in range(len(lengths)):
+            rng = np.random.default_rng([seed, i, 2 ** 20])
+            S0[i] = rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    if uniform:
+        assert len(set(lengths)) == 1
+    return PrologueBatch(q_raw=out['q'], k_raw=out['k'], v_raw=out['v'], log_alpha=out['la'],
+                         b_logit=out['xb'], w_logit=out['xw'], conv_w=cw, conv_b=cb, conv_in=conv_in,
+                         S0=S0, cu_seqlens=cu, B=len(lengths) if uniform else 1,
+                         T=lengths[0] if uniform else total, H=H, dk=dk, dv=dv, dtype=dtype,
+                         varlen=not uniform)
+
+
+def prologue_decode_state(seed: int, N: int, H: int, dk: int, dv: int, dtype: str = 'bf16',
+                          s0_std: float = 0.02):
+    """(S [N, H, dk, dv] float32, conv history dict 'q','k','v' -> [N, H, 3, d])."""
+    rng = np.random.default_rng([seed, 2 ** 25, 0])
+    f = np.float32
+    S = rng.standard_normal((N, H, dk, dv), dtype=f) * f(s0_std)
+    h = {n: rng.standard_normal((N, H, CONV_K - 1, d), dtype=f) for n, d in (('q', dk), ('k', dk), ('v', dv))}
+    if dtype == 'bf16':
+        h = {n: bf16_round(a) for n, a in h.items()}
+    return S, h
+
+
+def prologue_decode_step(seed: int, step: int, N: int, H: int, dk: int, dv: int, dtype: str = 'bf16'):
+    """(q_raw, k_raw, v_raw, log_alpha, b_logit, w_logit), each [N, H, d]."""
+    rng = np.random.default_rng([seed, 2 ** 25, step])
+    f = np.float32
+    arrs = [rng.standard_normal((N, H, d), dtype=f) for d in (dk, dk, dv, dk, dk, dv)]
+    arrs[3] = -_softplus(arrs[3] - f(3.0))
+    if dtype == 'bf16':
+        arrs = [a if i == 3 else bf16_round(a) for i, a in enumerate(arrs)]
+    return tuple(arrs)

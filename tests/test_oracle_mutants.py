@@ -56,3 +56,48 @@ def test_some_pin_catches(tmp_path, name, old, new):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f'no pin catches the planted mistake "{name}"'
+
+
+# ---- the prologue oracle (numpy): planted mistakes in a copy of its source
+import importlib.util
+
+import oracle.prologue
+import prologue_pins
+
+PRO_SRC = oracle.prologue.__file__
+
+PRO_MUTANTS = [
+    ('conv taps reversed', 'acc += wt[:, :, j] * ext[t + j]', 'acc += wt[:, :, KERNEL - 1 - j] * ext[t + j]'),
+    ('conv bias dropped', 'acc = bs.copy()', 'acc = np.zeros_like(bs)'),
+    ('conv history ignored', 'before = np.transpose(np.asarray(history, dtype=np.float64)[i], (1, 0, 2))',
+     'before = np.zeros((HIST, H, d))'),
+    ('history taken from the start', 'hist_out[i] = np.transpose(ext[-HIST:], (1, 0, 2))',
+     'hist_out[i] = np.transpose(ext[:HIST], (1, 0, 2))'),
+    ('norm over the token axis', 'n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))',
+     'n = np.sqrt(np.sum(x * x, axis=0, keepdims=True))'),
+    ('norm not square-rooted', 'n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))',
+     'n = np.sum(x * x, axis=-1, keepdims=True)'),
+    ('sigmoid of -x', 'np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))',
+     'np.where(x >= 0, e / (1.0 + e), 1.0 / (1.0 + e))'),
+    ('v normalised too', "return q, k, out['v'], sigmoid(b_logit)", "return q, k, l2_normalize(out['v']), sigmoid(b_logit)"),
+    ('k left unnormalised', "k = l2_normalize(out['k'])", "k = out['k']"),
+]
+
+
+@pytest.mark.parametrize('name,old,new', PRO_MUTANTS, ids=[m[0] for m in PRO_MUTANTS])
+def test_some_prologue_pin_catches(tmp_path, name, old, new):
+    src = open(PRO_SRC).read()
+    assert old in src, name
+    path = tmp_path / 'prologue_mutant.py'
+    path.write_text(src.replace(old, new, 1))
+    spec = importlib.util.spec_from_file_location('oracle.prologue_mutant', str(path))
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = 'oracle'
+    spec.loader.exec_module(mod)
+    caught = []
+    for pin in prologue_pins.ALL:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f'no pin catches the planted mistake "{name}"'

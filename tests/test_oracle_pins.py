@@ -53,3 +53,12 @@ def test_threads_do_not_change_results():
     a = oracle.forward(q, k, v, la, b, w, B=4, nthreads=1)
     c = oracle.forward(q, k, v, la, b, w, B=4, nthreads=5)
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+import oracle.prologue as prologue_oracle
+import prologue_pins
+
+
+@pytest.mark.parametrize('pin', prologue_pins.ALL, ids=[p.__name__ for p in prologue_pins.ALL])
+def test_prologue_pin(pin):
+    pin(prologue_oracle)
