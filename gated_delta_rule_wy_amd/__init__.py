@@ -30,7 +30,15 @@ CHUNK = 64
 EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
            'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_gates',
            'gdn2_decode_step', 'gdn2_decode_step_gates',
+           'gdn2_chunk_fwd_prologue', 'gdn2_decode_step_prologue',
            'gdn2_profile_begin', 'gdn2_profile_end', 'gdn2_profile_kernel')
+
+
+class ShortConv(ctypes.Structure):
+    """gdn2_short_conv: taps, biases and history of the three short convolutions."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        'weight_q', 'weight_k', 'weight_v', 'bias_q', 'bias_k', 'bias_v',
+        'state_in_q', 'state_in_k', 'state_in_v', 'state_out_q', 'state_out_k', 'state_out_v')]
 
 
 class Gdn2Error(RuntimeError):
@@ -60,6 +68,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn2_decode_step.restype = i
     lib.gdn2_decode_step_gates.argtypes = [vp] * 6 + [i] + [vp] * 2 + [i] * 6
     lib.gdn2_decode_step_gates.restype = i
+    pc = ctypes.POINTER(ShortConv)
+    lib.gdn2_chunk_fwd_prologue.argtypes = [vp] * 6 + [pc] + [vp] * 4 + [i] * 8 + [vp, sz]
+    lib.gdn2_chunk_fwd_prologue.restype = i
+    lib.gdn2_decode_step_prologue.argtypes = [vp] * 6 + [pc] + [vp] * 2 + [i] * 6
+    lib.gdn2_decode_step_prologue.restype = i
     lib.gdn2_profile_begin.argtypes = [i]
     lib.gdn2_profile_begin.restype = i
     lib.gdn2_profile_end.argtypes = []
@@ -235,4 +248,126 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
                                      _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
     if st != GDN2_OK:
         raise Gdn2Error(st, 'gdn2_decode_step_gates')
+    return out
+
+
+def _short_conv(H, dk, dv, dev, dt, lead_n, weight, bias, state_in, state_out) -> ShortConv:
+    """Marshal (q, k, v) triples of taps, biases and histories into a ShortConv."""
+    dims = (dk, dk, dv)
+    if weight is None or len(weight) != 3:
+        raise ValueError('conv_weight must be a (q, k, v) triple of [H*d, 4] float32 tensors')
+    sc = ShortConv()
+    for n, t, d in zip('qkv', weight, dims):
+        _check(t, f'conv_weight[{n}]', (H * d, 4), torch.float32, dev)
+        setattr(sc, f'weight_{n}', t.data_ptr())
+    if bias is not None:
+        for n, t, d in zip('qkv', bias, dims):
+            if t is not None:
+                _check(t, f'conv_bias[{n}]', (H * d,), torch.float32, dev)
+                setattr(sc, f'bias_{n}', t.data_ptr())
+    for label, trip in (('in', state_in), ('out', state_out)):
+        if trip is None:
+            continue
+        for n, t, d in zip('qkv', trip, dims):
+            _check(t, f'conv_state_{label}[{n}]', (lead_n, H, 3, d), dt, dev)
+            setattr(sc, f'state_{label}_{n}', t.data_ptr())
+    return sc
+
+
+def chunk_fwd_prologue(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor, log_alpha: torch.Tensor,
+                       b_logit: torch.Tensor, w_logit: torch.Tensor, conv_weight, conv_bias=None,
+                       S0: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                       conv_state=None, conv_state_out=None, output_conv_state: bool = True,
+                       out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                       output_final_state: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Prefill on the projections' outputs, with the prologue fused in:
+    q = L2Norm(ShortConv(q_raw)), k = L2Norm(ShortConv(k_raw)), v = ShortConv(v_raw),
+    b = sigmoid(b_logit), w = sigmoid(w_logit).
+
+    Shapes as in ``chunk_fwd`` (gates per channel). conv_weight: (q, k, v) taps
+    [H*dk, 4], [H*dk, 4], [H*dv, 4] float32, tap 3 on the current token;
+    conv_bias: such a triple of [H*d] (entries may be None) or None.
+    conv_state: (q, k, v) histories [N, H, 3, d] in the input dtype (the
+    three raw inputs before each sequence, oldest first) or None for zeros.
+    conv_state_out: tensors to receive the new histories (may be conv_state
+    itself); allocated when None and ``output_conv_state``.
+    Returns (o, S_T or None, conv_state_out triple or None).
+    """
+    if q_raw.dim() != 4:
+        raise ValueError('q_raw must be [B, T, H, dk]')
+    B, T, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    dev, dt = q_raw.device, q_raw.dtype
+    code = _dtype_code(q_raw)
+    for name, t, d in (('q_raw', q_raw, dk), ('k_raw', k_raw, dk), ('v_raw', v_raw, dv),
+                       ('b_logit', b_logit, dk), ('w_logit', w_logit, dv)):
+        _check(t, name, (B, T, H, d), dt, dev)
+    _check(log_alpha, 'log_alpha', (B, T, H, dk), torch.float32, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+            raise ValueError('cu_seqlens must be a 1-D int32 tensor on the same device')
+        if not cu_seqlens.is_contiguous():
+            raise ValueError('cu_seqlens must be contiguous')
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _check(S0, 'S0', (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(out, 'out', (B, T, H, dv), torch.float32, dev)
+    ST = None
+    if final_state is not None:
+        _check(final_state, 'final_state', (N, H, dk, dv), torch.float32, dev)
+        ST = final_state
+    elif output_final_state:
+        ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_state_out is None and output_conv_state:
+        conv_state_out = tuple(torch.empty((N, H, 3, d), dtype=dt, device=dev) for d in (dk, dk, dv))
+    sc = _short_conv(H, dk, dv, dev, dt, N, conv_weight, conv_bias, conv_state, conv_state_out)
+    varlen = cu_seqlens is not None
+    need = _lib.gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen))
+    if need == 0:
+        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, 'gdn2_chunk_fwd_workspace_bytes')
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    set_stream()
+    st = _lib.gdn2_chunk_fwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(log_alpha), _ptr(b_logit),
+                                      _ptr(w_logit), ctypes.byref(sc), _ptr(S0), _ptr(out), _ptr(ST),
+                                      _ptr(cu_seqlens), B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size())
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_chunk_fwd_prologue')
+    return out, ST, conv_state_out
+
+
+def decode_step_prologue(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor, log_alpha: torch.Tensor,
+                         b_logit: torch.Tensor, w_logit: torch.Tensor, S: torch.Tensor, conv_weight,
+                         conv_bias=None, conv_state=None, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence on raw inputs ([N, H, d]), prologue fused in.
+    S [N, H, dk, dv] float32 and the conv_state histories ((q, k, v) triple
+    of [N, H, 3, d], or None for zeros) are updated in place. Returns o."""
+    if q_raw.dim() != 3:
+        raise ValueError('q_raw must be [N, H, dk]')
+    N, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    dev, dt = q_raw.device, q_raw.dtype
+    code = _dtype_code(q_raw)
+    for name, t, d in (('q_raw', q_raw, dk), ('k_raw', k_raw, dk), ('v_raw', v_raw, dv),
+                       ('b_logit', b_logit, dk), ('w_logit', w_logit, dv)):
+        _check(t, name, (N, H, d), dt, dev)
+    _check(log_alpha, 'log_alpha', (N, H, dk), torch.float32, dev)
+    _check(S, 'S', (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(out, 'out', (N, H, dv), torch.float32, dev)
+    sc = _short_conv(H, dk, dv, dev, dt, N, conv_weight, conv_bias, conv_state, conv_state)
+    set_stream()
+    st = _lib.gdn2_decode_step_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(log_alpha), _ptr(b_logit),
+                                        _ptr(w_logit), ctypes.byref(sc), _ptr(S), _ptr(out), N, H, dk, dv, code,
+                                        GDN2_F32)
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_decode_step_prologue')
     return out

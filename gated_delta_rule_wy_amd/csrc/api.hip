@@ -183,11 +183,33 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                                 N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes);
 }
 
-int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
-                         const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
-                         const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
-                         size_t workspace_bytes)
+// The convolution parameters of a *_prologue call: weights required, biases
+// optional, history in / out each all-or-none.
+static int conv_args(const gdn2_short_conv *c, gdn2::Prologue *p)
+{
+    if (!c) return GDN2_ERR_INVALID;
+    const void *req[] = {c->weight_q, c->weight_k, c->weight_v};
+    for (const void *x : req)
+        if (!x || !aligned16(x)) return GDN2_ERR_INVALID;
+    const void *opt[] = {c->bias_q, c->bias_k, c->bias_v, c->state_in_q, c->state_in_k, c->state_in_v,
+                         c->state_out_q, c->state_out_k, c->state_out_v};
+    for (const void *x : opt)
+        if (x && !aligned16(x)) return GDN2_ERR_INVALID;
+    const int nin = !!c->state_in_q + !!c->state_in_k + !!c->state_in_v;
+    const int nout = !!c->state_out_q + !!c->state_out_k + !!c->state_out_v;
+    if ((nin != 0 && nin != 3) || (nout != 0 && nout != 3)) return GDN2_ERR_INVALID;
+    p->on = true;
+    p->q = {c->weight_q, c->bias_q, c->state_in_q, c->state_out_q};
+    p->k = {c->weight_k, c->bias_k, c->state_in_k, c->state_out_k};
+    p->v = {c->weight_v, c->bias_v, c->state_in_v, c->state_out_v};
+    return GDN2_OK;
+}
+
+static int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const void *b, const void *w, int gates, const gdn2_short_conv *conv, const float *S0,
+                          void *o, float *ST, const int32_t *cu_seqlens, int B, int T, int N, int H, int dk,
+                          int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                          size_t workspace_bytes)
 {
     if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     gdn2::ChunkPlan plan;
@@ -200,9 +222,10 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
     const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, o, ST, cu_seqlens, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_INVALID;
+    gdn2::ChunkArgs a;
+    if (conv && (st = conv_args(conv, &a.pro)) != GDN2_OK) return st;
     if (!workspace || workspace_bytes < plan.total_bytes) return GDN2_ERR_WORKSPACE;
 
-    gdn2::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
     a.log_alpha = log_alpha;
     a.S0 = S0;
@@ -219,6 +242,27 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
     return GDN2_OK;
 }
 
+int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
+                         const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                         size_t workspace_bytes)
+{
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, gates, nullptr, S0, o, ST, cu_seqlens, B, T, N, H, dk, dv,
+                          in_dtype, out_dtype, workspace, workspace_bytes);
+}
+
+int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
+                            const void *b_logit, const void *w_logit, const gdn2_short_conv *conv,
+                            const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B, int T,
+                            int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                            void *workspace, size_t workspace_bytes)
+{
+    if (!conv) return GDN2_ERR_INVALID;
+    return chunk_fwd_impl(q_raw, k_raw, v_raw, log_alpha, b_logit, w_logit, GDN2_GATES_PER_CHANNEL, conv, S0, o,
+                          ST, cu_seqlens, B, T, N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes);
+}
+
 int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
                      int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
@@ -227,9 +271,9 @@ int gdn2_decode_step(const void *q, const void *k, const void *v, const float *l
                                   out_dtype);
 }
 
-int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
-                           const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
-                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+static int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                       const void *b, const void *w, int gates, const gdn2_short_conv *conv, float *S, void *o,
+                       int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
 {
     if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
@@ -241,6 +285,8 @@ int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const fl
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return GDN2_ERR_INVALID;
     gdn2::DecodeArgs a;
+    int st;
+    if (conv && (st = conv_args(conv, &a.pro)) != GDN2_OK) return st;
     a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
     a.log_alpha = log_alpha;
     a.S = S;
@@ -251,6 +297,22 @@ int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const fl
     prof_call();
     if (gdn2::launch_decode(a, g_stream) != hipSuccess) return GDN2_ERR_HIP;
     return GDN2_OK;
+}
+
+int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
+                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+{
+    return decode_impl(q, k, v, log_alpha, b, w, gates, nullptr, S, o, N, H, dk, dv, in_dtype, out_dtype);
+}
+
+int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
+                              const void *b_logit, const void *w_logit, const gdn2_short_conv *conv, float *S,
+                              void *o, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+{
+    if (!conv) return GDN2_ERR_INVALID;
+    return decode_impl(q_raw, k_raw, v_raw, log_alpha, b_logit, w_logit, GDN2_GATES_PER_CHANNEL, conv, S, o, N, H,
+                       dk, dv, in_dtype, out_dtype);
 }
 
 } // extern "C"

@@ -73,7 +73,80 @@ bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varl
     return true;
 }
 
+static hipError_t launch_chunk_fwd_kernels(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st);
+
+// Convolution history after a prefill (fused prologue): for each sequence
+// and head, the last three raw inputs of q, k and v, reaching back into the
+// history given at the start when the sequence is shorter than three tokens.
+// One workgroup per (sequence, head) reads every value it writes before
+// writing any, so the history out may alias the history in.
+struct HistOut {
+    const void *x[3];         // raw q, k, v [tokens][H][d]
+    const void *in[3];        // history in [N][H][3][d] or null (zeros)
+    void *out[3];             // history out
+    int d[3];
+};
+
+template <typename In>
+__global__ __launch_bounds__(256) void conv_hist_kernel(HistOut hp, Seqs sq, int H)
+{
+    constexpr int NT = 256, MAXE = 3 * 3 * 128 / NT + 1;
+    const int nh = blockIdx.x, i = nh / H, h = nh % H, t = threadIdx.x;
+    const int tb = sq.t0(i), L = sq.t1(i) - tb;
+    const int e0 = 3 * hp.d[0], e1 = e0 + 3 * hp.d[1], e2 = e1 + 3 * hp.d[2];
+    In val[MAXE];
+#pragma unroll
+    for (int m = 0; m < MAXE; ++m) {
+        const int e = t + m * NT;
+        if (e >= e2) break;
+        const int x = e < e0 ? 0 : (e < e1 ? 1 : 2);
+        const int le = e - (x == 0 ? 0 : (x == 1 ? e0 : e1)), d = hp.d[x];
+        const int j = le / d, c = le % d, p = L - 3 + j;   // token p of the sequence
+        const In *hin = (const In *)hp.in[x];
+        if (p >= 0) val[m] = ((const In *)hp.x[x])[((size_t)(tb + p) * H + h) * d + c];
+        else val[m] = hin ? hin[((size_t)nh * 3 + 3 + p) * d + c] : (In)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXE; ++m) {
+        const int e = t + m * NT;
+        if (e >= e2) break;
+        const int x = e < e0 ? 0 : (e < e1 ? 1 : 2);
+        const int le = e - (x == 0 ? 0 : (x == 1 ? e0 : e1)), d = hp.d[x];
+        ((In *)hp.out[x])[(size_t)nh * 3 * d + le] = val[m];
+    }
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st)
+{
+    hipError_t err = launch_chunk_fwd_kernels(a, p, st);
+    if (err != hipSuccess || !a.pro.on || !a.pro.q.hist_out) return err;
+    Seqs sq;
+    sq.m.cu = a.cu_seqlens;
+    sq.m.co = nullptr;
+    sq.m.N = a.N;
+    sq.m.T = a.T;
+    sq.Ttot = a.cu_seqlens ? a.T : a.B * a.T;
+    sq.max_chunks = p.max_chunks;
+    sq.gates = 0;
+    HistOut hp;
+    const ConvTensor *ct[3] = {&a.pro.q, &a.pro.k, &a.pro.v};
+    const void *xs[3] = {a.q, a.k, a.v};
+    const int ds[3] = {a.dk, a.dk, a.dv};
+    for (int x = 0; x < 3; ++x) {
+        hp.x[x] = xs[x];
+        hp.in[x] = ct[x]->hist_in;
+        hp.out[x] = ct[x]->hist_out;
+        hp.d[x] = ds[x];
+    }
+    prof_before("gdn2_conv_state", st);
+    if (a.bf16) hipLaunchKernelGGL(conv_hist_kernel<uint16_t>, dim3(a.N * a.H), dim3(256), 0, st, hp, sq, a.H);
+    else hipLaunchKernelGGL(conv_hist_kernel<float>, dim3(a.N * a.H), dim3(256), 0, st, hp, sq, a.H);
+    prof_after(st);
+    return hipGetLastError();
+}
+
+static hipError_t launch_chunk_fwd_kernels(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st)
 {
     if (a.cu_seqlens) {
         prof_before("gdn2_chunk_plan", st);

@@ -85,6 +85,15 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 
 // ---------------------------------------------------------------------------
 
+// Short convolution of one raw input (fused prologue), device pointers:
+// taps [H*d][4] (tap 3 on the current token), bias [H*d] or null, history
+// [N][H][3][d] in the input type (oldest first) or null for zeros.
+struct ConvIn {
+    const float *w;
+    const float *bias;
+    const void *hist;
+};
+
 // Token range and chunk ids with the host-unchecked preconditions made safe:
 // offsets are clamped into [0, Ttot] and chunk ids capped at max_chunks.
 struct Seqs {
@@ -106,11 +115,19 @@ struct Seqs {
 // is used, with the exact pairwise path for diagonal blocks that need it.
 // All global loads are issued up front and unconditionally (rows past the
 // chunk's end are clamped and zeroed), so the wave waits once.
-template <typename In, typename Op, int DK, int G>
+//
+// PRO (fused prologue): q, k and b arrive raw. Each thread also loads the
+// three rows before its first one (the previous chunk's, or the history
+// before a sequence's start), applies the short convolution, scales q and k
+// to unit norm (a sum over the row's lanes) and takes the sigmoid of b, all
+// where the values are used.
+template <typename In, typename Op, int DK, int G, bool PRO>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const float *__restrict__ la,
-    const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops, int *__restrict__ prog, int nprog)
+    const In *__restrict__ b, Seqs sq, int H, uint8_t *__restrict__ ops, int *__restrict__ prog, int nprog,
+    ConvIn cq, ConvIn ck)
 {
+    static_assert(!PRO || G == 0, "the prologue takes per-channel gates");
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
@@ -162,13 +179,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // raw k, b, q of the thread's rows; rows past the chunk's end are zeroed
     // where the values are used (rowf), not here, so no load waits early
     constexpr bool BSC = (G & kGateB) != 0;   // b: one value per token-head
-    raw2 kr[RPG], qr[RPG];
+    constexpr int XO = PRO ? 3 : 0;             // raw rows before the first (convolution)
+    raw2 kr[RPG + XO], qr[RPG + XO];            // row r0 + x - XO in slot x
     typename std::conditional<BSC, In, raw2>::type br[RPG];
     auto bf2 = [&](int u) {
         if constexpr (BSC) { const float x = in2f<In>(br[u]); f2 r = {x, x}; return r; }
         else return Ld<In>::cvt2(br[u]);
     };
     auto rowf = [&](int u) { return r0 + u < n ? 1.f : 0.f; };
+    float hz[XO > 0 ? XO : 1];      // PRO: 0 for a row before the start with no history
+    f4 cwq[2], cwk[2];              // PRO: taps of columns c0, c0 + 1
+    f2 cbq, cbk;                    // PRO: biases
     {
         f2 lv[RPG];
 #pragma unroll
@@ -182,10 +203,41 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             else x = *reinterpret_cast<const f2 *>(la + off);
             if constexpr (BSC) br[u] = b[th];
             else br[u] = Ld<In>::ldraw2(b + off);
-            kr[u] = Ld<In>::ldraw2(k + off);
-            qr[u] = Ld<In>::ldraw2(q + off);
+            if constexpr (!PRO) {
+                kr[u] = Ld<In>::ldraw2(k + off);
+                qr[u] = Ld<In>::ldraw2(q + off);
+            }
             const f2 z = {0.f, 0.f};
             lv[u] = ok ? x : z;
+        }
+        if constexpr (PRO) {
+            // rows r0-3 .. r0+RPG-1; a row before the sequence's start reads
+            // the history (zeroed at use when there is none)
+            const int tb = sq.t0(i);
+            const In *hq = (const In *)cq.hist, *hk = (const In *)ck.hist;
+#pragma unroll
+            for (int x = 0; x < RPG + XO; ++x) {
+                const int rr = r0 + x - XO, rc = min(rr, n - 1);
+                const bool before = t0 + rr < tb;
+                const In *sq_ = q, *sk_ = k;
+                size_t off = ((size_t)(t0 + max(rc, tb - t0)) * H + h) * DK + c0;
+                if (before && hq) {
+                    sq_ = hq;
+                    sk_ = hk;
+                    off = ((size_t)(i * H + h) * 3 + 3 + rr) * DK + c0;
+                }
+                qr[x] = Ld<In>::ldraw2(sq_ + off);
+                kr[x] = Ld<In>::ldraw2(sk_ + off);
+                if (x < XO) hz[x] = (before && !hq) ? 0.f : 1.f;
+            }
+            const size_t wo = (size_t)h * DK + c0;
+            cwq[0] = *reinterpret_cast<const f4 *>(cq.w + 4 * wo);
+            cwq[1] = *reinterpret_cast<const f4 *>(cq.w + 4 * wo + 4);
+            cwk[0] = *reinterpret_cast<const f4 *>(ck.w + 4 * wo);
+            cwk[1] = *reinterpret_cast<const f4 *>(ck.w + 4 * wo + 4);
+            // without a bias, read the taps (any valid address) and zero at use
+            cbq = *reinterpret_cast<const f2 *>(cq.bias ? cq.bias + wo : cq.w + 4 * wo);
+            cbk = *reinterpret_cast<const f2 *>(ck.bias ? ck.bias + wo : ck.w + 4 * wo);
         }
         f2 run = {0.f, 0.f};
 #pragma unroll
@@ -213,6 +265,47 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     __syncthreads();
     const bool fast = sFlag[4] == 0;
 
+    // the thread's q, k (rows past the chunk's end zeroed) and b values
+    f2 qp[PRO ? RPG : 1], kp[PRO ? RPG : 1];
+    if constexpr (PRO) {
+        const float bfq = cq.bias ? 1.f : 0.f, bfk = ck.bias ? 1.f : 0.f;
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            f2 yq = cbq * bfq, yk = cbk * bfk;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                const int x = u + jt;   // slot of row r0 + u - 3 + jt
+                f2 xq = Ld<In>::cvt2(qr[x]), xk = Ld<In>::cvt2(kr[x]);
+                if (x < XO) { xq *= hz[x < XO ? x : 0]; xk *= hz[x < XO ? x : 0]; }
+                yq[0] += cwq[0][jt] * xq[0]; yq[1] += cwq[1][jt] * xq[1];
+                yk[0] += cwk[0][jt] * xk[0]; yk[1] += cwk[1][jt] * xk[1];
+            }
+            const float nq = lane_group_sum<CP>(yq[0] * yq[0] + yq[1] * yq[1]);
+            const float nk = lane_group_sum<CP>(yk[0] * yk[0] + yk[1] * yk[1]);
+            // 1 / max(norm, 1e-12)
+            const float rf = rowf(u);
+            qp[u] = yq * (rsqrtf(fmaxf(nq, 1e-24f)) * rf);
+            kp[u] = yk * (rsqrtf(fmaxf(nk, 1e-24f)) * rf);
+        }
+    }
+    auto qval = [&](int u) {
+        if constexpr (PRO) return qp[u];
+        else return Ld<In>::cvt2(qr[u]) * rowf(u);
+    };
+    auto kval = [&](int u) {
+        if constexpr (PRO) return kp[u];
+        else return Ld<In>::cvt2(kr[u]) * rowf(u);
+    };
+    auto bval = [&](int u) {
+        if constexpr (PRO) {
+            const f2 x = bf2(u);
+            f2 r;
+            r[0] = 1.f / (1.f + __expf(-x[0]));
+            r[1] = 1.f / (1.f + __expf(-x[1]));
+            return r;
+        } else return bf2(u);
+    };
+
     // ---- stage 2: decay factors, gamma, scaled operands in LDS ----
     if (t < DK) reinterpret_cast<float *>(blk + L::oG)[t] = __expf(sRef[4 * DK + t]);
     if (fast) {
@@ -228,8 +321,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             f2 e1, e2;
             e1[0] = __expf(gg[u][0] - mid[0]); e1[1] = __expf(gg[u][1] - mid[1]);
             e2[0] = __expf(mid[0] - gg[u][0]); e2[1] = __expf(mid[1] - gg[u][1]);
-            const float rf = rowf(u);
-            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
+            const f2 kv = kval(u), bv = bval(u), qv = qval(u);
             const f2 eh = bv * kv * e1, qh = qv * e1, kb_ = kv * e2;
             sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
             sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
@@ -282,8 +374,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
         for (int u = 0; u < RPG; ++u) {
             const int r = r0 + u;
-            const float rf = rowf(u);
-            const f2 kv = Ld<In>::cvt2(kr[u]) * rf, bv = bf2(u), qv = Ld<In>::cvt2(qr[u]) * rf;
+            const f2 kv = kval(u), bv = bval(u), qv = qval(u);
             const f2 eh = bv * kv * e1[u], qh = qv * e1[u], kb_ = kv * e2[u];
             sE[r * LDE + c0] = (Op)eh[0]; sE[r * LDE + c0 + 1] = (Op)eh[1];
             sQ[r * LDE + c0] = (Op)qh[0]; sQ[r * LDE + c0 + 1] = (Op)qh[1];
@@ -748,12 +839,20 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     __syncthreads();   // drains the line reads before the workgroup ends
 }
 
-template <typename In, typename Op, int DK, int DV, int NC, bool WSC>
+//
+// PRO (fused prologue): v and w arrive raw. The output waves keep the raw v
+// rows of three chunks in LDS (slot c % 3): each step stages the next
+// chunk's rows, and forms this chunk's U = sigmoid(w) * ShortConv(v) from
+// its own row (registers) and the three before it (LDS, reaching into the
+// previous chunk's slot, or the history rows placed in slot 2 before the
+// first chunk).
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
-    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf)
+    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf, ConvIn cv)
 {
+    static_assert(!PRO || !WSC, "the prologue takes per-channel gates");
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
     using frag = typename M::frag;
@@ -772,6 +871,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     __shared__ __attribute__((aligned(16))) Op sU[NC][2 * NSB * 64 * NE];   // U hi / lo B-fragments
     constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
     __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];          // o tiles
+    constexpr int LDV = 16 * NC;                                             // raw-v row stride (floats)
+    __shared__ __attribute__((aligned(16))) float sVr[PRO ? 3 : 1][PRO ? 64 * LDV : 4];   // PRO: raw v rows
 
     // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
     // sit on XCD c % 8
@@ -825,6 +926,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             f1.load_a(blk_of(1), wv, lane);
             f1.load_b(blk_of(1), wv, lane);
         }
+        if constexpr (PRO) __syncthreads();   // pairs with the output waves' staging of chunk 0
         // The prefetch of chunk c+2 is split over the two windows in which
         // the state waves would otherwise wait for the output waves.
         auto step = [&](int c, SF &cur, SF &pre) {
@@ -926,6 +1028,47 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             g1.load(blk_of(1), wo, lane);
             uv_load(u1, 1);
         }
+        // PRO: taps and bias of the thread's columns (per column tile)
+        f4 ctap[PRO ? NC : 1][4], cbias[PRO ? NC : 1];
+        auto stage_v = [&](const UV &u, int slot) {   // raw v row ur of a chunk into LDS
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                f4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = in2f<In>(u.q[q].v[e]);
+                *reinterpret_cast<f4 *>(&sVr[slot][ur * LDV + 16 * q + uc]) = x;
+            }
+        };
+        if constexpr (PRO) {
+            const float bflag = cv.bias ? 1.f : 0.f;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const size_t cofs = (size_t)h * DV + col0 + 16 * q + uc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ctap[q][e] = *reinterpret_cast<const f4 *>(cv.w + 4 * (cofs + e));
+                // without a bias, read the taps (any valid address) and zero them
+                cbias[q] = *reinterpret_cast<const f4 *>(cv.bias ? cv.bias + cofs : cv.w + 4 * cofs) * bflag;
+            }
+            if (nch > 0) {
+                stage_v(u0, 0);
+                // rows 61..63 of slot 2 stand for the three tokens before the
+                // sequence: the history, or zeros
+                if (ur >= 61) {
+                    const In *hv = (const In *)cv.hist;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) {
+                        f4 x = f4zero();
+                        if (hv) {
+                            const In *hp = hv + ((size_t)(i * H + h) * 3 + (ur - 61)) * DV + col0 + 16 * q + uc;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = in2f<In>(hp[e]);
+                        }
+                        *reinterpret_cast<f4 *>(&sVr[2][ur * LDV + 16 * q + uc]) = x;
+                    }
+                }
+            }
+            __syncthreads();   // pairs with the state waves' barrier before their loop
+        }
         // o tiles go through LDS (double-buffered) and leave as 16-byte
         // stores (NC per thread) after the next barrier
         auto store_o = [&](int c) {
@@ -938,21 +1081,54 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
             }
         };
-        auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &upre) {
+        // `sl` = c % 3 (a constant at every call site): the LDS slot of
+        // chunk c's raw v rows under PRO
+        auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &unext, UV &upre, int sl) {
+            f4 y[NC];   // PRO: ShortConv(v) of row ur
+            if constexpr (PRO) {
+                stage_v(unext, sl == 2 ? 0 : sl + 1);
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    f4 x3;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x3[e] = in2f<In>(ucur.q[q].v[e]);
+                    f4 acc = cbias[q];
+#pragma unroll
+                    for (int jt = 0; jt < 3; ++jt) {
+                        const int row = ur - 3 + jt;   // before the chunk: the previous slot
+                        const float *src = row >= 0 ? &sVr[sl][row * LDV] : &sVr[sl == 0 ? 2 : sl - 1][(row + 64) * LDV];
+                        const f4 xr = *reinterpret_cast<const f4 *>(src + 16 * q + uc);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[e] += ctap[q][e][jt] * xr[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] += ctap[q][e][3] * x3[e];
+                    y[q] = acc;
+                }
+            }
 #pragma unroll
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const UVTile<In> &uq = ucur.q[q];
-                    const float uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                    float uu;
+                    if constexpr (PRO) uu = uq.ok ? y[q][e] / (1.f + __expf(-in2f<In>(uq.w[e]))) : 0.f;
+                    else uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
                     const Op hi = (Op)uu;
                     const int ln = (uc + e) + 16 * ug;
                     sU[q][((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
                     sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
                 }
             __syncthreads();   // (1)
-            pre.load(blk_of(c + PD), wo, lane);
-            uv_load(upre, c + PD);
+            if constexpr (PRO) {
+                // v / w first: the next step waits for them (staging) but
+                // not for the operand fragments issued after
+                uv_load(upre, c + PD);
+                pre.load(blk_of(c + PD), wo, lane);
+            } else {
+                pre.load(blk_of(c + PD), wo, lane);
+                uv_load(upre, c + PD);
+            }
             if (c > 0) store_o(c - 1);
             f4 oacc[NC];
 #pragma unroll
@@ -978,12 +1154,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         };
         int c = 0;
         for (; c + 3 <= nch; c += 3) {
-            step(c, g0, g2, u0, u2);
-            step(c + 1, g1, g0, u1, u0);
-            step(c + 2, g2, g1, u2, u1);
+            step(c, g0, g2, u0, u1, u2, 0);
+            step(c + 1, g1, g0, u1, u2, u0, 1);
+            step(c + 2, g2, g1, u2, u0, u1, 2);
         }
-        if (c < nch) step(c, g0, g2, u0, u2);
-        if (c + 1 < nch) step(c + 1, g1, g0, u1, u0);
+        if (c < nch) step(c, g0, g2, u0, u1, u2, 0);
+        if (c + 1 < nch) step(c + 1, g1, g0, u1, u2, u0, 1);
         __syncthreads();   // final
         if (nch > 0) store_o(nch - 1);
     }
@@ -1029,15 +1205,17 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     if (p.max_chunks > 0) {
         prof_before("gdn2_chunk_prep", st);
         const dim3 pg((unsigned)((long long)p.max_chunks * a.H));
+        const ConvIn cq = {a.pro.q.w, a.pro.q.bias, a.pro.q.hist_in}, ck = {a.pro.k.w, a.pro.k.bias, a.pro.k.hist_in};
         auto prep = [&](auto kern) {
             hipLaunchKernelGGL(kern, pg, dim3(256), 0, st, (const In *)a.q, (const In *)a.k, a.log_alpha,
-                               (const In *)a.b, sq, a.H, ops, prog, (int)chains);
+                               (const In *)a.b, sq, a.H, ops, prog, (int)chains, cq, ck);
         };
-        switch (a.gates & (kGateB | kGateAlpha)) {
-        case 0: prep(chunk_prep_kernel<In, Op, DK, 0>); break;
-        case kGateB: prep(chunk_prep_kernel<In, Op, DK, kGateB>); break;
-        case kGateAlpha: prep(chunk_prep_kernel<In, Op, DK, kGateAlpha>); break;
-        default: prep(chunk_prep_kernel<In, Op, DK, kGateB | kGateAlpha>); break;
+        if (a.pro.on) prep(chunk_prep_kernel<In, Op, DK, 0, true>);
+        else switch (a.gates & (kGateB | kGateAlpha)) {
+        case 0: prep(chunk_prep_kernel<In, Op, DK, 0, false>); break;
+        case kGateB: prep(chunk_prep_kernel<In, Op, DK, kGateB, false>); break;
+        case kGateAlpha: prep(chunk_prep_kernel<In, Op, DK, kGateAlpha, false>); break;
+        default: prep(chunk_prep_kernel<In, Op, DK, kGateB | kGateAlpha, false>); break;
         }
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1061,19 +1239,22 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     const long long pass_grid = 8LL * (nsl + npf) * groups;
     if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
     prof_before("gdn2_chunk_pass", st);
+    const ConvIn cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in};
     auto pass = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)pass_grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
-                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf);
+                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf, cv);
     };
     const bool wsc = a.gates & kGateW;
     if (two) {
         if constexpr ((DV / 16) % 2 == 0) {
-            if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 2, true>);
-            else pass(chunk_pass_kernel<In, Op, DK, DV, 2, false>);
+            if (a.pro.on) pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, true>);
+            else if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 2, true, false>);
+            else pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, false>);
         }
     } else {
-        if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 1, true>);
-        else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false>);
+        if (a.pro.on) pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, true>);
+        else if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 1, true, false>);
+        else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, false>);
     }
     prof_after(st);
     return hipGetLastError();

@@ -10,6 +10,14 @@
 //
 // One workgroup per (sequence, head). Thread t owns 4 consecutive columns and
 // DK/ROWG rows of S, kept in registers between the reductions and the update.
+//
+// PRO (fused prologue): q, k, v arrive raw with their convolution history
+// (three earlier raw inputs per channel) and b, w as logits. q, k and v are
+// the short convolutions, b and w the sigmoids. The unit-norm scales of q and
+// k are applied to the reduced quantities (e, r, k.q) and to the rank-one
+// update rather than to every element: the sums of squares are reduced
+// alongside k.q, before they are needed. The history moves up by one token
+// (each thread rewrites the channels it read, so it may be updated in place).
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
@@ -22,11 +30,43 @@ template <int DK, int DV> struct DecodeShape {
     static constexpr int NT = COLG * ROWG;                               // threads
 };
 
-template <typename In, int DK, int DV>
+struct DecConv {
+    const float *w, *bias;   // taps [H*d][4] (tap 3 on the current token), bias [H*d] or null
+    const void *hin;         // history [N*H][3][d] or null (zeros)
+    void *hout;              // shifted history, or null; may equal hin
+};
+
+template <typename In, int D>
+__device__ __forceinline__ float conv_token(const In *x, const DecConv &c, int nh, int h, int ch, In raw[4])
+{
+    // raw[0..2]: the history (oldest first), raw[3]: this token
+    const In *hin = (const In *)c.hin;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) raw[j] = hin ? hin[((size_t)nh * 3 + j) * D + ch] : (In)0;
+    raw[3] = x[(size_t)nh * D + ch];
+    const f4 tap = *reinterpret_cast<const f4 *>(c.w + 4 * ((size_t)h * D + ch));
+    float y = c.bias ? c.bias[(size_t)h * D + ch] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y += tap[j] * in2f<In>(raw[j]);
+    return y;
+}
+
+template <typename In, int D>
+__device__ __forceinline__ void shift_history(const DecConv &c, int nh, int ch, const In raw[4])
+{
+    if (!c.hout) return;
+    In *ho = (In *)c.hout;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) ho[((size_t)nh * 3 + j) * D + ch] = raw[j + 1];
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+
+template <typename In, int DK, int DV, bool PRO>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
     const float *__restrict__ la, const In *__restrict__ b, const In *__restrict__ w,
-    float *__restrict__ S, float *__restrict__ o, int gates)
+    float *__restrict__ S, float *__restrict__ o, int gates, int H, DecConv cq, DecConv ck, DecConv cv)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int COLG = Sh::COLG, ROWG = Sh::ROWG, RPT = Sh::RPT, NT = Sh::NT;
@@ -36,7 +76,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 
     __shared__ float s_a[DK], s_bk[DK], s_q[DK], s_k[DK], s_u[DV];
     __shared__ f4 s_e[ROWG][COLG], s_r[ROWG][COLG];
-    __shared__ float s_kq[NT / 64 > 0 ? NT / 64 : 1];
+    constexpr int NW = NT / 64 > 0 ? NT / 64 : 1;
+    __shared__ float s_kq[NW], s_qq[NW], s_kk[NW];
 
     float *Sp = S + (size_t)nh * DK * DV;
     f4 sv[RPT];
@@ -46,24 +87,58 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 
     // gates: one value per channel, or per (sequence, head) where the bit is set
     const bool asc = gates & kGateAlpha, bsc = gates & kGateB, wsc = gates & kGateW;
-    float kq = 0.f;
+    float kq = 0.f, qq = 0.f, kk = 0.f;
     for (int c = t; c < DK; c += NT) {
         const size_t i = (size_t)nh * DK + c;
-        const float kc = Ld<In>::one(k + i), qc = Ld<In>::one(q + i);
+        float kc, qc, bc;
+        if constexpr (PRO) {
+            const int h = nh % H;
+            In rq[4], rk[4];
+            qc = conv_token<In, DK>(q, cq, nh, h, c, rq);
+            kc = conv_token<In, DK>(k, ck, nh, h, c, rk);
+            shift_history<In, DK>(cq, nh, c, rq);
+            shift_history<In, DK>(ck, nh, c, rk);
+            bc = sigmoidf_(Ld<In>::one(b + i));
+            qq += qc * qc;
+            kk += kc * kc;
+        } else {
+            kc = Ld<In>::one(k + i);
+            qc = Ld<In>::one(q + i);
+            bc = Ld<In>::one(b + (bsc ? (size_t)nh : i));
+        }
         s_a[c] = __expf(la[asc ? (size_t)nh : i]);
         s_k[c] = kc;
         s_q[c] = qc;
-        s_bk[c] = Ld<In>::one(b + (bsc ? (size_t)nh : i)) * kc;
+        s_bk[c] = bc * kc;
         kq += kc * qc;
     }
     for (int j = t; j < DV; j += NT) {
         const size_t i = (size_t)nh * DV + j;
-        s_u[j] = Ld<In>::one(w + (wsc ? (size_t)nh : i)) * Ld<In>::one(v + i);
+        if constexpr (PRO) {
+            In rv[4];
+            const float vc = conv_token<In, DV>(v, cv, nh, nh % H, j, rv);
+            shift_history<In, DV>(cv, nh, j, rv);
+            s_u[j] = sigmoidf_(Ld<In>::one(w + i)) * vc;
+        } else {
+            s_u[j] = Ld<In>::one(w + (wsc ? (size_t)nh : i)) * Ld<In>::one(v + i);
+        }
     }
-    // k.q: wave reduction, then across waves
+    // k.q (and under PRO the squared norms): wave reduction, then across waves
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
-    if ((t & 63) == 0) s_kq[t >> 6] = kq;
+    for (int off = 32; off > 0; off >>= 1) {
+        kq += __shfl_xor(kq, off);
+        if constexpr (PRO) {
+            qq += __shfl_xor(qq, off);
+            kk += __shfl_xor(kk, off);
+        }
+    }
+    if ((t & 63) == 0) {
+        s_kq[t >> 6] = kq;
+        if constexpr (PRO) {
+            s_qq[t >> 6] = qq;
+            s_kk[t >> 6] = kk;
+        }
+    }
     __syncthreads();
 
     f4 e = f4zero(), rr = f4zero();
@@ -83,7 +158,18 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     for (int g = 0; g < ROWG; ++g) { E += s_e[g][cg]; R += s_r[g][cg]; }
     float KQ = 0.f;
 #pragma unroll
-    for (int i = 0; i < (NT / 64 > 0 ? NT / 64 : 1); ++i) KQ += s_kq[i];
+    for (int i = 0; i < NW; ++i) KQ += s_kq[i];
+    float kscale = 1.f;   // PRO: 1 / max(|k|, 1e-12), and likewise for q
+    if constexpr (PRO) {
+        float QQ = 0.f, KK = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) { QQ += s_qq[i]; KK += s_kk[i]; }
+        const float qscale = rsqrtf(fmaxf(QQ, 1e-24f));
+        kscale = rsqrtf(fmaxf(KK, 1e-24f));
+        E *= kscale;
+        R *= qscale;
+        KQ *= qscale * kscale;
+    }
     f4 u = *reinterpret_cast<const f4 *>(&s_u[4 * cg]);
     const f4 delta = u - E;
     if (rg == 0)
@@ -94,7 +180,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int c = rg + r * ROWG;
-        __builtin_nontemporal_store(sv[r] + delta * s_k[c],
+        __builtin_nontemporal_store(sv[r] + delta * (s_k[c] * kscale),
                                     reinterpret_cast<f4 *>(Sp + (size_t)(rg + r * ROWG) * DV + 4 * cg));
     }
 }
@@ -103,10 +189,17 @@ template <typename In, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st)
 {
     constexpr int NT = DecodeShape<DK, DV>::NT;
+    const DecConv cq = {a.pro.q.w, a.pro.q.bias, a.pro.q.hist_in, a.pro.q.hist_out};
+    const DecConv ck = {a.pro.k.w, a.pro.k.bias, a.pro.k.hist_in, a.pro.k.hist_out};
+    const DecConv cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in, a.pro.v.hist_out};
     prof_before("gdn2_decode", st);
-    hipLaunchKernelGGL((decode_kernel<In, DK, DV>), dim3(a.N * a.H), dim3(NT), 0, st,
-                       (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
-                       (const In *)a.b, (const In *)a.w, a.S, (float *)a.o, a.gates);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(a.N * a.H), dim3(NT), 0, st, (const In *)a.q, (const In *)a.k,
+                           (const In *)a.v, a.log_alpha, (const In *)a.b, (const In *)a.w, a.S, (float *)a.o,
+                           a.gates, a.H, cq, ck, cv);
+    };
+    if (a.pro.on) go(decode_kernel<In, DK, DV, true>);
+    else go(decode_kernel<In, DK, DV, false>);
     prof_after(st);
     return hipGetLastError();
 }

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdn2 {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -100,6 +102,25 @@ template <> struct Mma<float> {
     }
     static __device__ __forceinline__ f4 mma16(const f4 &a, const f4 &b, f4 c) { return mma(a, b, c); }
 };
+
+// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64), the result in
+// every lane of the group: DPP swaps within rows of 16 lanes (xor 1, xor 2,
+// then the half-row and row mirrors, which pair the halves once the smaller
+// groups already hold their sums), cross-lane permutes above that.
+template <int G> __device__ __forceinline__ float lane_group_sum(float x)
+{
+    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group of 8 to 64 lanes");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    if constexpr (G >= 16) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+    if constexpr (G >= 32) x += __shfl_xor(x, 16);
+    if constexpr (G >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
 
 __device__ __forceinline__ f4 f4zero() { f4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 

@@ -10,6 +10,23 @@ namespace gdn2 {
 // Gate layouts (bit set = one value per token and head instead of one per channel)
 enum : int { kGateB = 1, kGateW = 2, kGateAlpha = 4 };
 
+// Short convolution of one raw tensor (fused prologue): taps [H*d][4] with
+// tap 3 on the current token, optional bias [H*d], optional history in and
+// out [N][H][3][d] (input dtype, oldest first). Device pointers.
+struct ConvTensor {
+    const float *w = nullptr;
+    const float *bias = nullptr;
+    const void *hist_in = nullptr;
+    void *hist_out = nullptr;
+};
+
+// The fused prologue: q, k, v through their short convolutions, q and k to
+// unit norm, b and w through the sigmoid. Off: the inputs are used as given.
+struct Prologue {
+    bool on = false;
+    ConvTensor q, k, v;
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *b, *w;
     const float *log_alpha;
@@ -18,6 +35,7 @@ struct DecodeArgs {
     int N, H, dk, dv;
     int gates;
     bool bf16;
+    Prologue pro;
 };
 
 struct ChunkArgs {
@@ -32,6 +50,7 @@ struct ChunkArgs {
     bool bf16;
     void *workspace;
     size_t workspace_bytes;
+    Prologue pro;
 };
 
 // Workspace layout for one call (all offsets 256-byte aligned):

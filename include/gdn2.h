@@ -159,6 +159,73 @@ int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const fl
                            int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
 
 /*
+ * Fused input prologue. The layer computes the mixer's inputs from its
+ * projections as q = L2Norm(ShortConv(q_raw)), k = L2Norm(ShortConv(k_raw)),
+ * v = ShortConv(v_raw), b = sigmoid(b_logit), w = sigmoid(w_logit)
+ * (aifetchly-blog.pages.dev, "Gated DeltaNet-2 Guide", the "Architectural
+ * Workflow" diagram, steps 1 and 2, and section "2. Normalization and Short
+ * Convolutions"). The *_prologue entry points take the raw tensors and do
+ * these steps inside the mixer's own kernels, so q, k, v, b and w never
+ * travel through memory.
+ *
+ * ShortConv is a causal depthwise convolution of kernel 4 along the tokens
+ * of each sequence: for channel c of head h (row h*d + c of the weights),
+ *     y_t = bias[c] + sum_{j=0..3} weight[c][j] * x_{t-3+j}
+ * so weight[c][3] multiplies the current token; no activation follows (the
+ * construction in that guide's "End-to-End PyTorch Implementation"). L2Norm
+ * divides by max(||y||_2, 1e-12) over the head's channels.
+ *
+ * All pointers in the struct are device pointers; the struct itself is
+ * read on the host during the call.
+ *   weight_q, weight_k  [H*dk, 4] float   required
+ *   weight_v            [H*dv, 4] float   required
+ *   bias_q, bias_k      [H*dk] float, or NULL for no bias
+ *   bias_v              [H*dv] float, or NULL
+ *   state_in_q/k/v      [N, H, 3, d] in_dtype: the three raw inputs before
+ *                       each sequence's first token, oldest first; all three
+ *                       NULL means zeros (sequences that start here)
+ *   state_out_q/k/v     [N, H, 3, d] in_dtype: receives the last three raw
+ *                       inputs of each sequence (reaching back into
+ *                       state_in when a sequence is shorter than three
+ *                       tokens), or all three NULL; may alias state_in
+ * Only all-or-none of the three state_in (and of the three state_out)
+ * pointers may be NULL, else GDN2_ERR_INVALID.
+ */
+typedef struct gdn2_short_conv {
+    const float *weight_q, *weight_k, *weight_v;
+    const float *bias_q, *bias_k, *bias_v;
+    const void *state_in_q, *state_in_k, *state_in_v;
+    void *state_out_q, *state_out_k, *state_out_v;
+} gdn2_short_conv;
+
+/*
+ * gdn2_chunk_fwd on the raw tensors, with the prologue above fused in.
+ *   q_raw, k_raw, b_logit  [tokens, H, dk]  in_dtype
+ *   v_raw, w_logit         [tokens, H, dv]  in_dtype
+ *   conv                   host pointer to the convolution parameters
+ * log_alpha, S0, o, ST, cu_seqlens, sizes, dtypes, workspace (the size from
+ * gdn2_chunk_fwd_workspace_bytes) and errors are those of gdn2_chunk_fwd.
+ * Gates are per channel. The state_out tensors are written after every
+ * read of state_in, so the two may alias.
+ */
+int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
+                            const void *b_logit, const void *w_logit, const gdn2_short_conv *conv,
+                            const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B, int T,
+                            int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                            void *workspace, size_t workspace_bytes);
+
+/*
+ * gdn2_decode_step on the raw inputs of one token per sequence
+ * (q_raw, k_raw, b_logit [N, H, dk]; v_raw, w_logit [N, H, dv]), with the
+ * prologue fused in. conv->state_in_* is the convolution history (NULL:
+ * zeros, the sequence's first token); conv->state_out_* receives the history
+ * shifted by this token and may alias state_in_* (the usual in-place cache).
+ */
+int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
+                              const void *b_logit, const void *w_logit, const gdn2_short_conv *conv, float *S,
+                              void *o, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+
+/*
  * Per-kernel timing, for measurement tools (not needed for computing).
  * gdn2_profile_begin(max_calls) makes this thread's next gdn2_chunk_fwd /
  * gdn2_decode_step calls (up to max_calls of them, 1..4096) record a HIP

@@ -167,3 +167,51 @@ def test_python_binding_validates_before_calling():
         gdn2.chunk_fwd(x, x[:, :32], x, la, x, x)
     with pytest.raises(TypeError):
         gdn2.chunk_fwd(x.half(), x.half(), x.half(), la, x.half(), x.half())
+
+
+def _conv(**kw):
+    P = 0x10000
+    c = gdn2.ShortConv(weight_q=P, weight_k=P, weight_v=P)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize('kw,status', [
+    (None, gdn2.GDN2_ERR_INVALID),                                   # no struct
+    (dict(weight_k=None), gdn2.GDN2_ERR_INVALID),                    # taps required
+    (dict(weight_v=0x10004), gdn2.GDN2_ERR_INVALID),                 # misaligned
+    (dict(bias_q=0x10008), gdn2.GDN2_ERR_INVALID),
+    (dict(state_in_q=0x20000), gdn2.GDN2_ERR_INVALID),               # history in: all or none
+    (dict(state_out_q=0x20000, state_out_k=0x20000), gdn2.GDN2_ERR_INVALID),
+    (dict(), gdn2.GDN2_ERR_WORKSPACE),                               # valid: the small workspace decides
+    (dict(bias_q=0x30000, bias_v=0x30000), gdn2.GDN2_ERR_WORKSPACE),
+    (dict(state_in_q=0x20000, state_in_k=0x20000, state_in_v=0x20000,
+          state_out_q=0x20000, state_out_k=0x20000, state_out_v=0x20000), gdn2.GDN2_ERR_WORKSPACE),
+])
+def test_prologue_conv_validation(kw, status):
+    """The convolution struct is checked on the host before anything launches."""
+    P = 0x10000
+    vp = ctypes.c_void_p
+    conv = None if kw is None else ctypes.byref(_conv(**kw))
+    st = gdn2.lib().gdn2_chunk_fwd_prologue(vp(P), vp(P), vp(P), vp(P), vp(P), vp(P), conv, None, vp(P), vp(P),
+                                            None, 1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, gdn2.GDN2_F32, vp(P), 1024)
+    assert st == status
+    if status == gdn2.GDN2_ERR_INVALID:
+        st = gdn2.lib().gdn2_decode_step_prologue(vp(P), vp(P), vp(P), vp(P), vp(P), vp(P), conv, vp(P), vp(P),
+                                                  4, 2, 128, 128, gdn2.GDN2_BF16, gdn2.GDN2_F32)
+        assert st == status
+
+
+def test_prologue_binding_validates_before_calling():
+    import torch
+    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    la = torch.zeros(1, 64, 1, 128)
+    wt = tuple(torch.zeros(128, 4) for _ in range(3))
+    with pytest.raises(ValueError):            # taps of the wrong shape
+        gdn2.chunk_fwd_prologue(x, x, x, la, x, x, (wt[0], wt[1], torch.zeros(128, 3)))
+    with pytest.raises(ValueError):            # not a triple
+        gdn2.chunk_fwd_prologue(x, x, x, la, x, x, wt[:2])
+    with pytest.raises(TypeError):             # history in the wrong dtype
+        gdn2.chunk_fwd_prologue(x, x, x, la, x, x, wt,
+                                conv_state=tuple(torch.zeros(1, 1, 3, 128) for _ in range(3)))
