@@ -6,7 +6,10 @@ d_k=d_v=128, bf16 q/k/v/b/w, fp32 log alpha, fp32 state and output, S0 ~
 N(0, 0.02)). One step = one gdn2_chunk_fwd call over the whole batch (chunk
 prep + sequential state pass). The decode workload (256 sequences x 16 heads,
 fp32 state resident, 1000 single-token steps with fresh inputs) is measured in
-the same run and reported under "decode".
+the same run and reported under "decode". Also reported: the same prefill with
+scalar gates ("gate_forms": the KDA and Gated DeltaNet layouts) and on the
+layer's raw inputs with the short convolution, unit norm and sigmoids fused
+in ("prologue_form", for prefill and decode).
 
 Prints ONE JSON line. Inputs are synthetic and seeded (gdn2_inputs), resident
 in HBM before timing starts. Per-kernel durations come from HIP events that
@@ -151,6 +154,8 @@ def bench_prefill(args, torch, gdn2, gi):
                         'kernels_ms': {kk: round(vv[1] / vv[0], 5) for kk, vv in fprof.items() if vv[0]}}
         log(f'[bench] prefill, {fname} gates: {fms:.3f} ms/step')
     res['gate_forms'] = forms
+    if not args.no_prologue:
+        res['prologue_form'] = bench_prefill_prologue(args, torch, gdn2, gi, ws)
 
     if not args.no_cpu_baseline:
         import oracle
@@ -173,6 +178,52 @@ def bench_prefill(args, torch, gdn2, gi):
     del q, k, v, b, w, la, o, ws, b1, la1, o1, ST1
     torch.cuda.empty_cache()
     return res
+
+
+def bench_prefill_prologue(args, torch, gdn2, gi, ws):
+    """The same workload in the layer's raw form: q, k, v before the short
+    convolution and b, w as logits (gdn2_chunk_fwd_prologue: the convolution,
+    unit norm and sigmoid run inside the mixer's kernels), with a
+    convolution history in and out per sequence."""
+    c = gi.WORKLOADS['prefill_t65536']
+    B, T, H, dk, dv = c['B'], c['T'], c['H'], c['dk'], c['dv']
+    t0 = time.time()
+    p = gi.prologue_prefill(c['seed'], [T] * B, H, dk, dv, c['dtype'], c['s0_std'], conv_history=True,
+                            threads=nthreads())
+    dev = torch.device('cuda:0')
+    bf = torch.bfloat16
+    t = lambda x, d: torch.from_numpy(x).to(dev).to(d).reshape(B, T, H, x.shape[-1])
+    qr, kr, vr, xb, xw = (t(x, bf) for x in (p.q_raw, p.k_raw, p.v_raw, p.b_logit, p.w_logit))
+    la = t(p.log_alpha, torch.float32)
+    trip = lambda d, dt: tuple(torch.from_numpy(d[n]).to(dev).to(dt) for n in ('q', 'k', 'v'))
+    cw, cb, hin = trip(p.conv_w, torch.float32), trip(p.conv_b, torch.float32), trip(p.conv_in, bf)
+    hout = tuple(torch.empty_like(x) for x in hin)
+    S0 = torch.from_numpy(p.S0).to(dev)
+    o = torch.empty(B, T, H, dv, device=dev)
+    ST = torch.empty_like(S0)
+    log(f'[bench] generated the raw-form workload in {time.time() - t0:.1f}s')
+    run = lambda: gdn2.chunk_fwd_prologue(qr, kr, vr, la, xb, xw, cw, cb, S0, conv_state=hin, conv_state_out=hout,
+                                          out=o, final_state=ST, workspace=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    gdn2.profile_begin(args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    prof = gdn2.profile_end()
+    TH = B * T * H
+    conv_bytes = H * (2 * dk + dv) * 5 * 4 + 2 * B * H * 3 * (2 * dk + dv) * 2   # taps, biases, history in + out
+    nbytes = TH * (3 * dk * 2 + dk * 4) + TH * (2 * dv * 2 + dv * 4) + 2 * B * H * dk * dv * 4 + conv_bytes
+    log(f'[bench] prefill, fused prologue: {ms:.3f} ms/step')
+    del qr, kr, vr, xb, xw, la, o
+    return {'ms_per_step': round(ms, 4), 'value': B * T / (ms * 1e-3), 'unit': 'tokens/s',
+            'inputs': 'raw bf16 q,k,v and b,w logits; ShortConv k=4 with bias and history, L2 norm, sigmoid fused',
+            'alg_bytes_per_step': int(nbytes),
+            'step_roofline_frac': round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            'kernels_ms': {k: round(v[1] / v[0], 5) for k, v in prof.items() if v[0]}}
 
 
 def bench_decode(args, torch, gdn2, gi):
@@ -214,6 +265,36 @@ def bench_decode(args, torch, gdn2, gi):
                       'state': 'fp32 [N,H,dk,dv] resident, updated in place', 'inputs': 'bf16, fresh per step'},
            'roofline': roofline('gdn2_decode', per_chain * N * H, avg, name)}
     log(f'[bench] decode {res["ms_per_step"]} ms/step, kernel {avg * 1e3:.1f} us')
+    if not args.no_prologue:
+        # raw inputs (q, k, v before the short convolution, gate logits) with
+        # the convolution history updated in place
+        np_ = min(steps, 200)
+        raw = [gi.prologue_decode_step(c['seed'], s, N, H, d, d) for s in range(1, np_ + 1)]
+        rs = lambda j, dt: torch.from_numpy(np.stack([r[j] for r in raw])).to(dev).to(dt)
+        qr, kr, vr, xb, xw = (rs(j, bf) for j in (0, 1, 2, 4, 5))
+        lr = rs(3, torch.float32)
+        _, h_np = gi.prologue_decode_state(c['seed'], N, H, d, d)
+        hist = tuple(torch.from_numpy(h_np[n]).to(dev).to(bf) for n in ('q', 'k', 'v'))
+        cw_np, cb_np = gi.conv_params(c['seed'], H, d, d)
+        cw = tuple(torch.from_numpy(cw_np[n]).to(dev) for n in ('q', 'k', 'v'))
+        cb = tuple(torch.from_numpy(cb_np[n]).to(dev) for n in ('q', 'k', 'v'))
+        pstep = lambda s: gdn2.decode_step_prologue(qr[s], kr[s], vr[s], lr[s], xb[s], xw[s], S, cw, cb, hist, out=o)
+        for s in range(min(10, np_)):
+            pstep(s)
+        torch.cuda.synchronize()
+        gdn2.profile_begin(np_)
+        t0 = time.perf_counter()
+        for s in range(np_):
+            pstep(s)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n, tot = gdn2.profile_end()['gdn2_decode']
+        pavg = tot / n
+        per_pro = per_chain + 2 * 3 * 3 * d * 2   # + history of q, k, v read and written
+        res['prologue_form'] = {'steps': np_, 'ms_per_step': round((t1 - t0) * 1e3 / np_, 5),
+                                'value': np_ / (t1 - t0), 'unit': 'steps/s',
+                                'roofline': roofline('gdn2_decode', per_pro * N * H, pavg, name + '_prologue')}
+        log(f'[bench] decode, fused prologue: kernel {pavg * 1e3:.1f} us')
     if not args.no_cpu_baseline:
         import oracle
         ns = args.cpu_decode_steps
@@ -239,6 +320,8 @@ def main():
     ap.add_argument('--cpu-decode-steps', type=int, default=100)
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--no-decode', action='store_true')
+    ap.add_argument('--no-prologue', action='store_true',
+                    help='skip the fused-prologue (raw-input) timings')
     ap.add_argument('--no-gate-forms', action='store_true',
                     help='skip the scalar-gate (KDA, Gated DeltaNet) prefill timings')
     ap.add_argument('--copy-calibration-mib', type=int, default=0,
@@ -281,6 +364,8 @@ def main():
     out['step_roofline'] = pre['step_roofline']
     out['kernels_ms'] = pre['kernels_ms']
     out['gate_forms'] = pre['gate_forms']
+    if 'prologue_form' in pre:
+        out['prologue_form'] = pre['prologue_form']
     if 'parity_sample' in pre:
         out['parity_sample'] = pre['parity_sample']
     if not args.no_decode:

@@ -1039,6 +1039,30 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 *reinterpret_cast<f4 *>(&sVr[slot][ur * LDV + 16 * q + uc]) = x;
             }
         };
+        // PRO: U = sigmoid(w) * ShortConv(v) of row ur of one chunk, from its
+        // raw rows in LDS slot `slot` (and rows 61..63 of slot `pslot` for the
+        // rows before it), its own row and w in registers; zero past the end
+        f4 ucarry[PRO ? NC : 1];
+        auto conv_u = [&](const UV &u, int slot, int pslot) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                f4 acc = cbias[q];
+#pragma unroll
+                for (int jt = 0; jt < 3; ++jt) {
+                    const int row = ur - 3 + jt;
+                    const float *src = row >= 0 ? &sVr[slot][row * LDV] : &sVr[pslot][(row + 64) * LDV];
+                    const f4 xr = *reinterpret_cast<const f4 *>(src + 16 * q + uc);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] += ctap[q][e][jt] * xr[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = acc[e] + ctap[q][e][3] * in2f<In>(u.q[q].v[e]);
+                    const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-in2f<In>(u.q[q].w[e])));
+                    ucarry[q][e] = u.q[q].ok ? y * sg : 0.f;
+                }
+            }
+        };
         if constexpr (PRO) {
             const float bflag = cv.bias ? 1.f : 0.f;
 #pragma unroll
@@ -1068,6 +1092,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 }
             }
             __syncthreads();   // pairs with the state waves' barrier before their loop
+            if (nch > 0) conv_u(u0, 0, 2);
         }
         // o tiles go through LDS (double-buffered) and leave as 16-byte
         // stores (NC per thread) after the next barrier
@@ -1081,38 +1106,20 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
             }
         };
-        // `sl` = c % 3 (a constant at every call site): the LDS slot of
-        // chunk c's raw v rows under PRO
+        // `sl` = c % 3 (a constant at every call site). Under PRO, U of chunk
+        // c was formed during the previous step (ucarry); this step stages
+        // the raw v rows of chunk c + 1 in slot (c + 1) % 3 before the first
+        // barrier and forms its U after it, where these waves would wait.
         auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &unext, UV &upre, int sl) {
-            f4 y[NC];   // PRO: ShortConv(v) of row ur
-            if constexpr (PRO) {
-                stage_v(unext, sl == 2 ? 0 : sl + 1);
-#pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    f4 x3;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x3[e] = in2f<In>(ucur.q[q].v[e]);
-                    f4 acc = cbias[q];
-#pragma unroll
-                    for (int jt = 0; jt < 3; ++jt) {
-                        const int row = ur - 3 + jt;   // before the chunk: the previous slot
-                        const float *src = row >= 0 ? &sVr[sl][row * LDV] : &sVr[sl == 0 ? 2 : sl - 1][(row + 64) * LDV];
-                        const f4 xr = *reinterpret_cast<const f4 *>(src + 16 * q + uc);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[e] += ctap[q][e][jt] * xr[e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] += ctap[q][e][3] * x3[e];
-                    y[q] = acc;
-                }
-            }
+            const int sln = sl == 2 ? 0 : sl + 1;
+            if constexpr (PRO) stage_v(unext, sln);
 #pragma unroll
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const UVTile<In> &uq = ucur.q[q];
                     float uu;
-                    if constexpr (PRO) uu = uq.ok ? y[q][e] / (1.f + __expf(-in2f<In>(uq.w[e]))) : 0.f;
+                    if constexpr (PRO) uu = ucarry[q][e];
                     else uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
                     const Op hi = (Op)uu;
                     const int ln = (uc + e) + 16 * ug;
@@ -1120,16 +1127,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
                 }
             __syncthreads();   // (1)
-            if constexpr (PRO) {
-                // v / w first: the next step waits for them (staging) but
-                // not for the operand fragments issued after
-                uv_load(upre, c + PD);
-                pre.load(blk_of(c + PD), wo, lane);
-            } else {
-                pre.load(blk_of(c + PD), wo, lane);
-                uv_load(upre, c + PD);
-            }
+            pre.load(blk_of(c + PD), wo, lane);
+            uv_load(upre, c + PD);
             if (c > 0) store_o(c - 1);
+            if constexpr (PRO) conv_u(unext, sln, sl);
             f4 oacc[NC];
 #pragma unroll
             for (int q = 0; q < NC; ++q) oacc[q] = f4zero();

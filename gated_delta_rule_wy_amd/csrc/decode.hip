@@ -77,7 +77,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     __shared__ float s_a[DK], s_bk[DK], s_q[DK], s_k[DK], s_u[DV];
     __shared__ f4 s_e[ROWG][COLG], s_r[ROWG][COLG];
     constexpr int NW = NT / 64 > 0 ? NT / 64 : 1;
-    __shared__ float s_kq[NW], s_qq[NW], s_kk[NW];
+    __shared__ float s_kq[NW], s_qq[NW], s_kk[NW], s_kqp[PRO ? ROWG : 1];
 
     float *Sp = S + (size_t)nh * DK * DV;
     f4 sv[RPT];
@@ -88,77 +88,103 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     // gates: one value per channel, or per (sequence, head) where the bit is set
     const bool asc = gates & kGateAlpha, bsc = gates & kGateB, wsc = gates & kGateW;
     float kq = 0.f, qq = 0.f, kk = 0.f;
-    for (int c = t; c < DK; c += NT) {
-        const size_t i = (size_t)nh * DK + c;
-        float kc, qc, bc;
-        if constexpr (PRO) {
-            const int h = nh % H;
-            In rq[4], rk[4];
-            qc = conv_token<In, DK>(q, cq, nh, h, c, rq);
-            kc = conv_token<In, DK>(k, ck, nh, h, c, rk);
-            shift_history<In, DK>(cq, nh, c, rq);
-            shift_history<In, DK>(ck, nh, c, rk);
-            bc = sigmoidf_(Ld<In>::one(b + i));
-            qq += qc * qc;
-            kk += kc * kc;
-        } else {
-            kc = Ld<In>::one(k + i);
-            qc = Ld<In>::one(q + i);
-            bc = Ld<In>::one(b + (bsc ? (size_t)nh : i));
+    if constexpr (PRO) {
+        // one job per thread: a q channel, a k channel, a v channel (with its
+        // write gate), or an erase gate and decay; k.q waits for the first
+        // barrier (its factors come from different threads)
+        const int h = nh % H;
+        for (int x = t; x < 3 * DK + DV; x += NT) {
+            In raw[4];
+            if (x < DK) {
+                const float y = conv_token<In, DK>(q, cq, nh, h, x, raw);
+                shift_history<In, DK>(cq, nh, x, raw);
+                s_q[x] = y;
+                qq += y * y;
+            } else if (x < 2 * DK) {
+                const int c = x - DK;
+                const float y = conv_token<In, DK>(k, ck, nh, h, c, raw);
+                shift_history<In, DK>(ck, nh, c, raw);
+                s_k[c] = y;
+                kk += y * y;
+            } else if (x < 2 * DK + DV) {
+                const int j = x - 2 * DK;
+                const float y = conv_token<In, DV>(v, cv, nh, h, j, raw);
+                shift_history<In, DV>(cv, nh, j, raw);
+                s_u[j] = sigmoidf_(Ld<In>::one(w + (size_t)nh * DV + j)) * y;
+            } else {
+                const int c = x - 2 * DK - DV;
+                const size_t i = (size_t)nh * DK + c;
+                s_bk[c] = sigmoidf_(Ld<In>::one(b + i));   // the erase gate alone here
+                s_a[c] = __expf(la[i]);
+            }
         }
-        s_a[c] = __expf(la[asc ? (size_t)nh : i]);
-        s_k[c] = kc;
-        s_q[c] = qc;
-        s_bk[c] = bc * kc;
-        kq += kc * qc;
-    }
-    for (int j = t; j < DV; j += NT) {
-        const size_t i = (size_t)nh * DV + j;
-        if constexpr (PRO) {
-            In rv[4];
-            const float vc = conv_token<In, DV>(v, cv, nh, nh % H, j, rv);
-            shift_history<In, DV>(cv, nh, j, rv);
-            s_u[j] = sigmoidf_(Ld<In>::one(w + i)) * vc;
-        } else {
+    } else {
+        for (int c = t; c < DK; c += NT) {
+            const size_t i = (size_t)nh * DK + c;
+            const float kc = Ld<In>::one(k + i), qc = Ld<In>::one(q + i);
+            s_a[c] = __expf(la[asc ? (size_t)nh : i]);
+            s_k[c] = kc;
+            s_q[c] = qc;
+            s_bk[c] = Ld<In>::one(b + (bsc ? (size_t)nh : i)) * kc;
+            kq += kc * qc;
+        }
+        for (int j = t; j < DV; j += NT) {
+            const size_t i = (size_t)nh * DV + j;
             s_u[j] = Ld<In>::one(w + (wsc ? (size_t)nh : i)) * Ld<In>::one(v + i);
         }
     }
-    // k.q (and under PRO the squared norms): wave reduction, then across waves
+    // k.q (PRO: the squared norms of q and k): wave reduction, then across waves
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        kq += __shfl_xor(kq, off);
         if constexpr (PRO) {
             qq += __shfl_xor(qq, off);
             kk += __shfl_xor(kk, off);
+        } else {
+            kq += __shfl_xor(kq, off);
         }
     }
     if ((t & 63) == 0) {
-        s_kq[t >> 6] = kq;
         if constexpr (PRO) {
             s_qq[t >> 6] = qq;
             s_kk[t >> 6] = kk;
+        } else {
+            s_kq[t >> 6] = kq;
         }
     }
     __syncthreads();
 
     f4 e = f4zero(), rr = f4zero();
+    float kqp = 0.f;   // PRO: this thread's rows of k.q (one column group adds them)
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
         const int c = rg + r * ROWG;
         sv[r] = sv[r] * s_a[c];
-        e += sv[r] * s_bk[c];
+        if constexpr (PRO) {
+            const float kc = s_k[c], qc = s_q[c];
+            e += sv[r] * (s_bk[c] * kc);
+            kqp += kc * qc;
+        } else {
+            e += sv[r] * s_bk[c];
+        }
         rr += sv[r] * s_q[c];
     }
     s_e[rg][cg] = e;
     s_r[rg][cg] = rr;
+    if constexpr (PRO)
+        if (cg == 0) s_kqp[rg] = kqp;
     __syncthreads();
 
     f4 E = f4zero(), R = f4zero();
 #pragma unroll
     for (int g = 0; g < ROWG; ++g) { E += s_e[g][cg]; R += s_r[g][cg]; }
     float KQ = 0.f;
+    if constexpr (PRO) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) KQ += s_kq[i];
+        for (int g = 0; g < ROWG; ++g) KQ += s_kqp[g];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) KQ += s_kq[i];
+    }
     float kscale = 1.f;   // PRO: 1 / max(|k|, 1e-12), and likewise for q
     if constexpr (PRO) {
         float QQ = 0.f, KK = 0.f;
