@@ -300,8 +300,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         if constexpr (PRO) {
             const f2 x = bf2(u);
             f2 r;
-            r[0] = 1.f / (1.f + __expf(-x[0]));
-            r[1] = 1.f / (1.f + __expf(-x[1]));
+            r[0] = __builtin_amdgcn_rcpf(1.f + __expf(-x[0]));
+            r[1] = __builtin_amdgcn_rcpf(1.f + __expf(-x[1]));
             return r;
         } else return bf2(u);
     };

@@ -60,7 +60,7 @@ __device__ __forceinline__ void shift_history(const DecConv &c, int nh, int ch, 
     for (int j = 0; j < 3; ++j) ho[((size_t)nh * 3 + j) * D + ch] = raw[j + 1];
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 template <typename In, int DK, int DV, bool PRO>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(

@@ -104,21 +104,35 @@ template <> struct Mma<float> {
 };
 
 // Sum over aligned groups of G lanes (G = 8, 16, 32 or 64), the result in
-// every lane of the group: DPP swaps within rows of 16 lanes (xor 1, xor 2,
-// then the half-row and row mirrors, which pair the halves once the smaller
-// groups already hold their sums), cross-lane permutes above that.
+// every lane of the group; all 64 lanes must be active. Within rows of 16
+// lanes: DPP swaps (xor 1, xor 2, then the half-row and row mirrors, which
+// pair the halves once the smaller groups already hold their sums). Across
+// rows: the row broadcasts add row 0 into row 1 and row 2 into row 3 (lanes
+// 31 and 63 then hold the 32-lane sums) and lane 31 into rows 2 and 3 (lane
+// 63 holds the total), read back with readlane.
 template <int G> __device__ __forceinline__ float lane_group_sum(float x)
 {
     static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group of 8 to 64 lanes");
-    auto dpp = [](float v, auto ctrl) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    auto dpp = [](float v, auto ctrl, auto rows) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                          decltype(rows)::value, 0xF, false));
     };
-    x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
-    x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
-    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
-    if constexpr (G >= 16) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
-    if constexpr (G >= 32) x += __shfl_xor(x, 16);
-    if constexpr (G >= 64) x += __shfl_xor(x, 32);
+    using all = std::integral_constant<int, 0xF>;
+    x += dpp(x, std::integral_constant<int, 0xB1>{}, all{});    // quad_perm [1,0,3,2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{}, all{});    // quad_perm [2,3,0,1]
+    x += dpp(x, std::integral_constant<int, 0x141>{}, all{});   // row_half_mirror
+    if constexpr (G >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}, all{});   // row_mirror
+    if constexpr (G >= 32) {
+        x += dpp(x, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});   // row_bcast:15
+        if constexpr (G == 64) {
+            x += dpp(x, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});   // row_bcast:31
+            x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        } else {
+            const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+            const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+            x = (__lane_id() < 32) ? lo : hi;
+        }
+    }
     return x;
 }
 
