@@ -7,7 +7,8 @@ sequential recurrence of the Gated Delta Rule-2 (snilld.dk, section "Hvad
 Gated DeltaNet-2 ændrer", update equation) with readout o_t = S_t^T q_t after
 the update (aifetchly-blog.pages.dev, "Gated DeltaNet-2 Guide", layer
 workflow step 4). This module only marshals numpy arrays into fp64 and calls
-it.
+it. ``gdn2_oracle_bwd.c`` holds the gradients: reverse-mode differentiation
+of that recurrence, token by token.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, 'gdn2_oracle.c')
+_SRC_BWD = os.path.join(_HERE, 'gdn2_oracle_bwd.c')
 _LIB = os.path.join(_HERE, 'libgdn2_oracle.so')
 _lib = None
 _variants = {}
@@ -30,17 +32,21 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + '.tmp'
         subprocess.check_call(['gcc', '-O2', '-std=c11', '-fPIC', '-shared', '-pthread',
-                               '-o', tmp, _SRC, '-lm'])
+                               '-o', tmp, _SRC, _SRC_BWD, '-lm'])
         os.replace(tmp, _LIB)
     return _LIB
 
 
 def _bind(lib):
     dp = ctypes.POINTER(ctypes.c_double)
-    lib.gdn2_oracle_forward.argtypes = [dp] * 9 + [ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + [ctypes.c_int] * 5
-    lib.gdn2_oracle_forward.restype = ctypes.c_int
-    lib.gdn2_oracle_decode_step.argtypes = [dp] * 8 + [ctypes.c_int] * 5
-    lib.gdn2_oracle_decode_step.restype = ctypes.c_int
+    if hasattr(lib, 'gdn2_oracle_forward'):
+        lib.gdn2_oracle_forward.argtypes = [dp] * 9 + [ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + [ctypes.c_int] * 5
+        lib.gdn2_oracle_forward.restype = ctypes.c_int
+        lib.gdn2_oracle_decode_step.argtypes = [dp] * 8 + [ctypes.c_int] * 5
+        lib.gdn2_oracle_decode_step.restype = ctypes.c_int
+    if hasattr(lib, 'gdn2_oracle_backward'):
+        lib.gdn2_oracle_backward.argtypes = [dp] * 16 + [ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + [ctypes.c_int] * 5
+        lib.gdn2_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -117,3 +123,44 @@ def decode_step(q, k, v, log_alpha, b, w, S, nthreads: int = 1, lib: Optional[st
     if rc != 0:
         raise ValueError('oracle rejected its arguments')
     return o, Sd
+
+
+def backward(q, k, v, log_alpha, b, w, S0, dO, dST=None, cu_seqlens=None, B: Optional[int] = None,
+             nthreads: int = 1, lib: Optional[str] = None):
+    """Gradients of a loss with dL/do = dO and dL/dS_T = dST (None: zero).
+
+    Inputs as in ``forward``. Returns a dict with fp64 arrays 'q', 'k', 'v',
+    'log_alpha', 'b', 'w' (shapes of those inputs) and 'S0' [N, H, dk, dv].
+    """
+    q = np.asarray(q)
+    if q.ndim == 4:
+        B = q.shape[0] if B is None else B
+        q, k, v, log_alpha, b, w, dO = (np.asarray(t).reshape(-1, *np.asarray(t).shape[2:])
+                                        for t in (q, k, v, log_alpha, b, w, dO))
+    tokens, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        N, T = len(cu) - 1, 0
+        assert cu[0] == 0 and cu[-1] == tokens
+    else:
+        cu = None
+        N = 1 if B is None else int(B)
+        T = tokens // N
+        assert T * N == tokens
+    arrs = [_f64(t) for t in (q, k, v, log_alpha, b, w)]
+    S0d, dOd, dSTd = _f64(S0), _f64(dO), _f64(dST)
+    assert dOd.shape == (tokens, H, dv)
+    for x in (S0d, dSTd):
+        if x is not None:
+            assert x.shape == (N, H, dk, dv)
+    g = {name: np.zeros(a.shape) for name, a in zip(('q', 'k', 'v', 'log_alpha', 'b', 'w'), arrs)}
+    g['S0'] = np.zeros((N, H, dk, dv))
+    rc = _load(lib).gdn2_oracle_backward(*[_ptr(a) for a in arrs], _ptr(S0d), _ptr(dOd), _ptr(dSTd),
+                                         _ptr(g['q']), _ptr(g['k']), _ptr(g['v']), _ptr(g['log_alpha']),
+                                         _ptr(g['b']), _ptr(g['w']), _ptr(g['S0']),
+                                         None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         T, N, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError('oracle rejected its arguments')
+    return g

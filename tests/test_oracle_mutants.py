@@ -101,3 +101,47 @@ def test_some_prologue_pin_catches(tmp_path, name, old, new):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f'no pin catches the planted mistake "{name}"'
+
+
+# ---- the gradient oracle (C): planted mistakes in a copy of its source
+import backward_pins
+
+BWD_SRC = os.path.join(os.path.dirname(oracle.__file__), 'gdn2_oracle_bwd.c')
+
+BWD_MUTANTS = [
+    ('dq from the previous state', 's += Snew[(size_t)c * dv + j] * dO[j];', 's += Sprev[(size_t)c * dv + j] * dO[j];'),
+    ('readout gradient dropped', 'G[(size_t)c * dv + j] += q[c] * dO[j];', 'G[(size_t)c * dv + j] += 0.0 * q[c] * dO[j];'),
+    ('erase term sign', 'dSd[(size_t)c * dv + j] = G[(size_t)c * dv + j] - b[c] * k[c] * dd[j];',
+     'dSd[(size_t)c * dv + j] = G[(size_t)c * dv + j] + b[c] * k[c] * dd[j];'),
+    ('erase-key gradient sign', 's -= Sd[(size_t)c * dv + j] * dd[j];', 's += Sd[(size_t)c * dv + j] * dd[j];'),
+    ('decay gradient from the undecayed state', 's += dSd[(size_t)c * dv + j] * Sd[(size_t)c * dv + j];',
+     's += dSd[(size_t)c * dv + j] * Sprev[(size_t)c * dv + j];'),
+    ('state gradient not decayed', 'G[(size_t)c * dv + j] = al * dSd[(size_t)c * dv + j];',
+     'G[(size_t)c * dv + j] = dSd[(size_t)c * dv + j];'),
+    ('key gradient misses the erase path', 'dkk[c] += dbk[c] * b[c];', 'dkk[c] += 0.0 * dbk[c];'),
+    ('write and value gradients swapped', [('dw[j] = dd[j] * v[j];', 'dw[j] = dd[j] * w[j];'),
+                                           ('dvv[j] = dd[j] * w[j];', 'dvv[j] = dd[j] * v[j];')], None),
+]
+
+
+@pytest.mark.parametrize('name,old,new', BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_some_backward_pin_catches(tmp_path, name, old, new):
+    mut = open(BWD_SRC).read()
+    for a, b in (old if new is None else [(old, new)]):
+        assert a in mut, name
+        mut = mut.replace(a, b, 1)
+    c = tmp_path / 'mb.c'
+    c.write_text(mut)
+    so = tmp_path / 'libmb.so'
+    subprocess.check_call(['gcc', '-O2', '-std=c11', '-fPIC', '-shared', '-pthread', '-o', str(so), str(c), '-lm'])
+
+    def bwd(*a, **kw):
+        return oracle.backward(*a, **kw, lib=str(so))
+
+    caught = []
+    for pin in backward_pins.ALL:
+        try:
+            pin(bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f'no pin catches the planted mistake "{name}"'

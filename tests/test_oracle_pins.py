@@ -62,3 +62,11 @@ import prologue_pins
 @pytest.mark.parametrize('pin', prologue_pins.ALL, ids=[p.__name__ for p in prologue_pins.ALL])
 def test_prologue_pin(pin):
     pin(prologue_oracle)
+
+
+import backward_pins
+
+
+@pytest.mark.parametrize('pin', backward_pins.ALL, ids=[p.__name__ for p in backward_pins.ALL])
+def test_backward_pin(pin):
+    pin(oracle.backward)
