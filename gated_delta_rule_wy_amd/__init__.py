@@ -31,6 +31,7 @@ EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
            'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_gates',
            'gdn2_decode_step', 'gdn2_decode_step_gates',
            'gdn2_chunk_fwd_prologue', 'gdn2_decode_step_prologue',
+           'gdn2_chunk_bwd_workspace_bytes', 'gdn2_chunk_bwd',
            'gdn2_profile_begin', 'gdn2_profile_end', 'gdn2_profile_kernel')
 
 
@@ -73,6 +74,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn2_chunk_fwd_prologue.restype = i
     lib.gdn2_decode_step_prologue.argtypes = [vp] * 6 + [pc] + [vp] * 2 + [i] * 6
     lib.gdn2_decode_step_prologue.restype = i
+    lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [i] * 8
+    lib.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn2_chunk_bwd.argtypes = [vp] * 10 + [i] * 7 + [vp] * 7 + [vp, sz]
+    lib.gdn2_chunk_bwd.restype = i
     lib.gdn2_profile_begin.argtypes = [i]
     lib.gdn2_profile_begin.restype = i
     lib.gdn2_profile_end.argtypes = []
@@ -371,3 +376,52 @@ def decode_step_prologue(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.
     if st != GDN2_OK:
         raise Gdn2Error(st, 'gdn2_decode_step_prologue')
     return out
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+              b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor], dO: torch.Tensor,
+              dST: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of a loss through ``chunk_fwd`` (per-channel gates): given
+    dO = dL/do [B, T, H, dv] float32 and dST = dL/dS_T [N, H, dk, dv] (or
+    None), returns float32 tensors {'q', 'k', 'v', 'log_alpha', 'b', 'w'}
+    shaped like those inputs and 'S0' [N, H, dk, dv]."""
+    if q.dim() != 4:
+        raise ValueError('q must be [B, T, H, dk]')
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (('q', q, dk), ('k', k, dk), ('v', v, dv), ('b', b, dk), ('w', w, dv)):
+        _check(t, name, (B, T, H, d), dt, dev)
+    _check(log_alpha, 'log_alpha', (B, T, H, dk), torch.float32, dev)
+    _check(dO, 'dO', (B, T, H, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+            raise ValueError('cu_seqlens must be a 1-D int32 tensor on the same device')
+        if not cu_seqlens.is_contiguous():
+            raise ValueError('cu_seqlens must be contiguous')
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (('S0', S0), ('dST', dST)):
+        if t is not None:
+            _check(t, name, (N, H, dk, dv), torch.float32, dev)
+    g = {name: torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+         for name, d in (('q', dk), ('k', dk), ('v', dv), ('log_alpha', dk), ('b', dk), ('w', dv))}
+    g['S0'] = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    varlen = cu_seqlens is not None
+    need = _lib.gdn2_chunk_bwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen))
+    if need == 0:
+        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, 'gdn2_chunk_bwd_workspace_bytes')
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    set_stream()
+    st = _lib.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO),
+                             _ptr(dST), _ptr(cu_seqlens), B, T, N, H, dk, dv, code,
+                             _ptr(g['q']), _ptr(g['k']), _ptr(g['v']), _ptr(g['log_alpha']), _ptr(g['b']),
+                             _ptr(g['w']), _ptr(g['S0']), _ptr(workspace),
+                             workspace.numel() * workspace.element_size())
+    if st != GDN2_OK:
+        raise Gdn2Error(st, 'gdn2_chunk_bwd')
+    return g

@@ -271,6 +271,56 @@ int gdn2_decode_step(const void *q, const void *k, const void *v, const float *l
                                   out_dtype);
 }
 
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
+                                      gdn2_dtype in_dtype, int varlen)
+{
+    gdn2::ChunkPlan plan;
+    if (chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan) != GDN2_OK) return 0;
+    gdn2::BwdPlan bp;
+    if (!gdn2::chunk_bwd_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, &bp)) return 0;
+    return bp.total_bytes > 0 ? bp.total_bytes : 256;
+}
+
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const void *b, const void *w, const float *S0, const float *dO, const float *dST,
+                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                   gdn2_dtype in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                   float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes)
+{
+    gdn2::ChunkPlan plan;
+    const int varlen = cu_seqlens != nullptr;
+    int st = chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan);
+    if (st != GDN2_OK) return st;
+    gdn2::BwdPlan bp;
+    if (!gdn2::chunk_bwd_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, &bp))
+        return GDN2_ERR_UNSUPPORTED;
+    const bool have_tokens = (long long)B * T > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk_ || !dv_ || !dlog_alpha ||
+                        !db || !dw))
+        return GDN2_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dST, cu_seqlens, dq, dk_, dv_, dlog_alpha, db, dw, dS0,
+                          workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID;
+    if (!workspace || workspace_bytes < bp.total_bytes) return GDN2_ERR_WORKSPACE;
+    gdn2::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.b = b; a.w = w;
+    a.log_alpha = log_alpha;
+    a.S0 = S0;
+    a.dO = dO;
+    a.dST = dST;
+    a.cu_seqlens = cu_seqlens;
+    a.B = B; a.T = T; a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = in_dtype == GDN2_BF16;
+    a.dq = dq; a.dk_ = dk_; a.dv_ = dv_; a.dlog_alpha = dlog_alpha; a.db = db; a.dw = dw;
+    a.dS0 = dS0;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    prof_call();
+    if (gdn2::launch_chunk_bwd(a, bp, g_stream) != hipSuccess) return GDN2_ERR_HIP;
+    return GDN2_OK;
+}
+
 static int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                        const void *b, const void *w, int gates, const gdn2_short_conv *conv, float *S, void *o,
                        int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)

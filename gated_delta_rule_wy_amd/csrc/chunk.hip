@@ -2,7 +2,7 @@
 // the dispatch over input type and head sizes. The kernels are in
 // chunk_impl.hpp; each (input type, d_k) is instantiated in a translation
 // unit of its own (chunk_<type>_d<d_k>.hip) so they compile in parallel.
-#include "chunk_impl.hpp"
+#include "chunk_bwd_impl.hpp"
 
 namespace gdn2 {
 
@@ -56,6 +56,61 @@ static size_t blk_bytes(int dk, bool bf16)
     return 0;
 }
 
+static size_t bblk_bytes(int dk, bool bf16)
+{
+    switch (dk) {
+    case 16: return bf16 ? 0 : BBlk<float, 16>::bytes;
+    case 32: return bf16 ? BBlk<_Float16, 32>::bytes : BBlk<float, 32>::bytes;
+    case 64: return bf16 ? BBlk<_Float16, 64>::bytes : BBlk<float, 64>::bytes;
+    case 128: return bf16 ? BBlk<_Float16, 128>::bytes : BBlk<float, 128>::bytes;
+    }
+    return 0;
+}
+
+bool chunk_bwd_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, BwdPlan *p)
+{
+    if (!chunk_plan(B, T, N, H, dk, dv, bf16, varlen, &p->fwd)) return false;
+    const size_t ops = bf16 ? 2 : 4;
+    const auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t slots = (size_t)p->fwd.max_chunks * H;
+    p->bblock_bytes = bblk_bytes(dk, bf16);
+    p->state_bytes = (size_t)dk * dv * ops;
+    p->delta_bytes = (size_t)64 * dv * ops;
+    p->off_bblocks = r256(p->fwd.total_bytes);
+    p->off_states = p->off_bblocks + r256(slots * p->bblock_bytes);
+    p->off_delta = p->off_states + r256(slots * p->state_bytes);
+    p->off_grads = p->off_delta + r256(slots * p->delta_bytes);
+    p->total_bytes = p->off_grads + r256(slots * p->state_bytes);
+    return p->bblock_bytes != 0;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, const BwdPlan &p, hipStream_t st)
+{
+    if (a.cu_seqlens) {
+        prof_before("gdn2_chunk_plan", st);
+        hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.N, a.T,
+                           p.fwd.max_chunks, (int32_t *)a.workspace);
+        prof_after(st);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (a.bf16) {
+        switch (a.dk) {
+        case 32: return dispatch_bwd<uint16_t, _Float16, 32>(a, p, st);
+        case 64: return dispatch_bwd<uint16_t, _Float16, 64>(a, p, st);
+        case 128: return dispatch_bwd<uint16_t, _Float16, 128>(a, p, st);
+        }
+    } else {
+        switch (a.dk) {
+        case 16: return dispatch_bwd<float, float, 16>(a, p, st);
+        case 32: return dispatch_bwd<float, float, 32>(a, p, st);
+        case 64: return dispatch_bwd<float, float, 64>(a, p, st);
+        case 128: return dispatch_bwd<float, float, 128>(a, p, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p)
 {
     if (dv != 16 && dv != 32 && dv != 64 && dv != 128) return false;
@@ -74,6 +129,13 @@ bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varl
 }
 
 static hipError_t launch_chunk_fwd_kernels(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st);
+extern template hipError_t dispatch_bwd<uint16_t, _Float16, 32>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<uint16_t, _Float16, 64>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<uint16_t, _Float16, 128>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<float, float, 16>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<float, float, 32>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<float, float, 64>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
+extern template hipError_t dispatch_bwd<float, float, 128>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
 
 // Convolution history after a prefill (fused prologue): for each sequence
 // and head, the last three raw inputs of q, k and v, reaching back into the

@@ -1,0 +1,760 @@
+// Chunkwise backward of the Gated Delta Rule-2 prefill on gfx950.
+//
+// A loss with gradients dO (outputs) and dS_T (final states) propagates
+// backwards through each chunk's affine map of the state. With the forward
+// chunk quantities (chunk_impl.hpp: W = T E, Q+, Khat, P, T, gamma = e^{g_n}):
+//   S_n = M S_c + Khat^T T U,  M = Diag(gamma) - Khat^T W
+//   O   = R S_c + P T U,       R = Q+ - P W
+// so the gradient at a chunk's start state, from the gradient G at its end
+// state, is
+//   G_c = M^T G + R^T dO = gamma * G + N^T G + R^T dO,  N^T = -W^T Khat,
+//   R^T = Q+^T - W^T P^T
+// (the chunk form is the plainest reading of the pages' chunkwise WY form;
+// snilld.dk, section "Hvad betyder det for træning og inferens").
+//
+// Kernels (all per head, chunk blocks head-major like the forward's):
+//  * chunk_bprep: per (chunk, head), N^T and R^T from the forward operand
+//    block, as MFMA A-fragments (gamma stays fp32, applied separately).
+//  * chunk_rpass: per (sequence, head, column slice), the chain G_c in
+//    registers from the last chunk to the first; stores each chunk's end
+//    gradient G, returns dS0.
+#pragma once
+
+#include "chunk_impl.hpp"
+
+namespace gdn2 {
+
+// Backward operand block for one (chunk, head).
+template <typename Op, int DK> struct BBlk {
+    using M = Mma<Op>;
+    static constexpr int KB = M::KB;
+    static constexpr int NKB = DK / KB;   // k-blocks over key channels
+    static constexpr int NSB = 64 / KB;   // k-blocks over chunk rows
+    static constexpr int NCT = DK / 16;   // 16-row tiles over key channels
+    static constexpr size_t FRAG = 64 * 16;
+    static constexpr size_t oN = 0;                          // N^T [NCT][NKB]
+    static constexpr size_t oR = oN + NCT * NKB * FRAG;      // R^T [NCT][NSB]
+    static constexpr size_t oG = oR + NCT * NSB * FRAG;      // gamma float[DK]
+    static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
+};
+
+// ---------------------------------------------------------------------------
+// N^T = (-W)^T Khat and R^T = Q+^T + (-W)^T P^T from one forward block.
+// The forward fragments serve directly as B operands: a Khat^T A-fragment
+// (rows = channels, contraction = chunk rows) is the B-fragment of Khat, and
+// a P A-fragment the B-fragment of P^T. (-W)^T and Q+ go through LDS.
+template <typename Op, int DK>
+__global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restrict__ ops, uint8_t *__restrict__ bops,
+                                                          Seqs sq, int H)
+{
+    using M = Mma<Op>;
+    using L = Blk<Op, DK>;
+    using BL = BBlk<Op, DK>;
+    using frag = typename M::frag;
+    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
+    constexpr int LDW = 64 + 8;          // (-W)^T rows (chunk rows along a row)
+    constexpr int LDQ = DK + 8;          // Q+ rows
+    constexpr int LDX = (DK > 64 ? DK : 64) + 8;   // output staging rows (N^T: DK wide; R^T: 64 wide)
+    __shared__ __attribute__((aligned(16))) Op sWt[DK * LDW];
+    __shared__ __attribute__((aligned(16))) Op sQp[64 * LDQ];
+    __shared__ __attribute__((aligned(16))) Op sX[DK * LDX];
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
+    if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
+    const uint8_t *blk = ops + ((size_t)h * sq.max_chunks + j) * L::bytes;
+    uint8_t *bb = bops + ((size_t)h * sq.max_chunks + j) * BL::bytes;
+
+    // unpack -W transposed and Q+ as is
+    for (int x = t; x < 4 * NKB * 64; x += 256) {
+        const int f = x >> 6, ln = x & 63, mt = f / NKB, kb = f % NKB, m = ln & 15, g = ln >> 4;
+        const frag w = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)f * 64 + ln) * 16);
+        const frag qf = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)f * 64 + ln) * 16);
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int c = kb * KB + kofs(g, i), r = 16 * mt + m;
+            sWt[c * LDW + r] = w[i];
+            sQp[r * LDQ + c] = qf[i];
+        }
+    }
+    if (t < DK) reinterpret_cast<float *>(bb + BL::oG)[t] = reinterpret_cast<const float *>(blk + L::oG)[t];
+    __syncthreads();
+
+    // N^T tiles (at, bt): contraction over the chunk rows
+    for (int tile = wv; tile < NCT * NCT; tile += 4) {
+        const int at = tile / NCT, bt = tile % NCT;
+        f4 acc = f4zero();
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const frag a = lds_row_frag<Op>(sWt + (16 * at + m16) * LDW, sb * KB, g4);
+            const frag b = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)(bt * NSB + sb) * 64 + lane) * 16);
+            acc = M::mma(a, b, acc);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sX[(16 * at + 4 * g4 + ii) * LDX + 16 * bt + m16] = (Op)acc[ii];
+    }
+    __syncthreads();
+    for (int f = wv; f < NCT * NKB; f += 4) {
+        const int at = f / NKB, kb = f % NKB;
+        *reinterpret_cast<frag *>(bb + BL::oN + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sX + (16 * at + m16) * LDX, kb * KB, g4);
+    }
+    __syncthreads();
+
+    // R^T tiles (at, rt): Q+^T plus (-W)^T P^T (P lower triangular)
+    for (int tile = wv; tile < NCT * 4; tile += 4) {
+        const int at = tile / 4, rt = tile % 4;
+        f4 acc = f4zero();
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            if (sb > L::sbmax(rt)) break;
+            const frag a = lds_row_frag<Op>(sWt + (16 * at + m16) * LDW, sb * KB, g4);
+            const frag b = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)L::tpos(rt, sb) * 64 + lane) * 16);
+            acc = M::mma(a, b, acc);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int a_ = 16 * at + 4 * g4 + ii, r = 16 * rt + m16;
+            sX[a_ * LDX + r] = (Op)(acc[ii] + (float)sQp[r * LDQ + a_]);
+        }
+    }
+    __syncthreads();
+    for (int f = wv; f < NCT * NSB; f += 4) {
+        const int at = f / NSB, sb = f % NSB;
+        *reinterpret_cast<frag *>(bb + BL::oR + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(sX + (16 * at + m16) * LDX, sb * KB, g4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state pass. Workgroup = (chain, slice of 16*NC value columns), 8
+// waves: state waves 0..3 hold the gradient G of their key rows (fp32 in
+// registers), loader waves 4..7 stage dO of the next chunk (hi + lo f16, the
+// B operand) in LDS. One barrier per chunk: G and dO live in two LDS buffers
+// by chunk parity. Each step stores the incoming G (the gradient at the
+// chunk's end state) for the gradient kernel.
+template <typename Op, int DK, int DV, int NC>
+__global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restrict__ dO, const float *__restrict__ dST,
+                                                          float *__restrict__ dS0, Seqs sq, int H,
+                                                          const uint8_t *__restrict__ bops, Op *__restrict__ gbuf)
+{
+    using M = Mma<Op>;
+    using BL = BBlk<Op, DK>;
+    using frag = typename M::frag;
+    constexpr int KB = M::KB, NE = M::NE, NKB = BL::NKB, NSB = BL::NSB, NCT = BL::NCT;
+    constexpr int TPW = (NCT + 3) / 4;
+    constexpr int TPK = KB / 16;
+    constexpr int NSL = DV / (16 * NC);
+    __shared__ __attribute__((aligned(16))) Op sG[2][NC][NCT * 64 * 4];
+    __shared__ __attribute__((aligned(16))) Op sD[2][NC][2 * NSB * 64 * NE];
+
+    const int Lid = blockIdx.x;
+    const int kq = Lid >> 3, js = kq % NSL;
+    const int chain = (kq / NSL) * 8 + (Lid & 7);
+    if (chain >= sq.m.N * H) return;
+    const int i = chain / H, h = chain % H;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int col0 = 16 * NC * js;
+    const size_t sbase = ((size_t)i * H + h) * DK * DV;
+    const int tb = sq.t0(i), te = sq.t1(i);
+    const int cbeg = sq.m.chunk0(i);
+    const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
+    const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
+    // step k handles chunk nch - 1 - k
+    auto bblk = [&](int k) { return bops + (slot0 + max(nch - 1 - k, 0)) * BL::bytes; };
+
+    if (wv < 4) {
+        __builtin_amdgcn_s_setprio(3);
+        struct F {
+            frag Nt[TPW][NKB], Rt[TPW][NSB];
+            f4 gam[TPW];
+        };
+        auto fload = [&](F &f, const uint8_t *b) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    f.Nt[u][kb] = *reinterpret_cast<const frag *>(b + BL::oN + ((size_t)(ct * NKB + kb) * 64 + lane) * 16);
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+                    f.Rt[u][sb] = *reinterpret_cast<const frag *>(b + BL::oR + ((size_t)(ct * NSB + sb) * 64 + lane) * 16);
+                f.gam[u] = *reinterpret_cast<const f4 *>(b + BL::oG + (size_t)(16 * ct + 4 * g4) * 4);
+            }
+        };
+        f4 Gr[NC][TPW];
+#pragma unroll
+        for (int q = 0; q < NC; ++q)
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                Gr[q][u] = f4zero();
+                if (ct < NCT) {
+                    if (dST) {
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            Gr[q][u][ii] = dST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16];
+                    }
+                    lds_tile_store<Op>(sG[0][q] + ct * 256, lane, Gr[q][u]);
+                }
+            }
+        // fp32 operands (four times the fragments) load at the step itself;
+        // f16 ones two steps ahead into a ring of three
+        constexpr bool RING = sizeof(Op) == 2;
+        F f0, f1, f2;
+        if (RING && nch > 0) {
+            fload(f0, bblk(0));
+            fload(f1, bblk(1));
+        }
+        auto step = [&](int k, F &cur, F &pre, int par) {
+            const int c = nch - 1 - k;
+            if constexpr (!RING) fload(cur, bblk(k));
+            Op *gp = gbuf + (slot0 + c) * DK * DV;
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        gp[(size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)Gr[q][u][ii];
+                }
+            __syncthreads();   // G and dO of this step in LDS buffer `par`
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    f4 s = Gr[q][u] * cur.gam[u];
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+                        s = M::mma(cur.Nt[u][kb], lds_bfrag<Op>(sG[par][q] + kb * TPK * 256, lane), s);
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) {
+                        const frag dh = *reinterpret_cast<const frag *>(&sD[par][q][((0 * NSB + sb) * 64 + lane) * NE]);
+                        const frag dl = *reinterpret_cast<const frag *>(&sD[par][q][((1 * NSB + sb) * 64 + lane) * NE]);
+                        s = M::mma(cur.Rt[u][sb], dh, s);
+                        s = M::mma(cur.Rt[u][sb], dl, s);
+                    }
+                    Gr[q][u] = s;
+                    lds_tile_store<Op>(sG[par ^ 1][q] + ct * 256, lane, s);
+                }
+            }
+            if constexpr (RING) fload(pre, bblk(k + 2));
+        };
+        int k = 0;
+        if constexpr (RING) {
+            for (; k + 6 <= nch; k += 6) {
+                step(k, f0, f2, 0);
+                step(k + 1, f1, f0, 1);
+                step(k + 2, f2, f1, 0);
+                step(k + 3, f0, f2, 1);
+                step(k + 4, f1, f0, 0);
+                step(k + 5, f2, f1, 1);
+            }
+            // tail: up to five more steps, ring slot k % 3 and parity k % 2
+            if (k < nch) step(k, f0, f2, 0);
+            if (k + 1 < nch) step(k + 1, f1, f0, 1);
+            if (k + 2 < nch) step(k + 2, f2, f1, 0);
+            if (k + 3 < nch) step(k + 3, f0, f2, 1);
+            if (k + 4 < nch) step(k + 4, f1, f0, 0);
+        } else {
+            for (; k + 2 <= nch; k += 2) {
+                step(k, f0, f0, 0);
+                step(k + 1, f0, f0, 1);
+            }
+            if (k < nch) step(k, f0, f0, 0);
+        }
+        if (dS0) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (ct >= NCT) continue;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        dS0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = Gr[q][u][ii];
+                }
+        }
+    } else {
+        // loader waves: thread `to` holds row ur, columns uc..uc+3 of each tile
+        const int to = t - 256, ur = to >> 2, uc = 4 * (to & 3);
+        const int usb = ur / KB, usl = ur % KB;
+        const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
+        struct D4 { f4 x[NC]; bool ok; };
+        auto dload = [&](D4 &d, int k) {
+            const int c = max(nch - 1 - k, 0);
+            const int tok = tb + 64 * c + ur;
+            d.ok = k < nch && tok < te;
+            const size_t off = ((size_t)min(tok, te - 1) * H + h) * DV + col0 + uc;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) d.x[q] = *reinterpret_cast<const f4 *>(dO + off + 16 * q);
+        };
+        auto dstage = [&](const D4 &d, int par) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = d.ok ? d.x[q][e] : 0.f;
+                    const Op hi = (Op)x;
+                    const int ln = (uc + e) + 16 * ug;
+                    sD[par][q][((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
+                    sD[par][q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(x - (float)hi);
+                }
+        };
+        D4 d0, d1, d2;
+        if (nch > 0) {
+            dload(d0, 0);
+            dload(d1, 1);
+            dstage(d0, 0);
+        }
+        auto step = [&](int k, D4 &nxt, D4 &pre, int par) {
+            __syncthreads();
+            dstage(nxt, par ^ 1);    // dO of step k + 1
+            dload(pre, k + 2);
+        };
+        int k = 0;
+        for (; k + 6 <= nch; k += 6) {
+            step(k, d1, d2, 0);
+            step(k + 1, d2, d0, 1);
+            step(k + 2, d0, d1, 0);
+            step(k + 3, d1, d2, 1);
+            step(k + 4, d2, d0, 0);
+            step(k + 5, d0, d1, 1);
+        }
+        if (k < nch) step(k, d1, d2, 0);
+        if (k + 1 < nch) step(k + 1, d2, d0, 1);
+        if (k + 2 < nch) step(k + 2, d0, d1, 0);
+        if (k + 3 < nch) step(k + 3, d1, d2, 1);
+        if (k + 4 < nch) step(k + 4, d2, d0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients, one workgroup (4 waves) per (chunk, head), from the
+// forward's chunk start state S_c and Delta, the reverse pass's end gradient
+// G, the forward block's P and T, dO and the raw inputs. With g the chunk's
+// cumulative log decay (g_n its last row) and, per channel,
+// e^{g_r - g_s} written Dec_rs:
+//   dDelta = P^T dO + Khat G,   dX = T^T dDelta,   dv = dX * w,  dw = dX * v
+//   dA = -strict_tril(dX Delta^T),   dP = tril(dO Delta^T)
+//   dq  = (dO S_c^T) * e^g + (dP o Dec) k
+//   dE~ = -(dX S_c^T) * e^g + (dA o Dec) k          (dE scaled by e^g)
+//   dk  = (dP o Dec)^T q + (dA o Dec)^T (b k) + (Delta G^T) * e^{g_n - g} + dE~ * b
+//   db  = dE~ * k
+//   dlog_alpha = reverse cumulative sum over the chunk of
+//     dq q - (dk through k e^{-g}) k - (dk through Khat) k + dE~ b k,
+//     plus, at the last row, sum_r (dk through Khat) k + e^{g_n} diag(G S_c^T)
+// where (M o Dec) x means sum_s M_rs x_s e^{g_r - g_s}.
+// Phase A (value columns in slices through LDS, matrix cores on the operand
+// type) forms dDelta, dX, dv, dw and accumulates dA, dP, dO S_c^T, dX S_c^T,
+// Delta G^T in registers. Phase B (key channels in slices, fp32 matrix
+// cores) forms the four decayed products blockwise over 16-row blocks:
+// off-diagonal blocks S < R through the references ref_{S+1} (every factor
+// <= 1), diagonal blocks around the block's middle row (bounded in fp32 for
+// log alpha >= -7 per token), then the elementwise gradients and the reverse
+// cumulative sum.
+template <typename In, typename Op, int DK, int DV>
+__global__ __launch_bounds__(256) void chunk_grad_kernel(
+    const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v, const float *__restrict__ la,
+    const In *__restrict__ b, const In *__restrict__ w, const float *__restrict__ dO, Seqs sq, int H,
+    const uint8_t *__restrict__ ops, const Op *__restrict__ sbuf, const Op *__restrict__ dbuf,
+    const Op *__restrict__ gbuf, float *__restrict__ dq, float *__restrict__ dk_, float *__restrict__ dv_,
+    float *__restrict__ dla, float *__restrict__ db, float *__restrict__ dw)
+{
+    using M = Mma<Op>;
+    using MF = Mma<float>;
+    using L = Blk<Op, DK>;
+    using frag = typename M::frag;
+    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB;
+    constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
+    constexpr int NVS = DV / VS, VT = VS / 16, VKB = VS / KB > 0 ? VS / KB : 1;
+    constexpr int CT = DK / 16;
+    constexpr int CW = DK < 32 ? DK : 32;                 // key channels per phase-B slice
+    constexpr int NCS = DK / CW, CWT = CW / 16;
+    static_assert(VS % KB == 0 || VS < KB, "slice width");
+    // LDS: persistent tables, then phase A and phase B regions over the same bytes
+    constexpr int VSP = VS < KB ? KB : VS;                // slice width padded to a k-block (zeros)
+    constexpr int LDP = 64 + 8, LDK = DK + 8, LDV = VSP + 8;
+    constexpr size_t A_PT = 0, A_TT = A_PT + 64 * LDP, A_KH = A_TT + 64 * LDP, A_GT = A_KH + 64 * LDK,
+                     A_GR = A_GT + VS * LDK, A_SJ = A_GR + DK * LDV, A_DJ = A_SJ + DK * LDV, A_OJ = A_DJ + 64 * LDV,
+                     A_OT = A_OJ + 64 * LDV, A_XJ = A_OT + VS * LDP, A_DT = A_XJ + 64 * LDV,
+                     A_END = A_DT + VS * LDP;                                      // elements of Op
+    constexpr int LDF = 64 + 4, LDC = CW + 1;
+    constexpr size_t B_DA = 0, B_DP = B_DA + 64 * LDF, B_XT = B_DP + 64 * LDF, B_XM = B_XT + CW * LDF,
+                     B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
+                     B_G = B_QM + CW * LDF, B_Q = B_G + 64 * LDC, B_K = B_Q + 64 * LDC, B_B = B_K + 64 * LDC,
+                     B_DG = B_B + 64 * LDC, B_END = B_DG + 64 * LDC;                // floats
+    constexpr size_t REGION = (A_END * sizeof(Op) > B_END * 4 ? A_END * sizeof(Op) : B_END * 4);
+    __shared__ float sRef[5 * DK], sMid[4 * DK], sGam[DK], sKhK[DK];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
+    Op *PT = (Op *)smem + A_PT, *TT = (Op *)smem + A_TT, *Kh = (Op *)smem + A_KH, *GT = (Op *)smem + A_GT;
+    Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
+    Op *OT = (Op *)smem + A_OT, *Xj = (Op *)smem + A_XJ, *DT = (Op *)smem + A_DT;
+    float *fb = (float *)smem;
+    float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
+    float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sqv = fb + B_Q, *skv = fb + B_K, *sbv = fb + B_B;
+    float *sdG = fb + B_DG;
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
+    if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
+    const int i = sq.m.seq_of(j);
+    const int t0 = sq.t0(i) + 64 * (j - sq.m.chunk0(i));
+    const int n = min(64, sq.t1(i) - t0);
+    const size_t slot = (size_t)h * sq.max_chunks + j;
+    const uint8_t *blk = ops + slot * L::bytes;
+    const Op *Sc = sbuf + slot * DK * DV, *Dl = dbuf + slot * 64 * DV, *Gp = gbuf + slot * DK * DV;
+    auto tok_k = [&](int r) { return ((size_t)(t0 + r) * H + h) * DK; };
+    auto tok_v = [&](int r) { return ((size_t)(t0 + r) * H + h) * DV; };
+
+    // ---- phase 0: references of the 16-row blocks, per channel ----
+    for (int c = t; c < DK; c += 256) {
+        float g = 0.f;
+        sRef[c] = 0.f;
+        for (int r = 0; r < 64; ++r) {
+            g += r < n ? la[tok_k(r) + c] : 0.f;
+            if ((r & 15) == 15) sRef[((r + 1) >> 4) * DK + c] = g;
+            if ((r & 15) == 7) sMid[(r >> 4) * DK + c] = g;
+        }
+        sKhK[c] = 0.f;
+    }
+
+    // ---- phase A ----
+    for (int x = t; x < 64 * LDP; x += 256) { PT[x] = (Op)0.f; TT[x] = (Op)0.f; }
+    if constexpr (VSP > VS) {   // padding columns of the slice tiles stay zero
+        for (int x = t; x < DK * (VSP - VS); x += 256) {
+            const int c = x / (VSP - VS), jj = VS + x % (VSP - VS);
+            Gr[c * LDV + jj] = (Op)0.f;
+            Sj[c * LDV + jj] = (Op)0.f;
+        }
+        for (int x = t; x < 64 * (VSP - VS); x += 256) {
+            const int r = x / (VSP - VS), jj = VS + x % (VSP - VS);
+            Dj[r * LDV + jj] = (Op)0.f;
+            Oj[r * LDV + jj] = (Op)0.f;
+            Xj[r * LDV + jj] = (Op)0.f;
+        }
+    }
+    __syncthreads();
+    for (int x = t; x < L::NTRI * 64; x += 256) {
+        const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4;
+        int mt = 0;
+        while (mt < 3 && L::tpos(mt + 1, 0) <= f) ++mt;
+        const int sb = f - L::tpos(mt, 0);
+        const frag pf = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)f * 64 + ln) * 16);
+        const frag tf = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)f * 64 + ln) * 16);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int cc = sb * KB + kofs(g, e), r = 16 * mt + m;
+            PT[cc * LDP + r] = pf[e];
+            TT[cc * LDP + r] = tf[e];
+        }
+    }
+    for (int x = t; x < L::NCT * NSB * 64; x += 256) {
+        const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4, ct = f / NSB, sb = f % NSB;
+        const frag kf = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)f * 64 + ln) * 16);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) Kh[(sb * KB + kofs(g, e)) * LDK + 16 * ct + m] = kf[e];
+    }
+    f4 accA[4], accP[4], F1[CT], F2[CT], F3[CT];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
+#pragma unroll
+    for (int x = 0; x < CT; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
+    float gam = 0.f;
+    for (int vs = 0; vs < NVS; ++vs) {
+        const int j0 = vs * VS;
+        __syncthreads();   // previous slice's readers are done
+        for (int x = t; x < DK * VS; x += 256) {
+            const int c = x / VS, jj = x % VS;
+            const Op gv = Gp[(size_t)c * DV + j0 + jj];
+            Gr[c * LDV + jj] = gv;
+            GT[jj * LDK + c] = gv;
+            Sj[c * LDV + jj] = Sc[(size_t)c * DV + j0 + jj];
+        }
+        for (int x = t; x < 64 * VS; x += 256) {
+            const int r = x / VS, jj = x % VS;
+            Dj[r * LDV + jj] = Dl[(size_t)r * DV + j0 + jj];
+            const Op o = (Op)(r < n ? dO[tok_v(r) + j0 + jj] : 0.f);
+            Oj[r * LDV + jj] = o;
+            OT[jj * LDP + r] = o;
+        }
+        __syncthreads();
+        // dDelta row tile wv: P^T dO + Khat G
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            f4 acc = f4zero();
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+                acc = M::mma(lds_row_frag<Op>(PT + (16 * wv + m16) * LDP, sb * KB, g4),
+                             lds_row_frag<Op>(OT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                acc = M::mma(lds_row_frag<Op>(Kh + (16 * wv + m16) * LDK, kb * KB, g4),
+                             lds_row_frag<Op>(GT + (16 * vt + m16) * LDK, kb * KB, g4), acc);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) DT[(16 * vt + m16) * LDP + 16 * wv + 4 * g4 + ii] = (Op)acc[ii];
+        }
+        __syncthreads();
+        // dX row tile wv: T^T dDelta; dv, dw
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            f4 acc = f4zero();
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+                acc = M::mma(lds_row_frag<Op>(TT + (16 * wv + m16) * LDP, sb * KB, g4),
+                             lds_row_frag<Op>(DT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * wv + 4 * g4 + ii, jj = 16 * vt + m16;
+                Xj[r * LDV + jj] = (Op)acc[ii];
+                if (r < n) {
+                    const size_t o = tok_v(r) + j0 + jj;
+                    dv_[o] = acc[ii] * Ld<In>::one(w + o);
+                    dw[o] = acc[ii] * Ld<In>::one(v + o);
+                }
+            }
+        }
+        __syncthreads();
+        // accumulate over this slice's columns
+#pragma unroll
+        for (int kb = 0; kb < VKB; ++kb) {
+            const frag ax = lds_row_frag<Op>(Xj + (16 * wv + m16) * LDV, kb * KB, g4);
+            const frag ao = lds_row_frag<Op>(Oj + (16 * wv + m16) * LDV, kb * KB, g4);
+            const frag ad = lds_row_frag<Op>(Dj + (16 * wv + m16) * LDV, kb * KB, g4);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const frag bd = lds_row_frag<Op>(Dj + (16 * st + m16) * LDV, kb * KB, g4);
+                accA[st] = M::mma(ax, bd, accA[st]);
+                accP[st] = M::mma(ao, bd, accP[st]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const frag bs = lds_row_frag<Op>(Sj + (16 * ct + m16) * LDV, kb * KB, g4);
+                const frag bg = lds_row_frag<Op>(Gr + (16 * ct + m16) * LDV, kb * KB, g4);
+                F1[ct] = M::mma(ao, bs, F1[ct]);
+                F2[ct] = M::mma(ax, bs, F2[ct]);
+                F3[ct] = M::mma(ad, bg, F3[ct]);
+            }
+        }
+        if (t < DK)
+            for (int jj = 0; jj < VS; ++jj) gam += (float)Gr[t * LDV + jj] * (float)Sj[t * LDV + jj];
+    }
+    __syncthreads();   // phase A's LDS is free from here
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int r = 16 * wv + 4 * g4 + ii, s_ = 16 * st + m16;
+            sdA[r * LDF + s_] = r > s_ ? -accA[st][ii] : 0.f;
+            sdP[r * LDF + s_] = r >= s_ ? accP[st][ii] : 0.f;
+        }
+    if (t < DK) sGam[t] = gam * __expf(sRef[4 * DK + t]);
+
+    // ---- phase B, key channels in slices of CW ----
+#pragma unroll
+    for (int cs = 0; cs < NCS; ++cs) {
+        const int c0 = cs * CW;
+        __syncthreads();
+        if (t < CW) {
+            float g = 0.f;
+            for (int r = 0; r < 64; ++r) {
+                g += r < n ? la[tok_k(r) + c0 + t] : 0.f;
+                sg[r * LDC + t] = g;
+            }
+        }
+        __syncthreads();
+        for (int x = t; x < 64 * CW; x += 256) {
+            const int r = x / CW, cl = x % CW, c = c0 + cl, R = r >> 4;
+            const bool ok = r < n;
+            const float kv = ok ? Ld<In>::one(k + tok_k(r) + c) : 0.f;
+            const float qv = ok ? Ld<In>::one(q + tok_k(r) + c) : 0.f;
+            const float bv = ok ? Ld<In>::one(b + tok_k(r) + c) : 0.f;
+            const float gv = sg[r * LDC + cl];
+            const float e1 = __expf(sRef[(R + 1) * DK + c] - gv), em = __expf(sMid[R * DK + c] - gv);
+            const float e2 = __expf(gv - sRef[R * DK + c]), en = __expf(gv - sMid[R * DK + c]);
+            XtT[cl * LDF + r] = kv * e1;
+            XmT[cl * LDF + r] = kv * em;
+            BtT[cl * LDF + r] = bv * kv * e2;   // row side of (dA o Dec)^T (b k), like q
+            BmT[cl * LDF + r] = bv * kv * en;
+            QtT[cl * LDF + r] = qv * e2;
+            QmT[cl * LDF + r] = qv * en;
+            sqv[r * LDC + cl] = qv;
+            skv[r * LDC + cl] = kv;
+            sbv[r * LDC + cl] = bv;
+        }
+        __syncthreads();
+        const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
+#pragma unroll
+        for (int ct = 0; ct < CWT; ++ct) {
+            const int cl = 16 * ct + m16, c = c0 + cl, ctg = cs * CWT + ct;
+            // (M o Dec) x for rows of block R
+            auto rows = [&](const float *Mt, const float *Xt, const float *Xm) {
+                f4 y = f4zero();
+                for (int S = 0; S < R; ++S) {
+                    const f4 a = *reinterpret_cast<const f4 *>(Mt + (16 * R + m16) * LDF + 16 * S + 4 * g4);
+                    const f4 bx = *reinterpret_cast<const f4 *>(Xt + cl * LDF + 16 * S + 4 * g4);
+                    const f4 p = MF::mma(a, bx, f4zero());
+                    const float ref = sRef[(S + 1) * DK + c];
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) y[ii] += p[ii] * __expf(sg[(16 * R + 4 * g4 + ii) * LDC + cl] - ref);
+                }
+                const f4 a = *reinterpret_cast<const f4 *>(Mt + (16 * R + m16) * LDF + 16 * R + 4 * g4);
+                const f4 bx = *reinterpret_cast<const f4 *>(Xm + cl * LDF + 16 * R + 4 * g4);
+                const f4 p = MF::mma(a, bx, f4zero());
+                const float mid = sMid[R * DK + c];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) y[ii] += p[ii] * __expf(sg[(16 * R + 4 * g4 + ii) * LDC + cl] - mid);
+                return y;
+            };
+            // (M o Dec)^T y for rows s of block S = R
+            auto cols = [&](const float *Mt, const float *Yt, const float *Ym) {
+                f4 z = f4zero();
+                for (int Rr = R + 1; Rr < 4; ++Rr) {
+                    f4 a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = Mt[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
+                    const f4 by = *reinterpret_cast<const f4 *>(Yt + cl * LDF + 16 * Rr + 4 * g4);
+                    const f4 p = MF::mma(a, by, f4zero());
+                    const float ref = sRef[Rr * DK + c];
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) z[ii] += p[ii] * __expf(ref - sg[(16 * R + 4 * g4 + ii) * LDC + cl]);
+                }
+                f4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = Mt[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
+                const f4 by = *reinterpret_cast<const f4 *>(Ym + cl * LDF + 16 * R + 4 * g4);
+                const f4 p = MF::mma(a, by, f4zero());
+                const float mid = sMid[R * DK + c];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) z[ii] += p[ii] * __expf(mid - sg[(16 * R + 4 * g4 + ii) * LDC + cl]);
+                return z;
+            };
+            const f4 Y1 = rows(sdP, XtT, XmT), Y2 = rows(sdA, XtT, XmT);
+            const f4 Z1 = cols(sdP, QtT, QmT), Z2 = cols(sdA, BtT, BmT);
+            const float gn = sRef[4 * DK + c];
+            float khk = 0.f;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * R + 4 * g4 + ii;
+                const float gv = sg[r * LDC + cl], eg = __expf(gv), egn = __expf(gn - gv);
+                const float qv = sqv[r * LDC + cl], kv = skv[r * LDC + cl], bv = sbv[r * LDC + cl];
+                const float dqv = F1[ctg][ii] * eg + Y1[ii];
+                const float dEe = -F2[ctg][ii] * eg + Y2[ii];
+                const float dkm = Z1[ii] + Z2[ii];
+                const float dkh = F3[ctg][ii] * egn;
+                const float dkv = dkm + dkh + dEe * bv;
+                const float dbv = dEe * kv;
+                sdG[r * LDC + cl] = dqv * qv - dkm * kv - dkh * kv + dEe * bv * kv;
+                khk += dkh * kv;
+                if (r < n) {
+                    const size_t o = tok_k(r) + c;
+                    dq[o] = dqv;
+                    dk_[o] = dkv;
+                    db[o] = dbv;
+                }
+            }
+            atomicAdd(&sKhK[c], khk);
+        }
+        __syncthreads();
+        if (t < CW) {
+            const int c = c0 + t;
+            float acc = sKhK[c] + sGam[c];
+            for (int r = 63; r >= 0; --r) {
+                acc += sdG[r * LDC + t];
+                if (r < n) dla[tok_k(r) + c] = acc;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename In, typename Op, int DK, int DV>
+static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st)
+{
+    uint8_t *ws = (uint8_t *)a.workspace;
+    ChunkArgs fa;
+    fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.b = a.b; fa.w = a.w;
+    fa.log_alpha = a.log_alpha;
+    fa.S0 = a.S0;
+    fa.o = nullptr;
+    fa.ST = nullptr;
+    fa.cu_seqlens = a.cu_seqlens;
+    fa.B = a.B; fa.T = a.T; fa.N = a.N; fa.H = a.H; fa.dk = a.dk; fa.dv = a.dv;
+    fa.gates = 0;
+    fa.bf16 = a.bf16;
+    fa.workspace = a.workspace;
+    fa.workspace_bytes = a.workspace_bytes;
+    // forward: operand blocks, then the pass keeping S_c and Delta
+    const SaveOut so = {ws + bp.off_states, ws + bp.off_delta};
+    hipError_t err = launch_t<In, Op, DK, DV>(fa, bp.fwd, st, so);
+    if (err != hipSuccess) return err;
+
+    Seqs sq;
+    sq.m.cu = a.cu_seqlens;
+    sq.m.co = a.cu_seqlens ? (const int32_t *)ws : nullptr;
+    sq.m.N = a.N;
+    sq.m.T = a.T;
+    sq.Ttot = a.cu_seqlens ? a.T : a.B * a.T;
+    sq.max_chunks = bp.fwd.max_chunks;
+    sq.gates = 0;
+    const uint8_t *ops = ws + bp.fwd.plan_bytes + bp.fwd.prog_bytes;
+    uint8_t *bops = ws + bp.off_bblocks;
+    if (bp.fwd.max_chunks > 0) {
+        prof_before("gdn2_chunk_bprep", st);
+        hipLaunchKernelGGL((chunk_bprep_kernel<Op, DK>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
+                           dim3(256), 0, st, ops, bops, sq, a.H);
+        prof_after(st);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    int cus = 0;
+    if ((err = device_cus(&cus)) != hipSuccess) return err;
+    const long long chains = (long long)a.N * a.H, groups = (chains + 7) / 8;
+    constexpr int NSL1 = DV / 16;
+    const bool two = NSL1 % 2 == 0 && 8LL * NSL1 * groups > cus;
+    const long long grid = 8LL * (two ? NSL1 / 2 : NSL1) * groups;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    Op *gbuf = (Op *)(ws + bp.off_grads);
+    prof_before("gdn2_chunk_rpass", st);
+    if constexpr (NSL1 % 2 == 0) {
+        if (two)
+            hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 2>), dim3((unsigned)grid), dim3(512), 0, st, a.dO,
+                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+        else
+            hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 1>), dim3((unsigned)grid), dim3(512), 0, st, a.dO,
+                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+    } else {
+        hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 1>), dim3((unsigned)grid), dim3(512), 0, st, a.dO, a.dST,
+                           a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+    }
+    prof_after(st);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (bp.fwd.max_chunks > 0) {
+        prof_before("gdn2_chunk_grad", st);
+        hipLaunchKernelGGL((chunk_grad_kernel<In, Op, DK, DV>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
+                           dim3(256), 0, st, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
+                           (const In *)a.b, (const In *)a.w, a.dO, sq, a.H, ops, (const Op *)(ws + bp.off_states),
+                           (const Op *)(ws + bp.off_delta), (const Op *)gbuf, a.dq, a.dk_, a.dv_, a.dlog_alpha, a.db,
+                           a.dw);
+        prof_after(st);
+    }
+    return hipGetLastError();
+}
+
+template <typename In, typename Op, int DK>
+hipError_t dispatch_bwd(const ChunkBwdArgs &a, const BwdPlan &p, hipStream_t st)
+{
+    switch (a.dv) {
+    case 16: return bwd_t<In, Op, DK, 16>(a, p, st);
+    case 32: return bwd_t<In, Op, DK, 32>(a, p, st);
+    case 64: return bwd_t<In, Op, DK, 64>(a, p, st);
+    case 128: return bwd_t<In, Op, DK, 128>(a, p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace gdn2

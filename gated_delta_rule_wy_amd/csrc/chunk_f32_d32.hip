@@ -1,6 +1,7 @@
 // Prefill kernels for fp32 inputs and d_k = 32.
-#include "chunk_impl.hpp"
+#include "chunk_bwd_impl.hpp"
 
 namespace gdn2 {
 template hipError_t dispatch_dv<float, float, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+template hipError_t dispatch_bwd<float, float, 32>(const ChunkBwdArgs &, const BwdPlan &, hipStream_t);
 }

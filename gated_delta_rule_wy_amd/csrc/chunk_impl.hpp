@@ -846,11 +846,21 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
 // its own row (registers) and the three before it (LDS, reaching into the
 // previous chunk's slot, or the history rows placed in slot 2 before the
 // first chunk).
-template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO>
+//
+// SAVE (for the backward): no output; the state waves store each chunk's
+// start state S_c [dk][dv] and Delta [64][dv] (operand type, the values the
+// step used) at (head, chunk) slots of two buffers, head-major like the
+// operand blocks.
+struct SaveOut {
+    void *S;   // [H * max_chunks][dk][dv]
+    void *D;   // [H * max_chunks][64][dv]
+};
+
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
-    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf, ConvIn cv)
+    const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf, ConvIn cv, SaveOut so)
 {
     static_assert(!PRO || !WSC, "the prologue takes per-channel gates");
     using M = Mma<Op>;
@@ -929,7 +939,21 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         if constexpr (PRO) __syncthreads();   // pairs with the output waves' staging of chunk 0
         // The prefetch of chunk c+2 is split over the two windows in which
         // the state waves would otherwise wait for the output waves.
+        const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
         auto step = [&](int c, SF &cur, SF &pre) {
+            if constexpr (SAVE) {
+                Op *sp = (Op *)so.S + (slot0 + c) * DK * DV;
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u) {
+                        const int ct = wv * TPW + u;
+                        if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            sp[(size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)Sr[q][u][ii];
+                    }
+            }
             __syncthreads();   // (1) state tiles and U ready
             f4 acc[NC], accw[NC];
 #pragma unroll
@@ -952,6 +976,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     accw[q] = M::mma(cur.nW[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), accw[q]);
 #pragma unroll
             for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sD[q] + wv * 256, lane, acc[q] + accw[q]);
+            if constexpr (SAVE) {
+                Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        dp[(size_t)(16 * wv + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)(acc[q][ii] + accw[q][ii]);
+            }
             pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready
             frag Db[NC][NSB];
@@ -1023,9 +1055,9 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         OF g0, g1, g2;
         UV u0, u1, u2;
         if (nch > 0) {
-            g0.load(blk_of(0), wo, lane);
+            if constexpr (!SAVE) g0.load(blk_of(0), wo, lane);
             uv_load(u0, 0);
-            g1.load(blk_of(1), wo, lane);
+            if constexpr (!SAVE) g1.load(blk_of(1), wo, lane);
             uv_load(u1, 1);
         }
         // PRO: taps and bias of the thread's columns (per column tile)
@@ -1127,10 +1159,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
                 }
             __syncthreads();   // (1)
-            pre.load(blk_of(c + PD), wo, lane);
+            if constexpr (!SAVE) pre.load(blk_of(c + PD), wo, lane);
             uv_load(upre, c + PD);
-            if (c > 0) store_o(c - 1);
             if constexpr (PRO) conv_u(unext, sln, sl);
+            if constexpr (SAVE) {
+                __syncthreads();   // (2)
+                return;
+            }
+            if (c > 0) store_o(c - 1);
             f4 oacc[NC];
 #pragma unroll
             for (int q = 0; q < NC; ++q) oacc[q] = f4zero();
@@ -1162,7 +1198,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         if (c < nch) step(c, g0, g2, u0, u1, u2, 0);
         if (c + 1 < nch) step(c + 1, g1, g0, u1, u2, u0, 1);
         __syncthreads();   // final
-        if (nch > 0) store_o(nch - 1);
+        if (!SAVE && nch > 0) store_o(nch - 1);
     }
 }
 
@@ -1188,7 +1224,7 @@ static hipError_t device_cus(int *cus)
 }
 
 template <typename In, typename Op, int DK, int DV>
-static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st)
+static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st, SaveOut so = {nullptr, nullptr})
 {
     uint8_t *ws = (uint8_t *)a.workspace;
     Seqs sq;
@@ -1243,10 +1279,16 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     const ConvIn cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in};
     auto pass = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)pass_grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
-                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf, cv);
+                           (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf, cv, so);
     };
     const bool wsc = a.gates & kGateW;
-    if (two) {
+    if (so.S) {
+        // the forward part of the backward: per-channel gates, raw inputs
+        if constexpr ((DV / 16) % 2 == 0) {
+            if (two) pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, false, true>);
+            else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, false, true>);
+        } else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, false, true>);
+    } else if (two) {
         if constexpr ((DV / 16) % 2 == 0) {
             if (a.pro.on) pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, true>);
             else if (wsc) pass(chunk_pass_kernel<In, Op, DK, DV, 2, true, false>);

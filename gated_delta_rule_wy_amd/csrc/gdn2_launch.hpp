@@ -69,6 +69,37 @@ struct ChunkPlan {
 // Returns false when the sizes are not supported.
 bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p);
 
+// Backward of the prefill (gradients of a loss through o and S_T).
+struct ChunkBwdArgs {
+    const void *q, *k, *v, *b, *w;
+    const float *log_alpha;
+    const float *S0;             // or null (zeros)
+    const float *dO;             // [tokens][H][dv]
+    const float *dST;            // [N][H][dk][dv] or null (zero)
+    const int32_t *cu_seqlens;
+    int B, T, N, H, dk, dv;
+    bool bf16;
+    float *dq, *dk_, *dv_, *dlog_alpha, *db, *dw;   // gradients, layouts of their inputs
+    float *dS0;                  // or null
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Backward workspace: the forward plan's regions, then (256-byte aligned)
+//   backward operand blocks   [H * max_chunks] x bblock_bytes
+//   chunk start states S_c    [H * max_chunks][dk][dv]  operand type
+//   chunk Delta               [H * max_chunks][64][dv]  operand type
+//   chunk end gradients G     [H * max_chunks][dk][dv]  operand type
+struct BwdPlan {
+    ChunkPlan fwd;
+    size_t bblock_bytes, state_bytes, delta_bytes;   // per (chunk, head)
+    size_t off_bblocks, off_states, off_delta, off_grads;
+    size_t total_bytes;
+};
+
+bool chunk_bwd_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, BwdPlan *p);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, const BwdPlan &p, hipStream_t st);
+
 // Optional per-kernel event timing (see gdn2_profile_begin): the launchers
 // bracket every kernel launch with these; they do nothing unless enabled.
 void prof_before(const char *kernel, hipStream_t st);

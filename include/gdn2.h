@@ -226,6 +226,38 @@ int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *
                               void *o, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
 
 /*
+ * Backward of gdn2_chunk_fwd: the gradients of a scalar loss L with respect
+ * to every input, given dL/do and dL/dS_T. The chunkwise form runs the
+ * forward again (keeping each chunk's start state and corrected writes),
+ * passes the state gradient from the last chunk to the first, then forms
+ * the per-chunk gradients in parallel (the pages name a fused chunkwise WY
+ * backward for training: snilld.dk, section "Hvad betyder det for træning og
+ * inferens"; aifetchly, "Gated DeltaNet-2 Guide", section "3. Chunkwise
+ * Parallel Algorithm for GPU Training").
+ *
+ *   q, k, v, log_alpha, b, w, S0, cu_seqlens, B, T, N, H, dk, dv, in_dtype
+ *                    as in gdn2_chunk_fwd (gates per channel)
+ *   dO               [tokens, H, dv] float: dL/do
+ *   dST              [N, H, dk, dv] float, or NULL for zero
+ *   dq, dk_, db, dlog_alpha   [tokens, H, dk] float (written)
+ *   dv_, dw          [tokens, H, dv] float (written)
+ *   dS0              [N, H, dk, dv] float, or NULL (not written)
+ *   workspace        device memory of at least
+ *                    gdn2_chunk_bwd_workspace_bytes(...) bytes
+ * Gradient outputs must not alias any input. Errors as in gdn2_chunk_fwd.
+ * Precondition (not checked): log_alpha >= -7 per token, so that within 16
+ * tokens the decay factors stay inside fp32 range.
+ */
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
+                                      gdn2_dtype in_dtype, int varlen);
+
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const void *b, const void *w, const float *S0, const float *dO, const float *dST,
+                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                   gdn2_dtype in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                   float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes);
+
+/*
  * Per-kernel timing, for measurement tools (not needed for computing).
  * gdn2_profile_begin(max_calls) makes this thread's next gdn2_chunk_fwd /
  * gdn2_decode_step calls (up to max_calls of them, 1..4096) record a HIP
