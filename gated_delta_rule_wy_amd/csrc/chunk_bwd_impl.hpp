@@ -380,10 +380,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     // LDS: persistent tables, then phase A and phase B regions over the same bytes
     constexpr int VSP = VS < KB ? KB : VS;                // slice width padded to a k-block (zeros)
     constexpr int LDP = 64 + 8, LDK = DK + 8, LDV = VSP + 8;
+    // f16 operands: dO (for dDelta), dDelta and dX also as low parts (value - f16(value))
+    constexpr bool SPLIT = sizeof(Op) == 2;
+    constexpr int LO = SPLIT ? 1 : 0;
     constexpr size_t A_PT = 0, A_TT = A_PT + 64 * LDP, A_KH = A_TT + 64 * LDP, A_GT = A_KH + 64 * LDK,
                      A_GR = A_GT + VS * LDK, A_SJ = A_GR + DK * LDV, A_DJ = A_SJ + DK * LDV, A_OJ = A_DJ + 64 * LDV,
                      A_OT = A_OJ + 64 * LDV, A_XJ = A_OT + VS * LDP, A_DT = A_XJ + 64 * LDV,
-                     A_END = A_DT + VS * LDP;                                      // elements of Op
+                     A_OTL = A_DT + VS * LDP, A_XJL = A_OTL + LO * VS * LDP, A_DTL = A_XJL + LO * 64 * LDV,
+                     A_END = A_DTL + LO * VS * LDP;                                // elements of Op
     constexpr int LDF = 64 + 4, LDC = CW + 1;
     constexpr size_t B_DA = 0, B_DP = B_DA + 64 * LDF, B_XT = B_DP + 64 * LDF, B_XM = B_XT + CW * LDF,
                      B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
@@ -395,6 +399,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     Op *PT = (Op *)smem + A_PT, *TT = (Op *)smem + A_TT, *Kh = (Op *)smem + A_KH, *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
     Op *OT = (Op *)smem + A_OT, *Xj = (Op *)smem + A_XJ, *DT = (Op *)smem + A_DT;
+    Op *OTl = (Op *)smem + A_OTL, *Xjl = (Op *)smem + A_XJL, *DTl = (Op *)smem + A_DTL;
     float *fb = (float *)smem;
     float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
     float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sqv = fb + B_Q, *skv = fb + B_K, *sbv = fb + B_B;
@@ -437,6 +442,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             Dj[r * LDV + jj] = (Op)0.f;
             Oj[r * LDV + jj] = (Op)0.f;
             Xj[r * LDV + jj] = (Op)0.f;
+            if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)0.f;
         }
     }
     __syncthreads();
@@ -479,9 +485,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         for (int x = t; x < 64 * VS; x += 256) {
             const int r = x / VS, jj = x % VS;
             Dj[r * LDV + jj] = Dl[(size_t)r * DV + j0 + jj];
-            const Op o = (Op)(r < n ? dO[tok_v(r) + j0 + jj] : 0.f);
+            const float of = r < n ? dO[tok_v(r) + j0 + jj] : 0.f;
+            const Op o = (Op)of;
             Oj[r * LDV + jj] = o;
             OT[jj * LDP + r] = o;
+            if constexpr (SPLIT) OTl[jj * LDP + r] = (Op)(of - (float)o);
         }
         __syncthreads();
         // dDelta row tile wv: P^T dO + Khat G
@@ -489,15 +497,21 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         for (int vt = 0; vt < VT; ++vt) {
             f4 acc = f4zero();
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
-                acc = M::mma(lds_row_frag<Op>(PT + (16 * wv + m16) * LDP, sb * KB, g4),
-                             lds_row_frag<Op>(OT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+            for (int sb = 0; sb < NSB; ++sb) {
+                const frag ap = lds_row_frag<Op>(PT + (16 * wv + m16) * LDP, sb * KB, g4);
+                acc = M::mma(ap, lds_row_frag<Op>(OT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+                if constexpr (SPLIT) acc = M::mma(ap, lds_row_frag<Op>(OTl + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+            }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
                 acc = M::mma(lds_row_frag<Op>(Kh + (16 * wv + m16) * LDK, kb * KB, g4),
                              lds_row_frag<Op>(GT + (16 * vt + m16) * LDK, kb * KB, g4), acc);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) DT[(16 * vt + m16) * LDP + 16 * wv + 4 * g4 + ii] = (Op)acc[ii];
+            for (int ii = 0; ii < 4; ++ii) {
+                const Op hi = (Op)acc[ii];
+                DT[(16 * vt + m16) * LDP + 16 * wv + 4 * g4 + ii] = hi;
+                if constexpr (SPLIT) DTl[(16 * vt + m16) * LDP + 16 * wv + 4 * g4 + ii] = (Op)(acc[ii] - (float)hi);
+            }
         }
         __syncthreads();
         // dX row tile wv: T^T dDelta; dv, dw
@@ -505,13 +519,17 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         for (int vt = 0; vt < VT; ++vt) {
             f4 acc = f4zero();
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
-                acc = M::mma(lds_row_frag<Op>(TT + (16 * wv + m16) * LDP, sb * KB, g4),
-                             lds_row_frag<Op>(DT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+            for (int sb = 0; sb < NSB; ++sb) {
+                const frag at_ = lds_row_frag<Op>(TT + (16 * wv + m16) * LDP, sb * KB, g4);
+                acc = M::mma(at_, lds_row_frag<Op>(DT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+                if constexpr (SPLIT) acc = M::mma(at_, lds_row_frag<Op>(DTl + (16 * vt + m16) * LDP, sb * KB, g4), acc);
+            }
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * wv + 4 * g4 + ii, jj = 16 * vt + m16;
-                Xj[r * LDV + jj] = (Op)acc[ii];
+                const Op hi = (Op)acc[ii];
+                Xj[r * LDV + jj] = hi;
+                if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)(acc[ii] - (float)hi);
                 if (r < n) {
                     const size_t o = tok_v(r) + j0 + jj;
                     dv_[o] = acc[ii] * Ld<In>::one(w + o);
@@ -524,12 +542,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
 #pragma unroll
         for (int kb = 0; kb < VKB; ++kb) {
             const frag ax = lds_row_frag<Op>(Xj + (16 * wv + m16) * LDV, kb * KB, g4);
+            const frag axl = SPLIT ? lds_row_frag<Op>(Xjl + (16 * wv + m16) * LDV, kb * KB, g4) : ax;
             const frag ao = lds_row_frag<Op>(Oj + (16 * wv + m16) * LDV, kb * KB, g4);
             const frag ad = lds_row_frag<Op>(Dj + (16 * wv + m16) * LDV, kb * KB, g4);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const frag bd = lds_row_frag<Op>(Dj + (16 * st + m16) * LDV, kb * KB, g4);
                 accA[st] = M::mma(ax, bd, accA[st]);
+                if constexpr (SPLIT) accA[st] = M::mma(axl, bd, accA[st]);
                 accP[st] = M::mma(ao, bd, accP[st]);
             }
 #pragma unroll
@@ -538,6 +558,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                 const frag bg = lds_row_frag<Op>(Gr + (16 * ct + m16) * LDV, kb * KB, g4);
                 F1[ct] = M::mma(ao, bs, F1[ct]);
                 F2[ct] = M::mma(ax, bs, F2[ct]);
+                if constexpr (SPLIT) F2[ct] = M::mma(axl, bs, F2[ct]);
                 F3[ct] = M::mma(ad, bg, F3[ct]);
             }
         }
