@@ -9,7 +9,8 @@ fp32 state resident, 1000 single-token steps with fresh inputs) is measured in
 the same run and reported under "decode". Also reported: the same prefill with
 scalar gates ("gate_forms": the KDA and Gated DeltaNet layouts) and on the
 layer's raw inputs with the short convolution, unit norm and sigmoids fused
-in ("prologue_form", for prefill and decode).
+in ("prologue_form", for prefill and decode), and the backward of the same
+prefill ("backward": all input gradients from seeded dO and dS_T).
 
 Prints ONE JSON line. Inputs are synthetic and seeded (gdn2_inputs), resident
 in HBM before timing starts. Per-kernel durations come from HIP events that
@@ -156,6 +157,8 @@ def bench_prefill(args, torch, gdn2, gi):
     res['gate_forms'] = forms
     if not args.no_prologue:
         res['prologue_form'] = bench_prefill_prologue(args, torch, gdn2, gi, ws)
+    if not args.no_backward:
+        res['backward'] = bench_backward(args, torch, gdn2, q, k, v, la, b, w, S0, p)
 
     if not args.no_cpu_baseline:
         import oracle
@@ -176,6 +179,58 @@ def bench_prefill(args, torch, gdn2, gi):
                                 'tokens': n_s}
         log(f'[bench] oracle {n_s} tokens in {dt:.1f}s; parity {res["parity_sample"]}')
     del q, k, v, b, w, la, o, ws, b1, la1, o1, ST1
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_backward(args, torch, gdn2, q, k, v, la, b, w, S0, p):
+    """Gradients of a loss through the same prefill (gdn2_chunk_bwd: the
+    forward again keeping chunk states, the reverse state-gradient pass and
+    the per-chunk gradients), with seeded dO and dS_T."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    rng = np.random.default_rng(12345)
+    dO = torch.from_numpy(rng.standard_normal((B, T, H, dv), dtype=np.float32)).to(q.device)
+    dST = torch.from_numpy(rng.standard_normal((B, H, dk, dv), dtype=np.float32)).to(q.device)
+    need = gdn2.lib().gdn2_chunk_bwd_workspace_bytes(B, T, B, H, dk, dv, gdn2.GDN2_BF16, 0)
+    wsb = torch.empty(need, dtype=torch.uint8, device=q.device)
+    run = lambda: gdn2.chunk_bwd(q, k, v, la, b, w, S0, dO, dST, workspace=wsb)
+    for _ in range(args.warmup):
+        g = run()
+    torch.cuda.synchronize()
+    gdn2.profile_begin(args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g = run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    prof = gdn2.profile_end()
+    avg = {kk: vv[1] / vv[0] for kk, vv in prof.items() if vv[0]}
+    TH = B * T * H
+    # reads q, k, v, b, w (bf16), log alpha and dO (fp32); writes dq, dk, db,
+    # dlog alpha, dv, dw (fp32); S0, dS_T in, dS0 out
+    nbytes = TH * (3 * dk * 2 + 2 * dv * 2 + dk * 4 + dv * 4) + TH * (4 * dk * 4 + 2 * dv * 4) + 3 * B * H * dk * dv * 4
+    log(f'[bench] backward {ms:.3f} ms/step; kernels: ' + ', '.join(f'{kk} {vv:.4f} ms' for kk, vv in avg.items()))
+    res = {'ms_per_step': round(ms, 4), 'value': B * T / (ms * 1e-3), 'unit': 'tokens/s',
+           'inputs': 'same prefill; seeded dO and dS_T; fp32 gradients',
+           'alg_bytes_per_step': int(nbytes),
+           'step_roofline_frac': round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           'kernels_ms': {kk: round(vv, 5) for kk, vv in avg.items()},
+           # the per-chunk gradient kernel reads and writes every per-token tensor
+           'roofline': roofline('gdn2_chunk_grad', nbytes, avg['gdn2_chunk_grad'], 'backward_t65536')}
+    if not args.no_cpu_baseline:
+        import oracle
+        n_s = min(T, args.cpu_sample_tokens // 4)
+        sl = slice(0, n_s)
+        h = lambda x: x[0, sl].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.backward(h(q), h(k), h(v), h(la), h(b), h(w), p.S0, h(dO), dST.cpu().numpy(),
+                        nthreads=nthreads())
+        dt = time.perf_counter() - t0
+        res['cpu_baseline'] = {'value': round(n_s / dt, 1), 'unit': 'tokens/s', 'cores': min(nthreads(), H),
+                               'kind': 'oracle',
+                               'sample': f'first {n_s} of {T} tokens, all {H} heads, fp64 reverse sweep; {dt:.1f}s'}
+    del dO, dST, wsb, g
     torch.cuda.empty_cache()
     return res
 
@@ -320,6 +375,8 @@ def main():
     ap.add_argument('--cpu-decode-steps', type=int, default=100)
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--no-decode', action='store_true')
+    ap.add_argument('--no-backward', action='store_true',
+                    help='skip the backward (gradient) timing')
     ap.add_argument('--no-prologue', action='store_true',
                     help='skip the fused-prologue (raw-input) timings')
     ap.add_argument('--no-gate-forms', action='store_true',
@@ -366,6 +423,8 @@ def main():
     out['gate_forms'] = pre['gate_forms']
     if 'prologue_form' in pre:
         out['prologue_form'] = pre['prologue_form']
+    if 'backward' in pre:
+        out['backward'] = pre['backward']
     if 'parity_sample' in pre:
         out['parity_sample'] = pre['parity_sample']
     if not args.no_decode:

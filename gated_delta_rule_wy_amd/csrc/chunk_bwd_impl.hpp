@@ -334,6 +334,34 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
     }
 }
 
+// Inclusive running sums down (REV: up) the 64 rows of NCOL columns of an
+// LDS tile with row stride ld, by all 256 threads of the workgroup: thread t
+// takes column t % NCOL and one segment of rows; segment totals pass through
+// `part` (256 floats). Contains two barriers.
+template <int NCOL, bool REV>
+__device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int t)
+{
+    constexpr int SEGS = 256 / NCOL, SL = 64 / SEGS;
+    static_assert(SEGS * NCOL == 256 && SEGS * SL == 64, "256 threads over 64 rows");
+    const int c = t % NCOL, sg = t / NCOL;
+    const int r0 = REV ? 64 - SL * (sg + 1) : SL * sg;
+    float x[SL], tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) { x[i] = buf[(r0 + i) * ld + c]; tot += x[i]; }
+    part[sg * NCOL + c] = tot;
+    __syncthreads();
+    float a = 0.f;
+    for (int s = 0; s < sg; ++s) a += part[s * NCOL + c];
+    if constexpr (!REV) {
+#pragma unroll
+        for (int i = 0; i < SL; ++i) { a += x[i]; buf[(r0 + i) * ld + c] = a; }
+    } else {
+#pragma unroll
+        for (int i = SL - 1; i >= 0; --i) { a += x[i]; buf[(r0 + i) * ld + c] = a; }
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Per-chunk gradients, one workgroup (4 waves) per (chunk, head), from the
 // forward's chunk start state S_c and Delta, the reverse pass's end gradient
@@ -394,7 +422,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                      B_G = B_QM + CW * LDF, B_Q = B_G + 64 * LDC, B_K = B_Q + 64 * LDC, B_B = B_K + 64 * LDC,
                      B_DG = B_B + 64 * LDC, B_END = B_DG + 64 * LDC;                // floats
     constexpr size_t REGION = (A_END * sizeof(Op) > B_END * 4 ? A_END * sizeof(Op) : B_END * 4);
-    __shared__ float sRef[5 * DK], sMid[4 * DK], sGam[DK], sKhK[DK];
+    __shared__ float sRef[5 * DK], sMid[4 * DK], sGam[DK], sKhK[DK], sPart[256];
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
     Op *PT = (Op *)smem + A_PT, *TT = (Op *)smem + A_TT, *Kh = (Op *)smem + A_KH, *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
@@ -418,15 +446,27 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     auto tok_v = [&](int r) { return ((size_t)(t0 + r) * H + h) * DV; };
 
     // ---- phase 0: references of the 16-row blocks, per channel ----
-    for (int c = t; c < DK; c += 256) {
-        float g = 0.f;
-        sRef[c] = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            g += r < n ? la[tok_k(r) + c] : 0.f;
-            if ((r & 15) == 15) sRef[((r + 1) >> 4) * DK + c] = g;
-            if ((r & 15) == 7) sMid[(r >> 4) * DK + c] = g;
+    // (log alpha staged through LDS with coalesced loads; the running sums
+    // then read LDS, not memory)
+    {
+        constexpr int LDL = DK + 1;
+        static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
+        for (int x = t; x < 64 * DK; x += 256) {
+            const int r = x / DK, c = x % DK;
+            fb[r * LDL + c] = r < n ? la[tok_k(r) + c] : 0.f;
         }
-        sKhK[c] = 0.f;
+        __syncthreads();
+        col_scan64<DK, false>(fb, LDL, sPart, t);
+        for (int c = t; c < DK; c += 256) {
+            sRef[c] = 0.f;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                sRef[(R + 1) * DK + c] = fb[(16 * R + 15) * LDL + c];
+                sMid[R * DK + c] = fb[(16 * R + 7) * LDL + c];
+            }
+            sKhK[c] = 0.f;
+        }
+        __syncthreads();
     }
 
     // ---- phase A ----
@@ -475,17 +515,41 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     for (int vs = 0; vs < NVS; ++vs) {
         const int j0 = vs * VS;
         __syncthreads();   // previous slice's readers are done
-        for (int x = t; x < DK * VS; x += 256) {
-            const int c = x / VS, jj = x % VS;
-            const Op gv = Gp[(size_t)c * DV + j0 + jj];
-            Gr[c * LDV + jj] = gv;
-            GT[jj * LDK + c] = gv;
-            Sj[c * LDV + jj] = Sc[(size_t)c * DV + j0 + jj];
+        // four consecutive columns per thread and iteration; the loops are
+        // unrolled so that every load is issued before the first store
+        typedef Op op4 __attribute__((ext_vector_type(4)));
+        constexpr int NG = (DK * VS / 4 + 255) / 256, ND = (64 * VS / 4 + 255) / 256;
+        op4 gv4[NG], sv4[NG], dv4[ND];
+        f4 ov4[ND];
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int x = min(t + 256 * u, DK * VS / 4 - 1), c = x / (VS / 4), jj = 4 * (x % (VS / 4));
+            gv4[u] = *reinterpret_cast<const op4 *>(Gp + (size_t)c * DV + j0 + jj);
+            sv4[u] = *reinterpret_cast<const op4 *>(Sc + (size_t)c * DV + j0 + jj);
         }
-        for (int x = t; x < 64 * VS; x += 256) {
-            const int r = x / VS, jj = x % VS;
-            Dj[r * LDV + jj] = Dl[(size_t)r * DV + j0 + jj];
-            const float of = r < n ? dO[tok_v(r) + j0 + jj] : 0.f;
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+            const int x = min(t + 256 * u, 64 * VS / 4 - 1), r = x / (VS / 4), jj = 4 * (x % (VS / 4));
+            dv4[u] = *reinterpret_cast<const op4 *>(Dl + (size_t)r * DV + j0 + jj);
+            ov4[u] = *reinterpret_cast<const f4 *>(dO + tok_v(min(r, n - 1)) + j0 + jj);
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int x = t + 256 * u, c = x / (VS / 4), jj = 4 * (x % (VS / 4));
+            if (x >= DK * VS / 4) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Gr[c * LDV + jj + e] = gv4[u][e];
+                GT[(jj + e) * LDK + c] = gv4[u][e];
+                Sj[c * LDV + jj + e] = sv4[u][e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < ND * 4; ++u) {
+            const int x = t + 256 * (u / 4), r = x / (VS / 4), jj = 4 * (x % (VS / 4)) + (u % 4);
+            if (x >= 64 * VS / 4) break;
+            Dj[r * LDV + jj] = dv4[u / 4][u % 4];
+            const float of = r < n ? ov4[u / 4][u % 4] : 0.f;
             const Op o = (Op)of;
             Oj[r * LDV + jj] = o;
             OT[jj * LDP + r] = o;
@@ -581,20 +645,22 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     for (int cs = 0; cs < NCS; ++cs) {
         const int c0 = cs * CW;
         __syncthreads();
-        if (t < CW) {
-            float g = 0.f;
-            for (int r = 0; r < 64; ++r) {
-                g += r < n ? la[tok_k(r) + c0 + t] : 0.f;
-                sg[r * LDC + t] = g;
-            }
+        for (int x = t; x < 64 * CW; x += 256) {
+            const int r = x / CW, cl = x % CW;
+            sg[r * LDC + cl] = r < n ? la[tok_k(r) + c0 + cl] : 0.f;
         }
         __syncthreads();
-        for (int x = t; x < 64 * CW; x += 256) {
+        col_scan64<CW, false>(sg, LDC, sPart, t);
+        static_assert((64 * CW) % 256 == 0, "whole rounds of the workgroup");
+#pragma unroll
+        for (int u = 0; u < 64 * CW / 256; ++u) {
+            const int x = t + 256 * u;
             const int r = x / CW, cl = x % CW, c = c0 + cl, R = r >> 4;
             const bool ok = r < n;
-            const float kv = ok ? Ld<In>::one(k + tok_k(r) + c) : 0.f;
-            const float qv = ok ? Ld<In>::one(q + tok_k(r) + c) : 0.f;
-            const float bv = ok ? Ld<In>::one(b + tok_k(r) + c) : 0.f;
+            const size_t o = tok_k(min(r, n - 1)) + c;
+            const float kv = Ld<In>::one(k + o) * (ok ? 1.f : 0.f);
+            const float qv = Ld<In>::one(q + o) * (ok ? 1.f : 0.f);
+            const float bv = Ld<In>::one(b + o) * (ok ? 1.f : 0.f);
             const float gv = sg[r * LDC + cl];
             const float e1 = __expf(sRef[(R + 1) * DK + c] - gv), em = __expf(sMid[R * DK + c] - gv);
             const float e2 = __expf(gv - sRef[R * DK + c]), en = __expf(gv - sMid[R * DK + c]);
@@ -682,13 +748,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             atomicAdd(&sKhK[c], khk);
         }
         __syncthreads();
-        if (t < CW) {
-            const int c = c0 + t;
-            float acc = sKhK[c] + sGam[c];
-            for (int r = 63; r >= 0; --r) {
-                acc += sdG[r * LDC + t];
-                if (r < n) dla[tok_k(r) + c] = acc;
-            }
+        col_scan64<CW, true>(sdG, LDC, sPart, t);
+#pragma unroll
+        for (int u = 0; u < 64 * CW / 256; ++u) {
+            const int x = t + 256 * u, r = x / CW, cl = x % CW, c = c0 + cl;
+            if (r < n) dla[tok_k(r) + c] = sdG[r * LDC + cl] + sKhK[c] + sGam[c];
         }
     }
 }
