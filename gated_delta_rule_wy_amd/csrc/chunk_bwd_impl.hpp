@@ -66,10 +66,19 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     uint8_t *bb = bops + ((size_t)h * sq.max_chunks + j) * BL::bytes;
 
     // unpack -W transposed and Q+ as is
-    for (int x = t; x < 4 * NKB * 64; x += 256) {
+    constexpr int NU = (4 * NKB * 64) / 256;   // fragment lanes per thread (all loads first)
+    frag wf[NU], qfs[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int x = t + 256 * u;
+        wf[u] = *reinterpret_cast<const frag *>(blk + L::oW + (size_t)x * 16);
+        qfs[u] = *reinterpret_cast<const frag *>(blk + L::oQ + (size_t)x * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int x = t + 256 * u;
         const int f = x >> 6, ln = x & 63, mt = f / NKB, kb = f % NKB, m = ln & 15, g = ln >> 4;
-        const frag w = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)f * 64 + ln) * 16);
-        const frag qf = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)f * 64 + ln) * 16);
+        const frag w = wf[u], qf = qfs[u];
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
             const int c = kb * KB + kofs(g, i), r = 16 * mt + m;
@@ -451,9 +460,17 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     {
         constexpr int LDL = DK + 1;
         static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
-        for (int x = t; x < 64 * DK; x += 256) {
-            const int r = x / DK, c = x % DK;
-            fb[r * LDL + c] = r < n ? la[tok_k(r) + c] : 0.f;
+        constexpr int NU = 64 * DK / 256;
+        float lv[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int x = t + 256 * u, r = x / DK, c = x % DK;
+            lv[u] = la[tok_k(min(r, n - 1)) + c];
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int x = t + 256 * u, r = x / DK, c = x % DK;
+            fb[r * LDL + c] = r < n ? lv[u] : 0.f;
         }
         __syncthreads();
         col_scan64<DK, false>(fb, LDL, sPart, t);
@@ -486,13 +503,26 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         }
     }
     __syncthreads();
-    for (int x = t; x < L::NTRI * 64; x += 256) {
+    constexpr int NPU = (L::NTRI * 64 + 255) / 256, NKU = L::NCT * NSB * 64 / 256;
+    frag pfs[NPU], tfs[NPU], kfs[NKU];
+#pragma unroll
+    for (int u = 0; u < NPU; ++u) {
+        const int x = min(t + 256 * u, L::NTRI * 64 - 1);
+        pfs[u] = *reinterpret_cast<const frag *>(blk + L::oP + (size_t)x * 16);
+        tfs[u] = *reinterpret_cast<const frag *>(blk + L::oT + (size_t)x * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NKU; ++u)
+        kfs[u] = *reinterpret_cast<const frag *>(blk + L::oK + (size_t)(t + 256 * u) * 16);
+#pragma unroll
+    for (int u = 0; u < NPU; ++u) {
+        const int x = t + 256 * u;
+        if (x >= L::NTRI * 64) break;
         const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4;
         int mt = 0;
         while (mt < 3 && L::tpos(mt + 1, 0) <= f) ++mt;
         const int sb = f - L::tpos(mt, 0);
-        const frag pf = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)f * 64 + ln) * 16);
-        const frag tf = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)f * 64 + ln) * 16);
+        const frag pf = pfs[u], tf = tfs[u];
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             const int cc = sb * KB + kofs(g, e), r = 16 * mt + m;
@@ -500,9 +530,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             TT[cc * LDP + r] = tf[e];
         }
     }
-    for (int x = t; x < L::NCT * NSB * 64; x += 256) {
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) {
+        const int x = t + 256 * u;
         const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4, ct = f / NSB, sb = f % NSB;
-        const frag kf = *reinterpret_cast<const frag *>(blk + L::oK + ((size_t)f * 64 + ln) * 16);
+        const frag kf = kfs[u];
 #pragma unroll
         for (int e = 0; e < NE; ++e) Kh[(sb * KB + kofs(g, e)) * LDK + 16 * ct + m] = kf[e];
     }
@@ -645,9 +677,18 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     for (int cs = 0; cs < NCS; ++cs) {
         const int c0 = cs * CW;
         __syncthreads();
-        for (int x = t; x < 64 * CW; x += 256) {
-            const int r = x / CW, cl = x % CW;
-            sg[r * LDC + cl] = r < n ? la[tok_k(r) + c0 + cl] : 0.f;
+        {
+            float lv[64 * CW / 256];
+#pragma unroll
+            for (int u = 0; u < 64 * CW / 256; ++u) {
+                const int x = t + 256 * u, r = x / CW, cl = x % CW;
+                lv[u] = la[tok_k(min(r, n - 1)) + c0 + cl];
+            }
+#pragma unroll
+            for (int u = 0; u < 64 * CW / 256; ++u) {
+                const int x = t + 256 * u, r = x / CW, cl = x % CW;
+                sg[r * LDC + cl] = r < n ? lv[u] : 0.f;
+            }
         }
         __syncthreads();
         col_scan64<CW, false>(sg, LDC, sPart, t);
