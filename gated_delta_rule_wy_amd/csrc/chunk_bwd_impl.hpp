@@ -34,7 +34,10 @@ template <typename Op, int DK> struct BBlk {
     static constexpr size_t FRAG = 64 * 16;
     static constexpr size_t oN = 0;                          // N^T [NCT][NKB]
     static constexpr size_t oR = oN + NCT * NKB * FRAG;      // R^T [NCT][NSB]
-    static constexpr size_t oG = oR + NCT * NSB * FRAG;      // gamma float[DK]
+    static constexpr size_t oPT = oR + NCT * NSB * FRAG;     // P^T [4][NSB] (rows = chunk rows)
+    static constexpr size_t oTT = oPT + 4 * NSB * FRAG;      // T^T [4][NSB]
+    static constexpr size_t oKH = oTT + 4 * NSB * FRAG;      // Khat [4][NKB]
+    static constexpr size_t oG = oKH + 4 * NKB * FRAG;       // gamma float[DK]
     static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
 };
 
@@ -55,9 +58,12 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     constexpr int LDW = 64 + 8;          // (-W)^T rows (chunk rows along a row)
     constexpr int LDQ = DK + 8;          // Q+ rows
     constexpr int LDX = (DK > 64 ? DK : 64) + 8;   // output staging rows (N^T: DK wide; R^T: 64 wide)
-    __shared__ __attribute__((aligned(16))) Op sWt[DK * LDW];
-    __shared__ __attribute__((aligned(16))) Op sQp[64 * LDQ];
-    __shared__ __attribute__((aligned(16))) Op sX[DK * LDX];
+    // two phases over one area: (-W)^T, Q+ and the output staging, then
+    // P^T, T^T and Khat
+    constexpr int LDP = 64 + 8, LDK = DK + 8;
+    constexpr size_t PH1 = (size_t)DK * LDW + 64 * LDQ + (size_t)DK * LDX, PH2 = 2 * 64 * LDP + 64 * LDK;
+    __shared__ __attribute__((aligned(16))) Op sArea[PH1 > PH2 ? PH1 : PH2];
+    Op *sWt = sArea, *sQp = sArea + DK * LDW, *sX = sArea + DK * LDW + 64 * LDQ;
 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
@@ -132,6 +138,61 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
         const int at = f / NSB, sb = f % NSB;
         *reinterpret_cast<frag *>(bb + BL::oR + ((size_t)f * 64 + lane) * 16) =
             lds_row_frag<Op>(sX + (16 * at + m16) * LDX, sb * KB, g4);
+    }
+    __syncthreads();
+
+    // P^T, T^T and Khat as A-fragments (rows = chunk rows) for the gradient
+    // kernel: unpack P and T transposed (over (-W)^T) and Khat^T transposed
+    // (over the staging area), then pack
+    Op *PT = sArea, *TT = sArea + 64 * LDP, *Kh = sArea + 2 * 64 * LDP;
+    for (int x = t; x < 64 * LDP; x += 256) { PT[x] = (Op)0.f; TT[x] = (Op)0.f; }
+    __syncthreads();
+    {
+        constexpr int NPU = (L::NTRI * 64 + 255) / 256, NKU = NCT * NSB * 64 / 256;
+        frag pfs[NPU], tfs[NPU], kfs[NKU];
+#pragma unroll
+        for (int u = 0; u < NPU; ++u) {
+            const int x = min(t + 256 * u, L::NTRI * 64 - 1);
+            pfs[u] = *reinterpret_cast<const frag *>(blk + L::oP + (size_t)x * 16);
+            tfs[u] = *reinterpret_cast<const frag *>(blk + L::oT + (size_t)x * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) kfs[u] = *reinterpret_cast<const frag *>(blk + L::oK + (size_t)(t + 256 * u) * 16);
+#pragma unroll
+        for (int u = 0; u < NPU; ++u) {
+            const int x = t + 256 * u;
+            if (x >= L::NTRI * 64) break;
+            const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4;
+            int mt = 0;
+            while (mt < 3 && L::tpos(mt + 1, 0) <= f) ++mt;
+            const int sb = f - L::tpos(mt, 0);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int cc = sb * KB + kofs(g, e), r = 16 * mt + m;
+                PT[cc * LDP + r] = pfs[u][e];
+                TT[cc * LDP + r] = tfs[u][e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) {
+            const int x = t + 256 * u;
+            const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4, ct = f / NSB, sb = f % NSB;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) Kh[(sb * KB + kofs(g, e)) * LDK + 16 * ct + m] = kfs[u][e];
+        }
+    }
+    __syncthreads();
+    for (int f = wv; f < 4 * NSB; f += 4) {
+        const int rt = f / NSB, sb = f % NSB;
+        *reinterpret_cast<frag *>(bb + BL::oPT + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(PT + (16 * rt + m16) * LDP, sb * KB, g4);
+        *reinterpret_cast<frag *>(bb + BL::oTT + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(TT + (16 * rt + m16) * LDP, sb * KB, g4);
+    }
+    for (int f = wv; f < 4 * NKB; f += 4) {
+        const int rt = f / NKB, kb = f % NKB;
+        *reinterpret_cast<frag *>(bb + BL::oKH + ((size_t)f * 64 + lane) * 16) =
+            lds_row_frag<Op>(Kh + (16 * rt + m16) * LDK, kb * KB, g4);
     }
 }
 
@@ -399,19 +460,19 @@ template <typename In, typename Op, int DK, int DV>
 __global__ __launch_bounds__(256) void chunk_grad_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v, const float *__restrict__ la,
     const In *__restrict__ b, const In *__restrict__ w, const float *__restrict__ dO, Seqs sq, int H,
-    const uint8_t *__restrict__ ops, const Op *__restrict__ sbuf, const Op *__restrict__ dbuf,
+    const uint8_t *__restrict__ bops, const Op *__restrict__ sbuf, const Op *__restrict__ dbuf,
     const Op *__restrict__ gbuf, float *__restrict__ dq, float *__restrict__ dk_, float *__restrict__ dv_,
     float *__restrict__ dla, float *__restrict__ db, float *__restrict__ dw)
 {
     using M = Mma<Op>;
     using MF = Mma<float>;
-    using L = Blk<Op, DK>;
+    using BL = BBlk<Op, DK>;
     using frag = typename M::frag;
-    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB;
+    constexpr int KB = M::KB, NE = M::NE, NKB = BL::NKB, NSB = BL::NSB;
     constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
     constexpr int NVS = DV / VS, VT = VS / 16, VKB = VS / KB > 0 ? VS / KB : 1;
     constexpr int CT = DK / 16;
-    constexpr int CW = DK < 32 ? DK : 32;                 // key channels per phase-B slice
+    constexpr int CW = 16;                                // key channels per phase-B slice
     constexpr int NCS = DK / CW, CWT = CW / 16;
     static_assert(VS % KB == 0 || VS < KB, "slice width");
     // LDS: persistent tables, then phase A and phase B regions over the same bytes
@@ -420,27 +481,29 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     // f16 operands: dO (for dDelta), dDelta and dX also as low parts (value - f16(value))
     constexpr bool SPLIT = sizeof(Op) == 2;
     constexpr int LO = SPLIT ? 1 : 0;
-    constexpr size_t A_PT = 0, A_TT = A_PT + 64 * LDP, A_KH = A_TT + 64 * LDP, A_GT = A_KH + 64 * LDK,
-                     A_GR = A_GT + VS * LDK, A_SJ = A_GR + DK * LDV, A_DJ = A_SJ + DK * LDV, A_OJ = A_DJ + 64 * LDV,
+    constexpr size_t A_GT = 0, A_GR = A_GT + VS * LDK, A_SJ = A_GR + DK * LDV, A_DJ = A_SJ + DK * LDV, A_OJ = A_DJ + 64 * LDV,
                      A_OT = A_OJ + 64 * LDV, A_XJ = A_OT + VS * LDP, A_DT = A_XJ + 64 * LDV,
                      A_OTL = A_DT + VS * LDP, A_XJL = A_OTL + LO * VS * LDP, A_DTL = A_XJL + LO * 64 * LDV,
                      A_END = A_DTL + LO * VS * LDP;                                // elements of Op
-    constexpr int LDF = 64 + 4, LDC = CW + 1;
+    constexpr int LDF = 64 + 4, LDC = CW;
+    // phase B (floats, then the raw inputs of the slice in the input type)
     constexpr size_t B_DA = 0, B_DP = B_DA + 64 * LDF, B_XT = B_DP + 64 * LDF, B_XM = B_XT + CW * LDF,
                      B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
-                     B_G = B_QM + CW * LDF, B_Q = B_G + 64 * LDC, B_K = B_Q + 64 * LDC, B_B = B_K + 64 * LDC,
-                     B_DG = B_B + 64 * LDC, B_END = B_DG + 64 * LDC;                // floats
-    constexpr size_t REGION = (A_END * sizeof(Op) > B_END * 4 ? A_END * sizeof(Op) : B_END * 4);
-    __shared__ float sRef[5 * DK], sMid[4 * DK], sGam[DK], sKhK[DK], sPart[256];
+                     B_G = B_QM + CW * LDF, B_DG = B_G + 64 * LDC, B_GAM = B_DG + 64 * LDC, B_KHK = B_GAM + DK,
+                     B_END = B_KHK + DK;                                            // floats
+    constexpr size_t B_BYTES = B_END * 4 + 3 * 64 * CW * sizeof(In);
+    constexpr size_t REGION = (A_END * sizeof(Op) > B_BYTES ? A_END * sizeof(Op) : B_BYTES);
+    __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[256];
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
-    Op *PT = (Op *)smem + A_PT, *TT = (Op *)smem + A_TT, *Kh = (Op *)smem + A_KH, *GT = (Op *)smem + A_GT;
+    Op *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
     Op *OT = (Op *)smem + A_OT, *Xj = (Op *)smem + A_XJ, *DT = (Op *)smem + A_DT;
     Op *OTl = (Op *)smem + A_OTL, *Xjl = (Op *)smem + A_XJL, *DTl = (Op *)smem + A_DTL;
     float *fb = (float *)smem;
     float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
-    float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sqv = fb + B_Q, *skv = fb + B_K, *sbv = fb + B_B;
-    float *sdG = fb + B_DG;
+    float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sdG = fb + B_DG;
+    float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
+    In *sqv = (In *)(fb + B_END), *skv = sqv + 64 * CW, *sbv = skv + 64 * CW;
 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
@@ -449,7 +512,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     const int t0 = sq.t0(i) + 64 * (j - sq.m.chunk0(i));
     const int n = min(64, sq.t1(i) - t0);
     const size_t slot = (size_t)h * sq.max_chunks + j;
-    const uint8_t *blk = ops + slot * L::bytes;
+    const uint8_t *bblk = bops + slot * BL::bytes;
     const Op *Sc = sbuf + slot * DK * DV, *Dl = dbuf + slot * 64 * DV, *Gp = gbuf + slot * DK * DV;
     auto tok_k = [&](int r) { return ((size_t)(t0 + r) * H + h) * DK; };
     auto tok_v = [&](int r) { return ((size_t)(t0 + r) * H + h) * DV; };
@@ -481,13 +544,21 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                 sRef[(R + 1) * DK + c] = fb[(16 * R + 15) * LDL + c];
                 sMid[R * DK + c] = fb[(16 * R + 7) * LDL + c];
             }
-            sKhK[c] = 0.f;
         }
         __syncthreads();
     }
 
     // ---- phase A ----
-    for (int x = t; x < 64 * LDP; x += 256) { PT[x] = (Op)0.f; TT[x] = (Op)0.f; }
+    // A-fragments of this wave's 16 chunk rows of P^T, T^T and Khat
+    frag PTf[NSB], TTf[NSB], KHf[NKB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+        PTf[sb] = *reinterpret_cast<const frag *>(bblk + BL::oPT + ((size_t)(wv * NSB + sb) * 64 + lane) * 16);
+        TTf[sb] = *reinterpret_cast<const frag *>(bblk + BL::oTT + ((size_t)(wv * NSB + sb) * 64 + lane) * 16);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+        KHf[kb] = *reinterpret_cast<const frag *>(bblk + BL::oKH + ((size_t)(wv * NKB + kb) * 64 + lane) * 16);
     if constexpr (VSP > VS) {   // padding columns of the slice tiles stay zero
         for (int x = t; x < DK * (VSP - VS); x += 256) {
             const int c = x / (VSP - VS), jj = VS + x % (VSP - VS);
@@ -502,91 +573,79 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)0.f;
         }
     }
-    __syncthreads();
-    constexpr int NPU = (L::NTRI * 64 + 255) / 256, NKU = L::NCT * NSB * 64 / 256;
-    frag pfs[NPU], tfs[NPU], kfs[NKU];
-#pragma unroll
-    for (int u = 0; u < NPU; ++u) {
-        const int x = min(t + 256 * u, L::NTRI * 64 - 1);
-        pfs[u] = *reinterpret_cast<const frag *>(blk + L::oP + (size_t)x * 16);
-        tfs[u] = *reinterpret_cast<const frag *>(blk + L::oT + (size_t)x * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < NKU; ++u)
-        kfs[u] = *reinterpret_cast<const frag *>(blk + L::oK + (size_t)(t + 256 * u) * 16);
-#pragma unroll
-    for (int u = 0; u < NPU; ++u) {
-        const int x = t + 256 * u;
-        if (x >= L::NTRI * 64) break;
-        const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4;
-        int mt = 0;
-        while (mt < 3 && L::tpos(mt + 1, 0) <= f) ++mt;
-        const int sb = f - L::tpos(mt, 0);
-        const frag pf = pfs[u], tf = tfs[u];
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            const int cc = sb * KB + kofs(g, e), r = 16 * mt + m;
-            PT[cc * LDP + r] = pf[e];
-            TT[cc * LDP + r] = tf[e];
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < NKU; ++u) {
-        const int x = t + 256 * u;
-        const int f = x >> 6, ln = x & 63, m = ln & 15, g = ln >> 4, ct = f / NSB, sb = f % NSB;
-        const frag kf = kfs[u];
-#pragma unroll
-        for (int e = 0; e < NE; ++e) Kh[(sb * KB + kofs(g, e)) * LDK + 16 * ct + m] = kf[e];
-    }
     f4 accA[4], accP[4], F1[CT], F2[CT], F3[CT];
 #pragma unroll
     for (int x = 0; x < 4; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
 #pragma unroll
     for (int x = 0; x < CT; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
     float gam = 0.f;
-    for (int vs = 0; vs < NVS; ++vs) {
+    // value-column slices, software-pipelined: the next slice's loads (G,
+    // S_c, Delta, dO, and v, w for dv and dw) are issued before this slice's
+    // work, into a second set of registers
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    constexpr int NG = (DK * VS / 4 + 255) / 256, ND = (64 * VS / 4 + 255) / 256;
+    struct SR {
+        op4 g[NG], s[NG], d[ND];
+        f4 o[ND];
+        In vv[VT][4], ww[VT][4];
+    };
+    auto sload = [&](SR &R_, int vs) {
         const int j0 = vs * VS;
-        __syncthreads();   // previous slice's readers are done
-        // four consecutive columns per thread and iteration; the loops are
-        // unrolled so that every load is issued before the first store
-        typedef Op op4 __attribute__((ext_vector_type(4)));
-        constexpr int NG = (DK * VS / 4 + 255) / 256, ND = (64 * VS / 4 + 255) / 256;
-        op4 gv4[NG], sv4[NG], dv4[ND];
-        f4 ov4[ND];
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
             const int x = min(t + 256 * u, DK * VS / 4 - 1), c = x / (VS / 4), jj = 4 * (x % (VS / 4));
-            gv4[u] = *reinterpret_cast<const op4 *>(Gp + (size_t)c * DV + j0 + jj);
-            sv4[u] = *reinterpret_cast<const op4 *>(Sc + (size_t)c * DV + j0 + jj);
+            R_.g[u] = *reinterpret_cast<const op4 *>(Gp + (size_t)c * DV + j0 + jj);
+            R_.s[u] = *reinterpret_cast<const op4 *>(Sc + (size_t)c * DV + j0 + jj);
         }
 #pragma unroll
         for (int u = 0; u < ND; ++u) {
             const int x = min(t + 256 * u, 64 * VS / 4 - 1), r = x / (VS / 4), jj = 4 * (x % (VS / 4));
-            dv4[u] = *reinterpret_cast<const op4 *>(Dl + (size_t)r * DV + j0 + jj);
-            ov4[u] = *reinterpret_cast<const f4 *>(dO + tok_v(min(r, n - 1)) + j0 + jj);
+            R_.d[u] = *reinterpret_cast<const op4 *>(Dl + (size_t)r * DV + j0 + jj);
+            R_.o[u] = *reinterpret_cast<const f4 *>(dO + tok_v(min(r, n - 1)) + j0 + jj);
         }
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const size_t o = tok_v(min(16 * wv + 4 * g4 + ii, n - 1)) + j0 + 16 * vt + m16;
+                R_.vv[vt][ii] = v[o];
+                R_.ww[vt][ii] = w[o];
+            }
+    };
+    auto sstore = [&](const SR &R_) {
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
             const int x = t + 256 * u, c = x / (VS / 4), jj = 4 * (x % (VS / 4));
             if (x >= DK * VS / 4) break;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Gr[c * LDV + jj + e] = gv4[u][e];
-                GT[(jj + e) * LDK + c] = gv4[u][e];
-                Sj[c * LDV + jj + e] = sv4[u][e];
+                Gr[c * LDV + jj + e] = R_.g[u][e];
+                GT[(jj + e) * LDK + c] = R_.g[u][e];
+                Sj[c * LDV + jj + e] = R_.s[u][e];
             }
         }
 #pragma unroll
         for (int u = 0; u < ND * 4; ++u) {
             const int x = t + 256 * (u / 4), r = x / (VS / 4), jj = 4 * (x % (VS / 4)) + (u % 4);
             if (x >= 64 * VS / 4) break;
-            Dj[r * LDV + jj] = dv4[u / 4][u % 4];
-            const float of = r < n ? ov4[u / 4][u % 4] : 0.f;
+            Dj[r * LDV + jj] = R_.d[u / 4][u % 4];
+            const float of = r < n ? R_.o[u / 4][u % 4] : 0.f;
             const Op o = (Op)of;
             Oj[r * LDV + jj] = o;
             OT[jj * LDP + r] = o;
             if constexpr (SPLIT) OTl[jj * LDP + r] = (Op)(of - (float)o);
         }
+    };
+    SR ra, rb;
+    sload(ra, 0);
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) {
+        const int j0 = vs * VS;
+        SR &cur = (vs & 1) ? rb : ra;
+        SR &nxt = (vs & 1) ? ra : rb;
+        __syncthreads();   // previous slice's readers are done
+        sstore(cur);
+        if (vs + 1 < NVS) sload(nxt, vs + 1);
         __syncthreads();
         // dDelta row tile wv: P^T dO + Khat G
 #pragma unroll
@@ -594,14 +653,13 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             f4 acc = f4zero();
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                const frag ap = lds_row_frag<Op>(PT + (16 * wv + m16) * LDP, sb * KB, g4);
+                const frag ap = PTf[sb];
                 acc = M::mma(ap, lds_row_frag<Op>(OT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
                 if constexpr (SPLIT) acc = M::mma(ap, lds_row_frag<Op>(OTl + (16 * vt + m16) * LDP, sb * KB, g4), acc);
             }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                acc = M::mma(lds_row_frag<Op>(Kh + (16 * wv + m16) * LDK, kb * KB, g4),
-                             lds_row_frag<Op>(GT + (16 * vt + m16) * LDK, kb * KB, g4), acc);
+                acc = M::mma(KHf[kb], lds_row_frag<Op>(GT + (16 * vt + m16) * LDK, kb * KB, g4), acc);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const Op hi = (Op)acc[ii];
@@ -616,7 +674,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             f4 acc = f4zero();
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                const frag at_ = lds_row_frag<Op>(TT + (16 * wv + m16) * LDP, sb * KB, g4);
+                const frag at_ = TTf[sb];
                 acc = M::mma(at_, lds_row_frag<Op>(DT + (16 * vt + m16) * LDP, sb * KB, g4), acc);
                 if constexpr (SPLIT) acc = M::mma(at_, lds_row_frag<Op>(DTl + (16 * vt + m16) * LDP, sb * KB, g4), acc);
             }
@@ -628,8 +686,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                 if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)(acc[ii] - (float)hi);
                 if (r < n) {
                     const size_t o = tok_v(r) + j0 + jj;
-                    dv_[o] = acc[ii] * Ld<In>::one(w + o);
-                    dw[o] = acc[ii] * Ld<In>::one(v + o);
+                    dv_[o] = acc[ii] * in2f<In>(cur.ww[vt][ii]);
+                    dw[o] = acc[ii] * in2f<In>(cur.vv[vt][ii]);
                 }
             }
         }
@@ -670,26 +728,41 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             sdA[r * LDF + s_] = r > s_ ? -accA[st][ii] : 0.f;
             sdP[r * LDF + s_] = r >= s_ ? accP[st][ii] : 0.f;
         }
-    if (t < DK) sGam[t] = gam * __expf(sRef[4 * DK + t]);
+    if (t < DK) {
+        sGam[t] = gam * __expf(sRef[4 * DK + t]);
+        sKhK[t] = 0.f;
+    }
 
     // ---- phase B, key channels in slices of CW ----
+    // (software-pipelined like phase A: log alpha, q, k, b of the next slice
+    // load while this one is worked on)
+    constexpr int NBU = 64 * CW / 256;
+    struct BR { float l[NBU]; In q[NBU], k[NBU], b[NBU]; };
+    auto bload = [&](BR &R_, int cs) {
+#pragma unroll
+        for (int u = 0; u < NBU; ++u) {
+            const int x = t + 256 * u, r = x / CW, cl = x % CW;
+            const size_t o = tok_k(min(r, n - 1)) + cs * CW + cl;
+            R_.l[u] = la[o];
+            R_.q[u] = q[o];
+            R_.k[u] = k[o];
+            R_.b[u] = b[o];
+        }
+    };
+    BR ba, bb2;
+    bload(ba, 0);
 #pragma unroll
     for (int cs = 0; cs < NCS; ++cs) {
         const int c0 = cs * CW;
+        BR &bc = (cs & 1) ? bb2 : ba;
+        BR &bn = (cs & 1) ? ba : bb2;
         __syncthreads();
-        {
-            float lv[64 * CW / 256];
 #pragma unroll
-            for (int u = 0; u < 64 * CW / 256; ++u) {
-                const int x = t + 256 * u, r = x / CW, cl = x % CW;
-                lv[u] = la[tok_k(min(r, n - 1)) + c0 + cl];
-            }
-#pragma unroll
-            for (int u = 0; u < 64 * CW / 256; ++u) {
-                const int x = t + 256 * u, r = x / CW, cl = x % CW;
-                sg[r * LDC + cl] = r < n ? lv[u] : 0.f;
-            }
+        for (int u = 0; u < NBU; ++u) {
+            const int x = t + 256 * u, r = x / CW, cl = x % CW;
+            sg[r * LDC + cl] = r < n ? bc.l[u] : 0.f;
         }
+        if (cs + 1 < NCS) bload(bn, cs + 1);
         __syncthreads();
         col_scan64<CW, false>(sg, LDC, sPart, t);
         static_assert((64 * CW) % 256 == 0, "whole rounds of the workgroup");
@@ -698,10 +771,9 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             const int x = t + 256 * u;
             const int r = x / CW, cl = x % CW, c = c0 + cl, R = r >> 4;
             const bool ok = r < n;
-            const size_t o = tok_k(min(r, n - 1)) + c;
-            const float kv = Ld<In>::one(k + o) * (ok ? 1.f : 0.f);
-            const float qv = Ld<In>::one(q + o) * (ok ? 1.f : 0.f);
-            const float bv = Ld<In>::one(b + o) * (ok ? 1.f : 0.f);
+            const In zero_ = (In)0;
+            const In kr_ = ok ? bc.k[u] : zero_, qr_ = ok ? bc.q[u] : zero_, br_ = ok ? bc.b[u] : zero_;
+            const float kv = in2f<In>(kr_), qv = in2f<In>(qr_), bv = in2f<In>(br_);
             const float gv = sg[r * LDC + cl];
             const float e1 = __expf(sRef[(R + 1) * DK + c] - gv), em = __expf(sMid[R * DK + c] - gv);
             const float e2 = __expf(gv - sRef[R * DK + c]), en = __expf(gv - sMid[R * DK + c]);
@@ -711,9 +783,9 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             BmT[cl * LDF + r] = bv * kv * en;
             QtT[cl * LDF + r] = qv * e2;
             QmT[cl * LDF + r] = qv * en;
-            sqv[r * LDC + cl] = qv;
-            skv[r * LDC + cl] = kv;
-            sbv[r * LDC + cl] = bv;
+            sqv[r * CW + cl] = qr_;
+            skv[r * CW + cl] = kr_;
+            sbv[r * CW + cl] = br_;
         }
         __syncthreads();
         const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
@@ -770,7 +842,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * R + 4 * g4 + ii;
                 const float gv = sg[r * LDC + cl], eg = __expf(gv), egn = __expf(gn - gv);
-                const float qv = sqv[r * LDC + cl], kv = skv[r * LDC + cl], bv = sbv[r * LDC + cl];
+                const float qv = in2f<In>(sqv[r * CW + cl]), kv = in2f<In>(skv[r * CW + cl]), bv = in2f<In>(sbv[r * CW + cl]);
                 const float dqv = F1[ctg][ii] * eg + Y1[ii];
                 const float dEe = -F2[ctg][ii] * eg + Y2[ii];
                 const float dkm = Z1[ii] + Z2[ii];
@@ -863,7 +935,8 @@ static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st
         prof_before("gdn2_chunk_grad", st);
         hipLaunchKernelGGL((chunk_grad_kernel<In, Op, DK, DV>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
                            dim3(256), 0, st, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
-                           (const In *)a.b, (const In *)a.w, a.dO, sq, a.H, ops, (const Op *)(ws + bp.off_states),
+                           (const In *)a.b, (const In *)a.w, a.dO, sq, a.H, (const uint8_t *)bops,
+                           (const Op *)(ws + bp.off_states),
                            (const Op *)(ws + bp.off_delta), (const Op *)gbuf, a.dq, a.dk_, a.dv_, a.dlog_alpha, a.db,
                            a.dw);
         prof_after(st);
