@@ -280,16 +280,14 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
         auto step = [&](int k, F &cur, F &pre, int par) {
             const int c = nch - 1 - k;
             if constexpr (!RING) fload(cur, bblk(k));
-            Op *gp = gbuf + (slot0 + c) * DK * DV;
+            Op *gp = gbuf + (slot0 + c) * DK * DV;   // accumulator-tile order, as the forward's S_c
 #pragma unroll
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {
                     const int ct = wv * TPW + u;
                     if (NCT % 4 != 0 && ct >= NCT) continue;
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        gp[(size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)Gr[q][u][ii];
+                    tile_store<Op>(gp + ((size_t)ct * (DV / 16) + NC * js + q) * 256, lane, Gr[q][u]);
                 }
             __syncthreads();   // G and dO of this step in LDS buffer `par`
 #pragma unroll
@@ -582,8 +580,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     // value-column slices, software-pipelined: the next slice's loads (G,
     // S_c, Delta, dO, and v, w for dv and dw) are issued before this slice's
     // work, into a second set of registers
+    // G, S_c and Delta arrive in accumulator-tile order (tile (rt, ct) at
+    // (rt * DV/16 + ct) * 256; lane l = n + 16g holds rows 4g..4g+3 of
+    // column n): one 4-element load per lane and tile
     typedef Op op4 __attribute__((ext_vector_type(4)));
     constexpr int NG = (DK * VS / 4 + 255) / 256, ND = (64 * VS / 4 + 255) / 256;
+    static_assert((DK * VS / 4) % 64 == 0 && (64 * VS / 4) % 64 == 0, "whole tiles");
+    // x = tile * 64 + lane over the slice's tiles (row tile major)
+    auto tile_at = [&](int x, int &rt, int &ctl, int &ln) { ln = x & 63; rt = (x >> 6) / VT; ctl = (x >> 6) % VT; };
     struct SR {
         op4 g[NG], s[NG], d[ND];
         f4 o[ND];
@@ -593,14 +597,18 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         const int j0 = vs * VS;
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
-            const int x = min(t + 256 * u, DK * VS / 4 - 1), c = x / (VS / 4), jj = 4 * (x % (VS / 4));
-            R_.g[u] = *reinterpret_cast<const op4 *>(Gp + (size_t)c * DV + j0 + jj);
-            R_.s[u] = *reinterpret_cast<const op4 *>(Sc + (size_t)c * DV + j0 + jj);
+            int rt, ctl, ln;
+            tile_at(min(t + 256 * u, DK * VS / 4 - 1), rt, ctl, ln);
+            const size_t o = ((size_t)rt * (DV / 16) + j0 / 16 + ctl) * 256 + ln * 4;
+            R_.g[u] = *reinterpret_cast<const op4 *>(Gp + o);
+            R_.s[u] = *reinterpret_cast<const op4 *>(Sc + o);
         }
 #pragma unroll
         for (int u = 0; u < ND; ++u) {
+            int rt, ctl, ln;
+            tile_at(min(t + 256 * u, 64 * VS / 4 - 1), rt, ctl, ln);
+            R_.d[u] = *reinterpret_cast<const op4 *>(Dl + ((size_t)rt * (DV / 16) + j0 / 16 + ctl) * 256 + ln * 4);
             const int x = min(t + 256 * u, 64 * VS / 4 - 1), r = x / (VS / 4), jj = 4 * (x % (VS / 4));
-            R_.d[u] = *reinterpret_cast<const op4 *>(Dl + (size_t)r * DV + j0 + jj);
             R_.o[u] = *reinterpret_cast<const f4 *>(dO + tok_v(min(r, n - 1)) + j0 + jj);
         }
 #pragma unroll
@@ -615,20 +623,32 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     auto sstore = [&](const SR &R_) {
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
-            const int x = t + 256 * u, c = x / (VS / 4), jj = 4 * (x % (VS / 4));
+            const int x = t + 256 * u;
             if (x >= DK * VS / 4) break;
+            int rt, ctl, ln;
+            tile_at(x, rt, ctl, ln);
+            const int jj = 16 * ctl + (ln & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Gr[c * LDV + jj + e] = R_.g[u][e];
-                GT[(jj + e) * LDK + c] = R_.g[u][e];
-                Sj[c * LDV + jj + e] = R_.s[u][e];
+                const int c = 16 * rt + 4 * (ln >> 4) + e;
+                Gr[c * LDV + jj] = R_.g[u][e];
+                GT[jj * LDK + c] = R_.g[u][e];
+                Sj[c * LDV + jj] = R_.s[u][e];
             }
+        }
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+            const int x = t + 256 * u;
+            if (x >= 64 * VS / 4) break;
+            int rt, ctl, ln;
+            tile_at(x, rt, ctl, ln);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Dj[(16 * rt + 4 * (ln >> 4) + e) * LDV + 16 * ctl + (ln & 15)] = R_.d[u][e];
         }
 #pragma unroll
         for (int u = 0; u < ND * 4; ++u) {
             const int x = t + 256 * (u / 4), r = x / (VS / 4), jj = 4 * (x % (VS / 4)) + (u % 4);
             if (x >= 64 * VS / 4) break;
-            Dj[r * LDV + jj] = R_.d[u / 4][u % 4];
             const float of = r < n ? R_.o[u / 4][u % 4] : 0.f;
             const Op o = (Op)of;
             Oj[r * LDV + jj] = o;

@@ -850,11 +850,23 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
 // SAVE (for the backward): no output; the state waves store each chunk's
 // start state S_c [dk][dv] and Delta [64][dv] (operand type, the values the
 // step used) at (head, chunk) slots of two buffers, head-major like the
-// operand blocks.
+// operand blocks, in accumulator-tile order: tile (row tile rt, column tile
+// ct) at (rt * dv/16 + ct) * 256, lane l = n + 16g holding rows 4g..4g+3 of
+// column n (one 8- or 16-byte store per lane and tile).
 struct SaveOut {
-    void *S;   // [H * max_chunks][dk][dv]
-    void *D;   // [H * max_chunks][64][dv]
+    void *S;   // [H * max_chunks][dk/16][dv/16][64][4]
+    void *D;   // [H * max_chunks][4][dv/16][64][4]
 };
+
+template <typename Op>
+__device__ __forceinline__ void tile_store(Op *dst, int lane, const f4 &x)
+{
+    typedef Op op4 __attribute__((ext_vector_type(4)));
+    op4 y;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) y[ii] = (Op)x[ii];
+    *reinterpret_cast<op4 *>(dst + lane * 4) = y;
+}
 
 template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
@@ -949,9 +961,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     for (int u = 0; u < TPW; ++u) {
                         const int ct = wv * TPW + u;
                         if (NCT % 4 != 0 && ct >= NCT) continue;
-#pragma unroll
-                        for (int ii = 0; ii < 4; ++ii)
-                            sp[(size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)Sr[q][u][ii];
+                        tile_store<Op>(sp + ((size_t)ct * (DV / 16) + NC * js + q) * 256, lane, Sr[q][u]);
                     }
             }
             __syncthreads();   // (1) state tiles and U ready
@@ -980,9 +990,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
 #pragma unroll
                 for (int q = 0; q < NC; ++q)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        dp[(size_t)(16 * wv + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = (Op)(acc[q][ii] + accw[q][ii]);
+                    tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, acc[q] + accw[q]);
             }
             pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready

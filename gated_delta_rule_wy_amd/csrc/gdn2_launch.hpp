@@ -87,9 +87,9 @@ struct ChunkBwdArgs {
 
 // Backward workspace: the forward plan's regions, then (256-byte aligned)
 //   backward operand blocks   [H * max_chunks] x bblock_bytes
-//   chunk start states S_c    [H * max_chunks][dk][dv]  operand type
-//   chunk Delta               [H * max_chunks][64][dv]  operand type
-//   chunk end gradients G     [H * max_chunks][dk][dv]  operand type
+//   chunk start states S_c    [H * max_chunks][dk][dv]  operand type, 16x16 accumulator-tile order
+//   chunk Delta               [H * max_chunks][64][dv]  operand type, same order
+//   chunk end gradients G     [H * max_chunks][dk][dv]  operand type, same order
 struct BwdPlan {
     ChunkPlan fwd;
     size_t bblock_bytes, state_bytes, delta_bytes;   // per (chunk, head)
