@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
     constexpr int NVS = DV / VS, VT = VS / 16, VKB = VS / KB > 0 ? VS / KB : 1;
     constexpr int CT = DK / 16;
-    constexpr int CW = 16;                                // key channels per phase-B slice
+    constexpr int CW = DK < 32 ? DK : 32;                 // key channels per phase-B slice
     constexpr int NCS = DK / CW, CWT = CW / 16;
     static_assert(VS % KB == 0 || VS < KB, "slice width");
     // LDS: persistent tables, then phase A and phase B regions over the same bytes
