@@ -7,10 +7,12 @@ N(0, 0.02)). One step = one gdn2_chunk_fwd call over the whole batch (chunk
 prep + sequential state pass). The decode workload (256 sequences x 16 heads,
 fp32 state resident, 1000 single-token steps with fresh inputs) is measured in
 the same run and reported under "decode". Also reported: the same prefill with
-scalar gates ("gate_forms": the KDA and Gated DeltaNet layouts) and on the
-layer's raw inputs with the short convolution, unit norm and sigmoids fused
-in ("prologue_form", for prefill and decode), and the backward of the same
-prefill ("backward": all input gradients from seeded dO and dS_T).
+scalar gates ("gate_forms": the KDA and Gated DeltaNet layouts), with chunks
+of 32, 64 and 128 tokens ("chunk_sizes": latency, throughput and peak device
+memory of each), on the layer's raw inputs with the short convolution, unit
+norm and sigmoids fused in ("prologue_form", for prefill and decode), and the
+backward of the same prefill ("backward": all input gradients from seeded dO
+and dS_T).
 
 Prints ONE JSON line. Inputs are synthetic and seeded (gdn2_inputs), resident
 in HBM before timing starts. Per-kernel durations come from HIP events that
@@ -155,6 +157,34 @@ def bench_prefill(args, torch, gdn2, gi):
                         'kernels_ms': {kk: round(vv[1] / vv[0], 5) for kk, vv in fprof.items() if vv[0]}}
         log(f'[bench] prefill, {fname} gates: {fms:.3f} ms/step')
     res['gate_forms'] = forms
+
+    # Chunk sizes (the C = 32 / 64 / 128 trade-off): latency, throughput and
+    # peak device memory of the same workload, measured back to back.
+    sizes = {}
+    for C in (() if args.no_chunk_sizes else (64, 32, 128)):
+        need = gdn2.workspace_bytes(B, T, B, H, dk, dv, bf, False, chunk=C)
+        wsc = torch.empty(need, dtype=torch.uint8, device=dev)
+        crun = lambda: gdn2.chunk_fwd(q, k, v, la, b, w, S0, out=o1, final_state=ST1, workspace=wsc, chunk=C)
+        for _ in range(args.warmup):
+            crun()
+        torch.cuda.synchronize()
+        gdn2.profile_begin(args.steps)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            crun()
+        torch.cuda.synchronize()
+        cms = (time.perf_counter() - t0) * 1e3 / args.steps
+        cprof = gdn2.profile_end()
+        resident = sum(x.numel() * x.element_size() for x in (q, k, v, b, w, la, S0, o1, ST1))
+        sizes[str(C)] = {'ms_per_step': round(cms, 4), 'value': B * T / (cms * 1e-3), 'unit': 'tokens/s',
+                         'step_roofline_frac': round(step_bytes / (cms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         'workspace_bytes': int(need), 'peak_device_bytes': int(resident + need),
+                         'kernels_ms': {kk: round(vv[1] / vv[0], 5) for kk, vv in cprof.items() if vv[0]}}
+        log(f'[bench] prefill, chunk {C}: {cms:.3f} ms/step; kernels: ' +
+            ', '.join(f'{kk} {vv[1] / max(1, vv[0]):.4f} ms' for kk, vv in cprof.items()) +
+            f'; workspace {need / 2**20:.0f} MiB')
+        del wsc
+    res['chunk_sizes'] = sizes
     if not args.no_prologue:
         res['prologue_form'] = bench_prefill_prologue(args, torch, gdn2, gi, ws)
     if not args.no_backward:
@@ -381,6 +411,8 @@ def main():
                     help='skip the fused-prologue (raw-input) timings')
     ap.add_argument('--no-gate-forms', action='store_true',
                     help='skip the scalar-gate (KDA, Gated DeltaNet) prefill timings')
+    ap.add_argument('--no-chunk-sizes', action='store_true',
+                    help='skip the chunk-size (32 / 64 / 128 tokens) prefill timings')
     ap.add_argument('--copy-calibration-mib', type=int, default=0,
                     help='only run a plain device copy of this many MiB (x3), to calibrate '
                          'the FETCH_SIZE / WRITE_SIZE counters; prints nothing else')
@@ -421,6 +453,7 @@ def main():
     out['step_roofline'] = pre['step_roofline']
     out['kernels_ms'] = pre['kernels_ms']
     out['gate_forms'] = pre['gate_forms']
+    out['chunk_sizes'] = pre['chunk_sizes']
     if 'prologue_form' in pre:
         out['prologue_form'] = pre['prologue_form']
     if 'backward' in pre:

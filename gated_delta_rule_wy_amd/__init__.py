@@ -29,6 +29,7 @@ CHUNK = 64
 
 EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
            'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_gates',
+           'gdn2_chunk_fwd_sized_workspace_bytes', 'gdn2_chunk_fwd_sized',
            'gdn2_decode_step', 'gdn2_decode_step_gates',
            'gdn2_chunk_fwd_prologue', 'gdn2_decode_step_prologue',
            'gdn2_chunk_bwd_workspace_bytes', 'gdn2_chunk_bwd',
@@ -65,6 +66,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn2_chunk_fwd.restype = i
     lib.gdn2_chunk_fwd_gates.argtypes = [vp] * 6 + [i] + [vp] * 4 + [i] * 8 + [vp, sz]
     lib.gdn2_chunk_fwd_gates.restype = i
+    lib.gdn2_chunk_fwd_sized_workspace_bytes.argtypes = [i] * 9
+    lib.gdn2_chunk_fwd_sized_workspace_bytes.restype = sz
+    lib.gdn2_chunk_fwd_sized.argtypes = [vp] * 10 + [i] * 9 + [vp, sz]
+    lib.gdn2_chunk_fwd_sized.restype = i
     lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 6
     lib.gdn2_decode_step.restype = i
     lib.gdn2_decode_step_gates.argtypes = [vp] * 6 + [i] + [vp] * 2 + [i] * 6
@@ -129,9 +134,9 @@ def set_stream(stream: Optional[torch.cuda.Stream] = None) -> None:
 
 
 def workspace_bytes(B: int, T: int, N: int, H: int, dk: int, dv: int, dtype: torch.dtype,
-                    varlen: bool) -> int:
+                    varlen: bool, chunk: int = CHUNK) -> int:
     code = GDN2_BF16 if dtype == torch.bfloat16 else GDN2_F32
-    return int(_lib.gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen)))
+    return int(_lib.gdn2_chunk_fwd_sized_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen), int(chunk)))
 
 
 def profile_begin(max_calls: int) -> None:
@@ -176,13 +181,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
               b: torch.Tensor, w: torch.Tensor, S0: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None,
+              chunk: int = CHUNK) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise prefill. q, k, b: [B, T, H, dk]; v, w: [B, T, H, dv] (bf16 or
     fp32); log_alpha: [B, T, H, dk] fp32. With ``cu_seqlens`` (int32 [N+1] on
     the device) B must be 1 and the sequences are packed along T. S0: [N, H,
     dk, dv] fp32 or None (zeros). Returns (o [B, T, H, dv] fp32, S_T [N, H, dk,
     dv] fp32 or None). b, w and log_alpha may instead be [B, T, H], one gate
-    per token-head (KDA: b = w = beta; Gated DeltaNet: also a scalar decay)."""
+    per token-head (KDA: b = w = beta; Gated DeltaNet: also a scalar decay).
+    ``chunk``: tokens per chunk, 64, or 32 / 128 (gdn2_chunk_fwd_sized,
+    per-channel gates only)."""
     if q.dim() != 4:
         raise ValueError('q must be [B, T, H, dk]')
     B, T, H, dk = q.shape
@@ -213,18 +221,27 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     elif output_final_state:
         ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     varlen = cu_seqlens is not None
-    need = _lib.gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen))
+    if chunk != CHUNK and gates != GDN2_GATES_PER_CHANNEL:
+        raise ValueError(f'chunk = {chunk} takes per-channel gates only')
+    need = _lib.gdn2_chunk_fwd_sized_workspace_bytes(B, T, N, H, dk, dv, code, int(varlen), int(chunk))
     if need == 0:
-        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, 'gdn2_chunk_fwd_workspace_bytes')
+        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, 'gdn2_chunk_fwd_sized_workspace_bytes')
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     set_stream()
-    st = _lib.gdn2_chunk_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
-                                   _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
-                                   B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace),
-                                   workspace.numel() * workspace.element_size())
+    wsb = workspace.numel() * workspace.element_size()
+    if chunk == CHUNK:
+        st = _lib.gdn2_chunk_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
+                                       _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
+                                       B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace), wsb)
+        where = 'gdn2_chunk_fwd_gates'
+    else:
+        st = _lib.gdn2_chunk_fwd_sized(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                       _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
+                                       B, T, N, H, dk, dv, code, GDN2_F32, int(chunk), _ptr(workspace), wsb)
+        where = 'gdn2_chunk_fwd_sized'
     if st != GDN2_OK:
-        raise Gdn2Error(st, 'gdn2_chunk_fwd_gates')
+        raise Gdn2Error(st, where)
     return out, ST
 
 

@@ -151,8 +151,9 @@ const char *gdn2_status_string(int status)
 }
 
 static int chunk_check(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype, int varlen,
-                       gdn2::ChunkPlan *plan)
+                       gdn2::ChunkPlan *plan, int chunk = 64)
 {
+    if (chunk != 32 && chunk != 64 && chunk != 128) return GDN2_ERR_INVALID;
     if (B <= 0 || T < 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
     if (in_dtype != GDN2_F32 && in_dtype != GDN2_BF16) return GDN2_ERR_INVALID;
     if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID;
@@ -160,9 +161,17 @@ static int chunk_check(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in
     if ((long long)B * T > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
     if (H > 65535) return GDN2_ERR_UNSUPPORTED;   // grid y dimension
-    if (!gdn2::chunk_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, plan))
+    if (!gdn2::chunk_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, plan, chunk))
         return GDN2_ERR_UNSUPPORTED;
     return GDN2_OK;
+}
+
+size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype,
+                                            int varlen, int chunk)
+{
+    gdn2::ChunkPlan plan;
+    if (chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan, chunk) != GDN2_OK) return 0;
+    return plan.total_bytes > 0 ? plan.total_bytes : 256;
 }
 
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
@@ -209,12 +218,12 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
                           const void *b, const void *w, int gates, const gdn2_short_conv *conv, const float *S0,
                           void *o, float *ST, const int32_t *cu_seqlens, int B, int T, int N, int H, int dk,
                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
-                          size_t workspace_bytes)
+                          size_t workspace_bytes, int chunk = 64)
 {
     if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     gdn2::ChunkPlan plan;
     const int varlen = cu_seqlens != nullptr;
-    int st = chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan);
+    int st = chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan, chunk);
     if (st != GDN2_OK) return st;
     if (out_dtype != GDN2_F32) return out_dtype == GDN2_BF16 ? GDN2_ERR_UNSUPPORTED : GDN2_ERR_INVALID;
     const bool have_tokens = (long long)B * T > 0;
@@ -250,6 +259,15 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
 {
     return chunk_fwd_impl(q, k, v, log_alpha, b, w, gates, nullptr, S0, o, ST, cu_seqlens, B, T, N, H, dk, dv,
                           in_dtype, out_dtype, workspace, workspace_bytes);
+}
+
+int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                         const void *w, const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B,
+                         int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                         int chunk, void *workspace, size_t workspace_bytes)
+{
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, nullptr, S0, o, ST, cu_seqlens, B, T,
+                          N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes, chunk);
 }
 
 int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,

@@ -3,6 +3,7 @@
 // chunk_impl.hpp; each (input type, d_k) is instantiated in a translation
 // unit of its own (chunk_<type>_d<d_k>.hip) so they compile in parallel.
 #include "chunk_bwd_impl.hpp"
+#include "chunk_cs_impl.hpp"
 
 namespace gdn2 {
 
@@ -14,9 +15,24 @@ extern template hipError_t dispatch_dv<float, float, 32>(const ChunkArgs &, cons
 extern template hipError_t dispatch_dv<float, float, 64>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
 extern template hipError_t dispatch_dv<float, float, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
 
-// chunk offsets for packed batches: co[i] = sum_{i'<i} ceil(len_i'/64), capped
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 32, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 32, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 64, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 64, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 128, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<uint16_t, _Float16, 128, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 16, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 16, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 32, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 32, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 64, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 64, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 128, 32>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+extern template hipError_t dispatch_dv_cs<float, float, 128, 128>(const ChunkArgs &, const ChunkPlan &, hipStream_t);
+
+// chunk offsets for packed batches: co[i] = sum_{i'<i} ceil(len_i' / 2^lc), capped
 __global__ __launch_bounds__(1024) void chunk_plan_kernel(const int32_t *__restrict__ cu, int N, int T,
-                                                          int max_chunks, int32_t *__restrict__ co)
+                                                          int max_chunks, int lc, int32_t *__restrict__ co)
 {
     __shared__ int part[1024];
     const int t = threadIdx.x;
@@ -25,7 +41,7 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(const int32_t *__restr
     int sum = 0;
     for (int i = i0; i < i1; ++i) {
         const int a = clampi(cu[i], 0, T), b = clampi(cu[i + 1], a, T);
-        sum += (b - a + 63) >> 6;
+        sum += (b - a + (1 << lc) - 1) >> lc;
     }
     part[t] = sum;
     __syncthreads();
@@ -39,19 +55,30 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(const int32_t *__restr
     for (int i = i0; i < i1; ++i) {
         co[i] = min(run, max_chunks);
         const int a = clampi(cu[i], 0, T), b = clampi(cu[i + 1], a, T);
-        run += (b - a + 63) >> 6;
+        run += (b - a + (1 << lc) - 1) >> lc;
     }
     if (t == 1023) co[N] = min(part[1023], max_chunks);
 }
 
 // ---------------------------------------------------------------------------
-static size_t blk_bytes(int dk, bool bf16)
+// operand block bytes per (chunk, head); 0 where the prep does not support the chunk size
+template <typename Op, int DK> static size_t blk_bytes_t(int chunk)
+{
+    switch (chunk) {
+    case 32: return PrepCS<Op, DK, 32>::fits ? Blk<Op, DK, 32>::bytes : 0;
+    case 64: return Blk<Op, DK, 64>::bytes;
+    case 128: return PrepCS<Op, DK, 128>::fits ? Blk<Op, DK, 128>::bytes : 0;
+    }
+    return 0;
+}
+
+static size_t blk_bytes(int dk, bool bf16, int chunk)
 {
     switch (dk) {
-    case 16: return bf16 ? 0 : Blk<float, 16>::bytes;
-    case 32: return bf16 ? Blk<_Float16, 32>::bytes : Blk<float, 32>::bytes;
-    case 64: return bf16 ? Blk<_Float16, 64>::bytes : Blk<float, 64>::bytes;
-    case 128: return bf16 ? Blk<_Float16, 128>::bytes : Blk<float, 128>::bytes;
+    case 16: return bf16 ? 0 : blk_bytes_t<float, 16>(chunk);
+    case 32: return bf16 ? blk_bytes_t<_Float16, 32>(chunk) : blk_bytes_t<float, 32>(chunk);
+    case 64: return bf16 ? blk_bytes_t<_Float16, 64>(chunk) : blk_bytes_t<float, 64>(chunk);
+    case 128: return bf16 ? blk_bytes_t<_Float16, 128>(chunk) : blk_bytes_t<float, 128>(chunk);
     }
     return 0;
 }
@@ -89,7 +116,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, const BwdPlan &p, hipStream_t
     if (a.cu_seqlens) {
         prof_before("gdn2_chunk_plan", st);
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.N, a.T,
-                           p.fwd.max_chunks, (int32_t *)a.workspace);
+                           p.fwd.max_chunks, 6, (int32_t *)a.workspace);
         prof_after(st);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -111,15 +138,16 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, const BwdPlan &p, hipStream_t
     return hipErrorInvalidValue;
 }
 
-bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p)
+bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p, int chunk)
 {
     if (dv != 16 && dv != 32 && dv != 64 && dv != 128) return false;
-    const size_t bb = blk_bytes(dk, bf16);
+    const size_t bb = blk_bytes(dk, bf16, chunk);
     if (!bb) return false;
-    const long long per = ((long long)T + 63) / 64;
+    const long long per = ((long long)T + chunk - 1) / chunk;
     const long long mc = varlen ? per + N : per * B;
     if (mc * H > 0x7fffffffLL) return false;
     const long long chains = (long long)(varlen ? N : B) * H;
+    p->chunk = chunk;
     p->max_chunks = (int)mc;
     p->plan_bytes = varlen ? ((size_t)(N + 1) * 4 + 255) / 256 * 256 : 0;
     p->prog_bytes = ((size_t)chains * 4 + 255) / 256 * 256;
@@ -213,10 +241,29 @@ static hipError_t launch_chunk_fwd_kernels(const ChunkArgs &a, const ChunkPlan &
     if (a.cu_seqlens) {
         prof_before("gdn2_chunk_plan", st);
         hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.N, a.T,
-                           p.max_chunks, (int32_t *)a.workspace);
+                           p.max_chunks, __builtin_ctz((unsigned)p.chunk), (int32_t *)a.workspace);
         prof_after(st);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
+    }
+    if (p.chunk != 64) {
+        // chunk-size variants: per-channel gates, no prologue (checked by the caller)
+        const bool c32 = p.chunk == 32;
+        if (a.bf16) {
+            switch (a.dk) {
+            case 32: return c32 ? dispatch_dv_cs<uint16_t, _Float16, 32, 32>(a, p, st) : dispatch_dv_cs<uint16_t, _Float16, 32, 128>(a, p, st);
+            case 64: return c32 ? dispatch_dv_cs<uint16_t, _Float16, 64, 32>(a, p, st) : dispatch_dv_cs<uint16_t, _Float16, 64, 128>(a, p, st);
+            case 128: return c32 ? dispatch_dv_cs<uint16_t, _Float16, 128, 32>(a, p, st) : dispatch_dv_cs<uint16_t, _Float16, 128, 128>(a, p, st);
+            }
+        } else {
+            switch (a.dk) {
+            case 16: return c32 ? dispatch_dv_cs<float, float, 16, 32>(a, p, st) : dispatch_dv_cs<float, float, 16, 128>(a, p, st);
+            case 32: return c32 ? dispatch_dv_cs<float, float, 32, 32>(a, p, st) : dispatch_dv_cs<float, float, 32, 128>(a, p, st);
+            case 64: return c32 ? dispatch_dv_cs<float, float, 64, 32>(a, p, st) : dispatch_dv_cs<float, float, 64, 128>(a, p, st);
+            case 128: return c32 ? dispatch_dv_cs<float, float, 128, 32>(a, p, st) : dispatch_dv_cs<float, float, 128, 128>(a, p, st);
+            }
+        }
+        return hipErrorInvalidValue;
     }
     if (a.bf16) {
         switch (a.dk) {

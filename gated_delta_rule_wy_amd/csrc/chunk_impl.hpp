@@ -48,30 +48,34 @@
 
 namespace gdn2 {
 
-// Operand block written by chunk_prep for one (chunk, head); every fragment
-// is 64 lanes x 16 bytes in the lane order the consumer loads it.
-template <typename Op, int DK> struct Blk {
+// Operand block written by the prep for one (chunk, head) of CS tokens;
+// every fragment is 64 lanes x 16 bytes in the lane order the consumer loads it.
+template <typename Op, int DK, int CS = 64> struct Blk {
     using M = Mma<Op>;
     static constexpr int KB = M::KB, NE = M::NE;
+    static constexpr int NRB = CS / 16;   // 16-row tiles over chunk rows
     static constexpr int NKB = DK / KB;   // k-blocks over key channels
-    static constexpr int NSB = 64 / KB;   // k-blocks over chunk rows
+    static constexpr int NSB = CS / KB;   // k-blocks over chunk rows
     static constexpr int NCT = DK / 16;   // 16-row tiles over key channels
     static constexpr size_t FRAG = 64 * 16;
-    static constexpr size_t oW = 0;                          // -W   [4][NKB] frags
-    static constexpr size_t oQ = oW + 4 * NKB * FRAG;        // Q+   [4][NKB]
-    static constexpr size_t oK = oQ + 4 * NKB * FRAG;        // Khat^T [NCT][NSB]
+    static constexpr size_t oW = 0;                            // -W   [NRB][NKB] frags
+    static constexpr size_t oQ = oW + NRB * NKB * FRAG;        // Q+   [NRB][NKB]
+    static constexpr size_t oK = oQ + NRB * NKB * FRAG;        // Khat^T [NCT][NSB]
     // P and T are lower triangular: only the k-blocks sb <= sbmax(mt) of row
     // tile mt are stored, in row-tile order (tpos)
     static constexpr __host__ __device__ int sbmax(int mt) { return (16 * mt + 15) / KB; }
-    // closed form (a loop over a runtime mt would stay a loop in the pass)
+    // closed form (a loop over a runtime mt would stay a loop in the pass):
+    // row tile m holds m / 2 + 1 stored k-blocks of 32 rows, m + 1 of 16
     static_assert(KB == 32 || KB == 16, "k-block of 16 or 32 rows");
+    static_assert(CS == 32 || CS == 64 || CS == 128, "chunk of 32, 64 or 128 tokens");
     static constexpr __host__ __device__ int tpos(int mt, int sb) {
-        return (KB == 32 ? (mt < 2 ? mt : 2 * mt - 2) : mt * (mt + 1) / 2) + sb;
+        if (CS == 64) return (KB == 32 ? (mt < 2 ? mt : 2 * mt - 2) : mt * (mt + 1) / 2) + sb;
+        return (KB == 32 ? mt + (mt - 1) * (mt - 1) / 4 : mt * (mt + 1) / 2) + sb;
     }
-    static constexpr int NTRI = tpos(3, sbmax(3)) + 1;   // stored fragments of P (and of T)
-    static constexpr size_t oP = oK + NCT * NSB * FRAG;      // P    [NTRI]
-    static constexpr size_t oT = oP + NTRI * FRAG;           // T    [NTRI]
-    static constexpr size_t oG = oT + NTRI * FRAG;           // gamma float[DK]
+    static constexpr int NTRI = tpos(NRB - 1, sbmax(NRB - 1)) + 1;   // stored fragments of P (and of T)
+    static constexpr size_t oP = oK + NCT * NSB * FRAG;        // P    [NTRI]
+    static constexpr size_t oT = oP + NTRI * FRAG;             // T    [NTRI]
+    static constexpr size_t oG = oT + NTRI * FRAG;             // gamma float[DK]
     static constexpr size_t bytes = (oG + DK * 4 + 255) / 256 * 256;
 };
 
@@ -669,23 +673,57 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 // Workgroups are numbered so that the slices of one chain land on the same
 // XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), where they
 // share that XCD's L2 for the chain's operand blocks.
-template <typename Op, int DK> struct StateFrags {
+// Row tiles of a chunk handled by wave w (0..3) of either role: one (w) for
+// 64-token chunks, two ({w, 7 - w}, which evens out the triangular T and P
+// fragments between waves) for 128, and for 32 (two row tiles) waves 0 and 1
+// take one each while waves 2 and 3 have none.
+template <int CS> struct RowTiles {
+    static constexpr int NRB = CS / 16;
+    static constexpr int RPW = NRB >= 4 ? NRB / 4 : 1;
+    static_assert(RPW <= 2, "at most two row tiles per wave");
+    static __device__ __forceinline__ int rt(int w, int j) { return RPW == 1 ? w : ((j & 1) ? 4 * j + 3 - w : 4 * j + w); }
+    static constexpr bool ALL = NRB >= 4;   // every wave has row tiles
+    static __device__ __forceinline__ bool active(int w) { return ALL || w < NRB; }
+};
+
+template <typename Op, int DK, int CS = 64> struct StateFrags {
     using M = Mma<Op>;
-    using L = Blk<Op, DK>;
+    using L = Blk<Op, DK, CS>;
+    using RT = RowTiles<CS>;
     using frag = typename M::frag;
-    static constexpr int TPW = (L::NCT + 3) / 4;
-    frag nW[L::NKB], Ti[L::NSB], Kh[TPW][L::NSB];
+    static constexpr int TPW = (L::NCT + 3) / 4, RPW = RT::RPW;
+    frag nW[RPW][L::NKB], Ti[RPW][L::NSB], Kh[TPW][L::NSB];
     f4 gam[TPW];
+    // T k-blocks past a row tile's diagonal are never loaded, and the
+    // products that skip them sit under a runtime condition, which the
+    // compiler may leave without a branch around it (a matrix instruction
+    // then runs whatever the execution mask): they must read as zero. (The
+    // 64-token kernel keeps its loads inside the skipped region, which keeps
+    // the branch.)
+    __device__ __forceinline__ void zero_tri() {
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+            for (int sb = 0; sb < L::NSB; ++sb)
+#pragma unroll
+                for (int e = 0; e < M::NE; ++e) Ti[j][sb][e] = (Op)0;
+    }
     // first half: what the Delta step needs (T fragments above the diagonal are zero and skipped)
     __device__ __forceinline__ void load_a(const uint8_t *blk, int wv, int lane) {
+        if (!RT::ALL && !RT::active(wv)) return;
+        // (a one-trip loop over row tiles changes the 64-token kernel's schedule)
+        load_rows(blk, 0, RT::rt(wv, 0), lane);
+        if constexpr (RPW > 1) load_rows(blk, 1, RT::rt(wv, 1), lane);
+    }
+    __device__ __forceinline__ void load_rows(const uint8_t *blk, int j, int rt, int lane) {
 #pragma unroll
         for (int kb = 0; kb < L::NKB; ++kb)
-            nW[kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(wv * L::NKB + kb) * 64 + lane) * 16);
-        const int sbmax = (16 * wv + 15) / M::KB;
+            nW[j][kb] = *reinterpret_cast<const frag *>(blk + L::oW + ((size_t)(rt * L::NKB + kb) * 64 + lane) * 16);
+        const int sbmax = (16 * rt + 15) / M::KB;
 #pragma unroll
         for (int sb = 0; sb < L::NSB; ++sb)
             if (sb <= sbmax)
-                Ti[sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)L::tpos(wv, sb) * 64 + lane) * 16);
+                Ti[j][sb] = *reinterpret_cast<const frag *>(blk + L::oT + ((size_t)L::tpos(rt, sb) * 64 + lane) * 16);
     }
     // second half: what the state update needs
     __device__ __forceinline__ void load_b(const uint8_t *blk, int wv, int lane) {
@@ -702,20 +740,36 @@ template <typename Op, int DK> struct StateFrags {
     }
 };
 
-template <typename Op, int DK> struct OutFrags {
+template <typename Op, int DK, int CS = 64> struct OutFrags {
     using M = Mma<Op>;
-    using L = Blk<Op, DK>;
+    using L = Blk<Op, DK, CS>;
+    using RT = RowTiles<CS>;
     using frag = typename M::frag;
-    frag Qp[L::NKB], Pm[L::NSB];
+    static constexpr int RPW = RT::RPW;
+    frag Qp[RPW][L::NKB], Pm[RPW][L::NSB];
+    // as StateFrags::zero_tri, for P
+    __device__ __forceinline__ void zero_tri() {
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+            for (int sb = 0; sb < L::NSB; ++sb)
+#pragma unroll
+                for (int e = 0; e < M::NE; ++e) Pm[j][sb][e] = (Op)0;
+    }
     __device__ __forceinline__ void load(const uint8_t *blk, int wo, int lane) {
+        if (!RT::ALL && !RT::active(wo)) return;
+        load_rows(blk, 0, RT::rt(wo, 0), lane);
+        if constexpr (RPW > 1) load_rows(blk, 1, RT::rt(wo, 1), lane);
+    }
+    __device__ __forceinline__ void load_rows(const uint8_t *blk, int j, int rt, int lane) {
 #pragma unroll
         for (int kb = 0; kb < L::NKB; ++kb)
-            Qp[kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(wo * L::NKB + kb) * 64 + lane) * 16);
-        const int sbmax = (16 * wo + 15) / M::KB;   // P is lower triangular
+            Qp[j][kb] = *reinterpret_cast<const frag *>(blk + L::oQ + ((size_t)(rt * L::NKB + kb) * 64 + lane) * 16);
+        const int sbmax = (16 * rt + 15) / M::KB;   // P is lower triangular
 #pragma unroll
         for (int sb = 0; sb < L::NSB; ++sb)
             if (sb <= sbmax)
-                Pm[sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)L::tpos(wo, sb) * 64 + lane) * 16);
+                Pm[j][sb] = *reinterpret_cast<const frag *>(blk + L::oP + ((size_t)L::tpos(rt, sb) * 64 + lane) * 16);
     }
 };
 
@@ -797,7 +851,7 @@ static constexpr int kPfMaxSleeps = 64;
 typedef const __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
 
-template <typename In, int DV, size_t BYTES>
+template <typename In, int DV, size_t BYTES, int CS = 64>
 __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
                                               int chain, int h, int H, int pf, int npf, int nch, int tb, int te,
                                               int gates)
@@ -806,7 +860,7 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
     constexpr int RL = (RB + 127) / 128;                          // lines per row
     // lines per chunk: the block, then the v rows and (per-channel gates) the w rows
-    const int PL = NL + ((gates & kGateW) ? 1 : 2) * 64 * RL;
+    const int PL = NL + ((gates & kGateW) ? 1 : 2) * CS * RL;
     constexpr int NW = 8;                                         // waves
     __shared__ uint32_t sSink[NW * 64];
     const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
@@ -828,8 +882,8 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
             if (l < NL) {
                 a = blk0 + (size_t)c * BYTES + (size_t)l * 128;
             } else {
-                const int k = l - NL, which = k / (64 * RL), row = (k / RL) % 64, part = k % RL;
-                const int tok = min(tb + 64 * c + row, te - 1);
+                const int k = l - NL, which = k / (CS * RL), row = (k / RL) % CS, part = k % RL;
+                const int tok = min(tb + CS * c + row, te - 1);
                 a = reinterpret_cast<const uint8_t *>(which ? w : v) + ((size_t)tok * H + h) * RB +
                     min(part * 128, RB - 4);
             }
@@ -868,31 +922,38 @@ __device__ __forceinline__ void tile_store(Op *dst, int lane, const f4 &x)
     *reinterpret_cast<op4 *>(dst + lane * 4) = y;
 }
 
-template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false>
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false, int CS = 64>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
     const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf, ConvIn cv, SaveOut so)
 {
     static_assert(!PRO || !WSC, "the prologue takes per-channel gates");
+    static_assert(CS == 64 || (!PRO && !SAVE), "the prologue and the backward use 64-token chunks");
     using M = Mma<Op>;
-    using L = Blk<Op, DK>;
+    using L = Blk<Op, DK, CS>;
+    using RT = RowTiles<CS>;
     using frag = typename M::frag;
-    using SF = StateFrags<Op, DK>;
-    using OF = OutFrags<Op, DK>;
-    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT;
-    constexpr int TPW = SF::TPW;
+    using SF = StateFrags<Op, DK, CS>;
+    using OF = OutFrags<Op, DK, CS>;
+    constexpr int KB = M::KB, NE = M::NE, NKB = L::NKB, NSB = L::NSB, NCT = L::NCT, NRB = L::NRB;
+    constexpr int TPW = SF::TPW, RPW = RT::RPW;
     constexpr int TPK = KB / 16;              // accumulator tiles per k-block
     constexpr int NSL = DV / (16 * NC);       // column slices (workgroups per chain)
-    constexpr int PD = 2;                     // prefetch distance (register ring of 3)
+    // register ring of operand fragments: three chunks (prefetch distance 2),
+    // two for 128-token chunks (their fragment sets are twice the size)
+    constexpr int RING = CS >= 128 ? 2 : 3;
+    constexpr int PD = RING - 1;
+    constexpr int UR = CS >= 64 ? CS / 64 : 1;   // v / w rows per output-wave thread
+    constexpr int LCS = __builtin_ctz(CS);
     static_assert(NSL >= 1 && NSL * 16 * NC == DV, "slice width must divide dv");
 
     // per 16-column tile q of the slice
     __shared__ __attribute__((aligned(16))) Op sS[NC][NCT * 64 * 4];        // state operand tiles
-    __shared__ __attribute__((aligned(16))) Op sD[NC][4 * 64 * 4];          // Delta tiles
+    __shared__ __attribute__((aligned(16))) Op sD[NC][NRB * 64 * 4];        // Delta tiles
     __shared__ __attribute__((aligned(16))) Op sU[NC][2 * NSB * 64 * NE];   // U hi / lo B-fragments
     constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
-    __shared__ __attribute__((aligned(16))) float sO[2][64 * LDO];          // o tiles
+    __shared__ __attribute__((aligned(16))) float sO[2][CS * LDO];          // o tiles
     constexpr int LDV = 16 * NC;                                             // raw-v row stride (floats)
     __shared__ __attribute__((aligned(16))) float sVr[PRO ? 3 : 1][PRO ? 64 * LDV : 4];   // PRO: raw v rows
 
@@ -910,12 +971,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const int col0 = 16 * NC * js;            // first value column of the slice
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
     const int tb = sq.t0(i), te = sq.t1(i);
-    const int cbeg = sq.m.chunk0(i);
-    const int nch = min((te - tb + 63) >> 6, max(0, sq.max_chunks - cbeg));
+    const int cbeg = sq.m.template chunk0<CS>(i);
+    const int nch = min((te - tb + CS - 1) >> LCS, max(0, sq.max_chunks - cbeg));
     auto blk_of = [&](int c) { return ops + ((size_t)h * sq.max_chunks + cbeg + min(c, nch - 1)) * L::bytes; };
     if (role >= NSL) {
-        pass_prefetch<In, DV, L::bytes>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain, h,
-                                        H, role - NSL, npf, nch, tb, te, sq.gates);
+        pass_prefetch<In, DV, L::bytes, CS>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain,
+                                            h, H, role - NSL, npf, nch, tb, te, sq.gates);
         return;
     }
     const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
@@ -940,16 +1001,23 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
             }
-        const int sbmax = (16 * wv + 15) / KB;
+        const bool rows = RT::active(wv);
+        // last stored k-block of T / P for the wave's row tile j (RPW <= 2)
+        const int sbm0 = (16 * RT::rt(wv, 0) + 15) / KB;
+        const int sbm1 = RPW > 1 ? (16 * RT::rt(wv, 1) + 15) / KB : 0;
+        auto sbmax = [&](int j) { return j == 0 ? sbm0 : sbm1; };
         SF f0, f1, f2;
+        if constexpr (CS != 64) { f0.zero_tri(); f1.zero_tri(); f2.zero_tri(); }
         if (nch > 0) {
             f0.load_a(blk_of(0), wv, lane);
             f0.load_b(blk_of(0), wv, lane);
-            f1.load_a(blk_of(1), wv, lane);
-            f1.load_b(blk_of(1), wv, lane);
+            if constexpr (RING == 3) {
+                f1.load_a(blk_of(1), wv, lane);
+                f1.load_b(blk_of(1), wv, lane);
+            }
         }
         if constexpr (PRO) __syncthreads();   // pairs with the output waves' staging of chunk 0
-        // The prefetch of chunk c+2 is split over the two windows in which
+        // The prefetch of chunk c+PD is split over the two windows in which
         // the state waves would otherwise wait for the output waves.
         const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
         auto step = [&](int c, SF &cur, SF &pre) {
@@ -965,32 +1033,46 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     }
             }
             __syncthreads();   // (1) state tiles and U ready
-            f4 acc[NC], accw[NC];
+            if (RT::ALL || rows) {
+                f4 acc[RPW][NC], accw[RPW][NC];
 #pragma unroll
-            for (int q = 0; q < NC; ++q) { acc[q] = f4zero(); accw[q] = f4zero(); }
+                for (int j = 0; j < RPW; ++j)
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                if (sb > sbmax) break;
+                    for (int q = 0; q < NC; ++q) { acc[j][q] = f4zero(); accw[j][q] = f4zero(); }
 #pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
-                    const frag ul = *reinterpret_cast<const frag *>(&sU[q][((1 * NSB + sb) * 64 + lane) * NE]);
-                    acc[q] = M::mma(cur.Ti[sb], uh, acc[q]);
-                    acc[q] = M::mma(cur.Ti[sb], ul, acc[q]);
+                for (int sb = 0; sb < NSB; ++sb) {
+                    if (RPW == 1 && sb > sbmax(0)) break;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) {
+                        const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
+                        const frag ul = *reinterpret_cast<const frag *>(&sU[q][((1 * NSB + sb) * 64 + lane) * NE]);
+#pragma unroll
+                        for (int j = 0; j < RPW; ++j) {
+                            if (RPW > 1 && sb > sbmax(j)) continue;
+                            acc[j][q] = M::mma(cur.Ti[j][sb], uh, acc[j][q]);
+                            acc[j][q] = M::mma(cur.Ti[j][sb], ul, acc[j][q]);
+                        }
+                    }
                 }
-            }
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int q = 0; q < NC; ++q)
-                    accw[q] = M::mma(cur.nW[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), accw[q]);
+                    for (int q = 0; q < NC; ++q) {
+                        const frag sf = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
 #pragma unroll
-            for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sD[q] + wv * 256, lane, acc[q] + accw[q]);
-            if constexpr (SAVE) {
-                Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
+                        for (int j = 0; j < RPW; ++j) accw[j][q] = M::mma(cur.nW[j][kb], sf, accw[j][q]);
+                    }
 #pragma unroll
-                for (int q = 0; q < NC; ++q)
-                    tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, acc[q] + accw[q]);
+                for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                    for (int q = 0; q < NC; ++q)
+                        lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, acc[j][q] + accw[j][q]);
+                if constexpr (SAVE) {
+                    Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q)
+                        tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, acc[0][q] + accw[0][q]);
+                }
             }
             pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready
@@ -1019,17 +1101,25 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             // XCD and read the counter from the shared L2.
             if (report) __hip_atomic_store(prog + chain, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
-        // Full rounds of three steps carry no branches, so the register ring
+        // Full rounds of RING steps carry no branches, so the register ring
         // needs no merge copies (a copy of a register with a load in flight
         // waits for that load and every load issued before it).
         int c = 0;
-        for (; c + 3 <= nch; c += 3) {
-            step(c, f0, f2);
-            step(c + 1, f1, f0);
-            step(c + 2, f2, f1);
+        if constexpr (RING == 3) {
+            for (; c + 3 <= nch; c += 3) {
+                step(c, f0, f2);
+                step(c + 1, f1, f0);
+                step(c + 2, f2, f1);
+            }
+            if (c < nch) step(c, f0, f2);
+            if (c + 1 < nch) step(c + 1, f1, f0);
+        } else {
+            for (; c + 2 <= nch; c += 2) {
+                step(c, f0, f1);
+                step(c + 1, f1, f0);
+            }
+            if (c < nch) step(c, f0, f1);
         }
-        if (c < nch) step(c, f0, f2);
-        if (c + 1 < nch) step(c + 1, f1, f0);
         __syncthreads();   // final: pairs with the output waves' last o tile
         if (ST) {
 #pragma unroll
@@ -1046,27 +1136,39 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     } else {
         // ------------------------------------------------ output waves
         const int wo = wv - 4, to = t - 256;
-        const int sbmax = (16 * wo + 15) / KB;
-        // v / w tile coordinates of this thread (per column tile) and where its U values go
+        const bool rows = RT::active(wo);
+        // last stored k-block of T / P for the wave's row tile j (RPW <= 2)
+        const int sbm0 = (16 * RT::rt(wo, 0) + 15) / KB;
+        const int sbm1 = RPW > 1 ? (16 * RT::rt(wo, 1) + 15) / KB : 0;
+        auto sbmax = [&](int j) { return j == 0 ? sbm0 : sbm1; };
+        // v / w tile coordinates of this thread (rows ur + 64 x, per column
+        // tile) and where its U values go
         const int ur = to >> 2, uc = 4 * (to & 3);
+        const bool urow = CS >= 64 || ur < CS;
         const size_t uoff0 = (size_t)h * DV + col0 + uc;
         const int usb = ur / KB, usl = ur % KB;
         const int ug = (usl & 15) >> 2, ui = 4 * (usl >> 4) + (usl & 3);
-        auto uv_ok = [&](int c) { return c < nch && tb + 64 * c + ur < te; };
-        auto uv_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H * DV + uoff0; };
-        auto w_off = [&](int c) { return (size_t)min(tb + 64 * c + ur, te - 1) * H + h; };
-        struct UV { UVTile<In> q[NC]; };
+        auto uv_ok = [&](int c, int x) { return c < nch && urow && tb + CS * c + ur + 64 * x < te; };
+        auto uv_off = [&](int c, int x) { return (size_t)min(tb + CS * c + ur + 64 * x, te - 1) * H * DV + uoff0; };
+        auto w_off = [&](int c, int x) { return (size_t)min(tb + CS * c + ur + 64 * x, te - 1) * H + h; };
+        struct UV { UVTile<In> q[NC * UR]; };   // tile q of row ur + 64 x at q + NC x
         auto uv_load = [&](UV &u, int c) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q) u.q[q].template load<WSC>(v, w, uv_off(c) + 16 * q, w_off(c), uv_ok(c));
+            for (int x = 0; x < UR; ++x)
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+                    u.q[q + NC * x].template load<WSC>(v, w, uv_off(c, x) + 16 * q, w_off(c, x), uv_ok(c, x));
         };
         OF g0, g1, g2;
         UV u0, u1, u2;
+        if constexpr (CS != 64) { g0.zero_tri(); g1.zero_tri(); g2.zero_tri(); }
         if (nch > 0) {
             if constexpr (!SAVE) g0.load(blk_of(0), wo, lane);
             uv_load(u0, 0);
-            if constexpr (!SAVE) g1.load(blk_of(1), wo, lane);
-            uv_load(u1, 1);
+            if constexpr (RING == 3) {
+                if constexpr (!SAVE) g1.load(blk_of(1), wo, lane);
+                uv_load(u1, 1);
+            }
         }
         // PRO: taps and bias of the thread's columns (per column tile)
         f4 ctap[PRO ? NC : 1][4], cbias[PRO ? NC : 1];
@@ -1135,13 +1237,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             if (nch > 0) conv_u(u0, 0, 2);
         }
         // o tiles go through LDS (double-buffered) and leave as 16-byte
-        // stores (NC per thread) after the next barrier
+        // stores (CS * NC / 64 per thread) after the next barrier
         auto store_o = [&](int c) {
-            const int tok = tb + 64 * c, n = min(64, te - tok);
+            const int tok = tb + CS * c, n = min(CS, te - tok);
+            constexpr int NPC = CS * 4 * NC;   // 16-byte pieces per chunk
 #pragma unroll
-            for (int q = 0; q < NC; ++q) {
-                const int x = to + 256 * q, row = x / (4 * NC), q4 = x % (4 * NC);
-                if (row < n)
+            for (int pq = 0; pq < (NPC + 255) / 256; ++pq) {
+                const int x = to + 256 * pq, row = x / (4 * NC), q4 = x % (4 * NC);
+                if ((NPC % 256 == 0 || x < NPC) && row < n)
                     *reinterpret_cast<f4 *>(o + ((size_t)(tok + row) * H + h) * DV + col0 + 4 * q4) =
                         *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
             }
@@ -1153,19 +1256,23 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &unext, UV &upre, int sl) {
             const int sln = sl == 2 ? 0 : sl + 1;
             if constexpr (PRO) stage_v(unext, sln);
+            if (urow) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q)
+                for (int x = 0; x < UR; ++x)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const UVTile<In> &uq = ucur.q[q];
-                    float uu;
-                    if constexpr (PRO) uu = ucarry[q][e];
-                    else uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
-                    const Op hi = (Op)uu;
-                    const int ln = (uc + e) + 16 * ug;
-                    sU[q][((0 * NSB + usb) * 64 + ln) * NE + ui] = hi;
-                    sU[q][((1 * NSB + usb) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
-                }
+                    for (int q = 0; q < NC; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const UVTile<In> &uq = ucur.q[q + NC * x];
+                            float uu;
+                            if constexpr (PRO) uu = ucarry[q][e];
+                            else uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                            const Op hi = (Op)uu;
+                            const int ln = (uc + e) + 16 * ug, sbx = usb + 64 * x / KB;
+                            sU[q][((0 * NSB + sbx) * 64 + ln) * NE + ui] = hi;
+                            sU[q][((1 * NSB + sbx) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+                        }
+            }
             __syncthreads();   // (1)
             if constexpr (!SAVE) pre.load(blk_of(c + PD), wo, lane);
             uv_load(upre, c + PD);
@@ -1175,36 +1282,61 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 return;
             }
             if (c > 0) store_o(c - 1);
-            f4 oacc[NC];
+            f4 oacc[RPW][NC];
+            if (RT::ALL || rows) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q) oacc[q] = f4zero();
+                for (int j = 0; j < RPW; ++j)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                    for (int q = 0; q < NC; ++q) oacc[j][q] = f4zero();
 #pragma unroll
-                for (int q = 0; q < NC; ++q)
-                    oacc[q] = M::mma(cur.Qp[kb], lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane), oacc[q]);
-            __syncthreads();   // (2)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                if (sb > sbmax) break;
+                    for (int q = 0; q < NC; ++q) {
+                        const frag sf = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
 #pragma unroll
-                for (int q = 0; q < NC; ++q)
-                    oacc[q] = M::mma(cur.Pm[sb], lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane), oacc[q]);
+                        for (int j = 0; j < RPW; ++j) oacc[j][q] = M::mma(cur.Qp[j][kb], sf, oacc[j][q]);
+                    }
             }
+            __syncthreads();   // (2)
+            if (RT::ALL || rows) {
 #pragma unroll
-            for (int q = 0; q < NC; ++q)
+                for (int sb = 0; sb < NSB; ++sb) {
+                    if (RPW == 1 && sb > sbmax(0)) break;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-                    sO[c & 1][(16 * wo + 4 * g4 + ii) * LDO + 16 * q + m16] = oacc[q][ii];
+                    for (int q = 0; q < NC; ++q) {
+                        const frag df = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+#pragma unroll
+                        for (int j = 0; j < RPW; ++j) {
+                            if (RPW > 1 && sb > sbmax(j)) continue;
+                            oacc[j][q] = M::mma(cur.Pm[j][sb], df, oacc[j][q]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < RPW; ++j)
+#pragma unroll
+                    for (int q = 0; q < NC; ++q)
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            sO[c & 1][(16 * RT::rt(wo, j) + 4 * g4 + ii) * LDO + 16 * q + m16] = oacc[j][q][ii];
+            }
         };
         int c = 0;
-        for (; c + 3 <= nch; c += 3) {
-            step(c, g0, g2, u0, u1, u2, 0);
-            step(c + 1, g1, g0, u1, u2, u0, 1);
-            step(c + 2, g2, g1, u2, u0, u1, 2);
+        if constexpr (RING == 3) {
+            for (; c + 3 <= nch; c += 3) {
+                step(c, g0, g2, u0, u1, u2, 0);
+                step(c + 1, g1, g0, u1, u2, u0, 1);
+                step(c + 2, g2, g1, u2, u0, u1, 2);
+            }
+            if (c < nch) step(c, g0, g2, u0, u1, u2, 0);
+            if (c + 1 < nch) step(c + 1, g1, g0, u1, u2, u0, 1);
+        } else {
+            for (; c + 2 <= nch; c += 2) {
+                step(c, g0, g1, u0, u0, u1, 0);
+                step(c + 1, g1, g0, u1, u1, u0, 1);
+            }
+            if (c < nch) step(c, g0, g1, u0, u0, u1, 0);
         }
-        if (c < nch) step(c, g0, g2, u0, u1, u2, 0);
-        if (c + 1 < nch) step(c + 1, g1, g0, u1, u2, u0, 1);
         __syncthreads();   // final
         if (!SAVE && nch > 0) store_o(nch - 1);
     }
@@ -1231,18 +1363,51 @@ static hipError_t device_cus(int *cus)
     return hipSuccess;
 }
 
-template <typename In, typename Op, int DK, int DV>
-static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st, SaveOut so = {nullptr, nullptr})
+// The chunk bookkeeping of one call as the kernels see it.
+static inline Seqs make_seqs(const ChunkArgs &a, const ChunkPlan &p)
 {
-    uint8_t *ws = (uint8_t *)a.workspace;
     Seqs sq;
     sq.m.cu = a.cu_seqlens;
-    sq.m.co = a.cu_seqlens ? (const int32_t *)ws : nullptr;
+    sq.m.co = a.cu_seqlens ? (const int32_t *)a.workspace : nullptr;
     sq.m.N = a.N;
     sq.m.T = a.T;
     sq.Ttot = a.cu_seqlens ? a.T : a.B * a.T;
     sq.max_chunks = p.max_chunks;
     sq.gates = a.gates;
+    return sq;
+}
+
+// Shape of the pass grid. One 16-column tile per workgroup with L2 prefetch
+// workgroups where the grid stays resident at one workgroup per compute
+// unit; two tiles per workgroup where one tile would oversubscribe the chip
+// (half the workgroups, each streaming the same operand blocks once for
+// twice the columns), with prefetch workgroups if the halved grid leaves room.
+struct PassShape {
+    bool two;          // two 16-column tiles per workgroup
+    int npf;           // prefetch workgroups per chain
+    long long grid;    // workgroups
+};
+
+template <int DV> static hipError_t pass_shape(long long chains, const ChunkPlan &p, PassShape *ps)
+{
+    int cus = 0;
+    const hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
+    const long long groups = (chains + 7) / 8;
+    constexpr int NSL1 = DV / 16;
+    ps->two = (DV / 16) % 2 == 0 && 8LL * NSL1 * groups > cus;
+    const int nsl = ps->two ? NSL1 / 2 : NSL1;
+    const int n = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - nsl);
+    ps->npf = (n < 2 || p.max_chunks == 0) ? 0 : n;
+    ps->grid = 8LL * (nsl + ps->npf) * groups;
+    return ps->grid > 0x7fffffffLL ? hipErrorInvalidValue : hipSuccess;
+}
+
+template <typename In, typename Op, int DK, int DV>
+static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st, SaveOut so = {nullptr, nullptr})
+{
+    uint8_t *ws = (uint8_t *)a.workspace;
+    const Seqs sq = make_seqs(a, p);
     hipError_t err = hipSuccess;
     int *prog = (int *)(ws + p.plan_bytes);
     uint8_t *ops = ws + p.plan_bytes + p.prog_bytes;
@@ -1265,28 +1430,14 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    // One 16-column tile per workgroup with L2 prefetch workgroups where the
-    // grid stays resident at one workgroup per compute unit; two tiles per
-    // workgroup where one tile would oversubscribe the chip (half the
-    // workgroups, each streaming the same operand blocks once for twice the
-    // columns), with prefetch workgroups if the halved grid leaves room.
-    int cus = 0;
-    if ((err = device_cus(&cus)) != hipSuccess) return err;
-    const long long groups = (chains + 7) / 8;
-    auto npf_for = [&](int nsl) {
-        int n = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - nsl);
-        return (n < 2 || p.max_chunks == 0) ? 0 : n;
-    };
-    constexpr int NSL1 = DV / 16;
-    const bool two = (DV / 16) % 2 == 0 && 8LL * NSL1 * groups > cus;
-    const int nsl = two ? NSL1 / 2 : NSL1;
-    const int npf = npf_for(nsl);
-    const long long pass_grid = 8LL * (nsl + npf) * groups;
-    if (pass_grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    PassShape ps;
+    if ((err = pass_shape<DV>(chains, p, &ps)) != hipSuccess) return err;
+    const bool two = ps.two;
+    const int npf = ps.npf;
     prof_before("gdn2_chunk_pass", st);
     const ConvIn cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in};
     auto pass = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)pass_grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
+        hipLaunchKernelGGL(kern, dim3((unsigned)ps.grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
                            (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf, cv, so);
     };
     const bool wsc = a.gates & kGateW;

@@ -156,21 +156,23 @@ __device__ __forceinline__ typename Mma<Op>::frag lds_row_frag(const Op *rowp, i
 }
 
 // ---- chunk bookkeeping -------------------------------------------------------
-// Sequences are token ranges [cu[i], cu[i+1]); each is cut into 64-token
-// chunks starting at its first token; chunk ids are numbered sequence by
-// sequence (co[i] = first chunk id of sequence i). Uniform batches (no
-// cu_seqlens) use cu[i] = i*T and co[i] = i*ceil(T/64) computed in place.
+// Sequences are token ranges [cu[i], cu[i+1]); each is cut into CS-token
+// chunks (64 unless a chunk-size variant asks otherwise) starting at its first
+// token; chunk ids are numbered sequence by sequence (co[i] = first chunk id
+// of sequence i). Uniform batches (no cu_seqlens) use cu[i] = i*T and
+// co[i] = i*ceil(T/CS) computed in place.
 struct SeqMap {
     const int32_t *cu;   // device [N+1] or null (uniform)
     const int32_t *co;   // device [N+1] chunk offsets (varlen) or null
     int N, T;            // T: tokens per sequence when uniform
     __device__ __forceinline__ int tok0(int i) const { return cu ? cu[i] : i * T; }
     __device__ __forceinline__ int tok1(int i) const { return cu ? cu[i + 1] : (i + 1) * T; }
-    __device__ __forceinline__ int chunk0(int i) const { return co ? co[i] : i * ((T + 63) >> 6); }
-    __device__ __forceinline__ int nchunks() const { return co ? co[N] : N * ((T + 63) >> 6); }
+    template <int CS = 64> __device__ __forceinline__ int per_seq() const { return (T + CS - 1) >> __builtin_ctz(CS); }
+    template <int CS = 64> __device__ __forceinline__ int chunk0(int i) const { return co ? co[i] : i * per_seq<CS>(); }
+    template <int CS = 64> __device__ __forceinline__ int nchunks() const { return co ? co[N] : N * per_seq<CS>(); }
     // sequence owning chunk id j (j < nchunks()): largest i with chunk0(i) <= j
-    __device__ __forceinline__ int seq_of(int j) const {
-        if (!co) return j / ((T + 63) >> 6);
+    template <int CS = 64> __device__ __forceinline__ int seq_of(int j) const {
+        if (!co) return j / per_seq<CS>();
         int lo = 0, hi = N - 1;
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;

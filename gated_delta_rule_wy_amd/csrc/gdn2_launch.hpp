@@ -59,6 +59,7 @@ struct ChunkArgs {
 //   [plan_bytes + prog_bytes, ...)       operand blocks, head-major:
 //                                        block (h, j) at (h * max_chunks + j)
 struct ChunkPlan {
+    int chunk;                   // tokens per chunk: 64, or 32 / 128 (per-channel gates, no prologue)
     int max_chunks;              // grid bound on chunk ids
     size_t plan_bytes;           // bytes reserved for co[]
     size_t prog_bytes;           // bytes reserved for the progress counters
@@ -66,8 +67,8 @@ struct ChunkPlan {
     size_t total_bytes;
 };
 
-// Returns false when the sizes are not supported.
-bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p);
+// Returns false when the sizes (or the chunk size) are not supported.
+bool chunk_plan(int B, int T, int N, int H, int dk, int dv, bool bf16, bool varlen, ChunkPlan *p, int chunk = 64);
 
 // Backward of the prefill (gradients of a loss through o and S_T).
 struct ChunkBwdArgs {

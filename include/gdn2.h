@@ -132,6 +132,29 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
                          size_t workspace_bytes);
 
 /*
+ * Chunk-size variants of the prefill forward: gdn2_chunk_fwd with chunks of
+ * `chunk` tokens, 32, 64 or 128 (snilld.dk, section "POC-matrix der dækker
+ * de hårde hjørner": latency, throughput and peak memory at C = 32 and 128
+ * besides the C = 64 of the implementation). The result is the same
+ * recurrence; a longer chunk halves the serial chain over chunks and
+ * doubles the triangular work per token. chunk = 64 is gdn2_chunk_fwd.
+ *
+ * Arguments, layouts, ownership and errors as gdn2_chunk_fwd (per-channel
+ * gates), with the workspace size from gdn2_chunk_fwd_sized_workspace_bytes
+ * for the same chunk. A chunk other than 32, 64 or 128 gives
+ * GDN2_ERR_INVALID; f32 inputs with dk = 128 and chunk = 128 give
+ * GDN2_ERR_UNSUPPORTED (the preparation kernel's tiles would not fit one
+ * compute unit's 160 KB of LDS).
+ */
+size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
+                                            gdn2_dtype in_dtype, int varlen, int chunk);
+int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const void *b, const void *w, const float *S0, void *o, float *ST,
+                         const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, int chunk, void *workspace,
+                         size_t workspace_bytes);
+
+/*
  * One recurrent decode step for N independent sequences (the same update
  * and readout for a single token; constant-size state, aifetchly, "Gated
  * DeltaNet-2 Guide", section "3. Chunkwise Parallel Algorithm ...": O(1)

@@ -73,6 +73,66 @@ def test_workspace_bytes():
     assert WS(1, 64, 1, 1, 128, 128, 7, 0) == 0                   # unknown dtype
 
 
+WSC = gdn2.lib().gdn2_chunk_fwd_sized_workspace_bytes
+
+
+def _block_bytes(dk, bf16, C):
+    """Operand block of one (chunk, head): -W and Q+ (C/16 x dk/KB fragments
+    each), Khat^T (dk/16 x C/KB), the stored lower-triangle fragments of P and
+    T, and gamma (dk floats); a fragment is 64 lanes x 16 bytes."""
+    KB = 32 if bf16 else 16
+    nrb = C // 16
+    ntri = sum((16 * m + 15) // KB + 1 for m in range(nrb))
+    frags = 2 * nrb * (dk // KB) + (dk // 16) * (C // KB) + 2 * ntri
+    return (frags * 1024 + 4 * dk + 255) // 256 * 256
+
+
+@pytest.mark.parametrize('C', [32, 64, 128])
+@pytest.mark.parametrize('dt,dk', [(gdn2.GDN2_BF16, 128), (gdn2.GDN2_BF16, 32), (gdn2.GDN2_F32, 16),
+                                   (gdn2.GDN2_F32, 64)])
+def test_sized_workspace_bytes(C, dt, dk):
+    bf = dt == gdn2.GDN2_BF16
+    one = _block_bytes(dk, bf, C)
+    assert WSC(1, C, 1, 1, dk, 64, dt, 0, C) == 256 + one
+    assert WSC(1, C + 1, 1, 3, dk, 64, dt, 0, C) == 256 + 6 * one
+    assert WSC(1, 5 * C, 2, 1, dk, 64, dt, 1, C) == 256 + 256 + 7 * one   # varlen: one extra chunk per sequence
+    if C == 64:
+        assert WSC(1, 4096, 1, 16, dk, 64, dt, 0, C) == WS(1, 4096, 1, 16, dk, 64, dt, 0)
+
+
+def test_sized_workspace_rejects():
+    assert WSC(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0, 48) == 0     # chunk not 32, 64 or 128
+    assert WSC(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0, 256) == 0
+    assert WSC(1, 64, 1, 1, 128, 128, gdn2.GDN2_F32, 0, 128) == 0     # fp32 dk=128 at C=128: LDS
+    assert WSC(1, 64, 1, 1, 128, 128, gdn2.GDN2_F32, 0, 32) > 0
+    assert WSC(1, 64, 1, 1, 16, 128, gdn2.GDN2_BF16, 0, 32) == 0      # bf16 needs dk >= 32
+
+
+def _chunk_sized(chunk, **kw):
+    P = 0x10000
+    a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S0=None, o=P, ST=P, cu=None, B=1, T=64, N=1, H=1,
+             dk=128, dv=128, dt=gdn2.GDN2_BF16, odt=gdn2.GDN2_F32, ws=P, wsb=1 << 30)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return gdn2.lib().gdn2_chunk_fwd_sized(*(vp(a[x]) if a[x] else None for x in
+                                             ('q', 'k', 'v', 'la', 'b', 'w', 'S0', 'o', 'ST', 'cu')),
+                                           a['B'], a['T'], a['N'], a['H'], a['dk'], a['dv'], a['dt'], a['odt'],
+                                           chunk, vp(a['ws']) if a['ws'] else None, a['wsb'])
+
+
+@pytest.mark.parametrize('chunk,kw,status', [
+    (48, {}, gdn2.GDN2_ERR_INVALID),
+    (0, {}, gdn2.GDN2_ERR_INVALID),
+    (128, dict(dt=gdn2.GDN2_F32), gdn2.GDN2_ERR_UNSUPPORTED),
+    (32, dict(q=None), gdn2.GDN2_ERR_INVALID),
+    (128, dict(N=2), gdn2.GDN2_ERR_INVALID),
+    (32, dict(dk=16), gdn2.GDN2_ERR_UNSUPPORTED),
+    (128, dict(wsb=1024), gdn2.GDN2_ERR_WORKSPACE),
+])
+def test_sized_rejects(chunk, kw, status):
+    assert _chunk_sized(chunk, **kw) == status
+
+
 def _chunk(**kw):
     P = 0x10000   # a fake, aligned, never-dereferenced address
     a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S0=None, o=P, ST=P, cu=None, B=1, T=64, N=1, H=1,

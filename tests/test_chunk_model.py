@@ -7,7 +7,7 @@ import oracle
 import pins
 
 
-@pytest.mark.parametrize('C', [1, 16, 64])
+@pytest.mark.parametrize('C', [1, 16, 32, 64, 128])
 def test_chunk_form_equals_oracle(C):
     rng = np.random.default_rng(40 + C)
     lens = [130, 64, 1, 0, 77]
@@ -30,9 +30,10 @@ def test_chunk_form_strong_decay():
     q, k, v, la, b, w, S0 = pins.rand_inputs(rng, T, H, dk, dv)
     la = np.full_like(la, -5.0)
     o_ref, ST_ref = oracle.forward(q, k, v, la, b, w, S0)
-    o, ST = chunk_model.chunk_forward(q, k, v, la, b, w, S0)
-    pins.close(o, o_ref, 1e-12, 'strong decay o')
-    pins.close(ST, ST_ref, 1e-12, 'strong decay S_T')
+    for C in (32, 64, 128):
+        o, ST = chunk_model.chunk_forward(q, k, v, la, b, w, S0, C=C)
+        pins.close(o, o_ref, 1e-12, f'strong decay o, C={C}')
+        pins.close(ST, ST_ref, 1e-12, f'strong decay S_T, C={C}')
 
 
 @pytest.mark.parametrize('C', [1, 16, 64])
