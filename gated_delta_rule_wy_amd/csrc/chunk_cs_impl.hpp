@@ -45,7 +45,10 @@ template <typename Op, int DK, int CS> struct PrepCS {
     static constexpr size_t bE = (size_t)CS * LDE * sizeof(Op);
     static constexpr size_t bA = (size_t)NTB * BSZ * 4;
     static constexpr size_t bT = (size_t)NTB * BSZ * sizeof(Op);
-    static constexpr size_t bScr = (size_t)(NRG + 2 * NRB + 2) * DK * 4;
+    static constexpr int NDEC = (NRB - 1) * (NRB - 2) / 2;         // block pairs (R, S), R >= S + 2
+    // scratch: partial sums, references, middles, g at row 0; then the slow
+    // path's factor tables (diagonal E and K sides, off-diagonal pairs)
+    static constexpr size_t bScr = (size_t)(NRG + 2 * NRB + 2 + 2 * NRB + NDEC) * DK * 4;
     static constexpr size_t bTab = (size_t)2 * NRB * DK * 4;
     static constexpr size_t oE = 0;                                  // E-side operand
     static constexpr size_t oQK = oE + bE;                           // Q-, K-side operands; then A
@@ -90,6 +93,10 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
     float *sRef = sPart + NRG * DK;           // [NRB + 1][DK]: ref_0..ref_NRB (ref_NRB = g at the last row)
     float *sMid = sRef + (NRB + 1) * DK;      // [NRB][DK]
     float *sG0 = sMid + NRB * DK;             // [DK]: g at the first row
+    // slow path: e^{ref_R - mid_R} (E side) and e^{mid_R - ref_{R+1}} (K side)
+    // of diagonal block R; e^{ref_R - ref_{S+1}} of block (R, S), R >= S + 2,
+    // at row (R - 2)(R - 1)/2 + S
+    float *tDiagE = sG0 + DK, *tDiagK = tDiagE + NRB * DK, *tDec = tDiagK + NRB * DK;
     // [0, NRB): Q+ / E scale per row block; [NRB, 2 NRB): Khat scale (the fast path uses rows 0 and NRB)
     float *tExpRef = (float *)(lds + PL::oTab), *tExpKh = tExpRef + NRB * DK;
     int *sFlag = (int *)(lds + PL::oFlag);    // [0, NRB): exact diagonal blocks; [NRB]: slow chunk
@@ -150,6 +157,18 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
     __syncthreads();
     const bool fast = sFlag[NRB] == 0;
     auto kval = [&](int u) { return Ld<In>::cvt2(kr[u]) * rowf(u); };
+    // fragment element i times tab[kbase + kofs(g4, i)] (tab null: zero)
+    auto scale_frag = [](frag x, const float *tab, int kbase, int g) {
+        frag y;
+#pragma unroll
+        for (int pq = 0; pq < NE / 4; ++pq) {
+            f4 f = f4zero();
+            if (tab) f = *reinterpret_cast<const f4 *>(tab + kbase + 16 * pq + 4 * g);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) y[4 * pq + ii] = (Op)((float)x[4 * pq + ii] * f[ii]);
+        }
+        return y;
+    };
     auto qval = [&](int u) { return Ld<In>::cvt2(qr[u]) * rowf(u); };
     auto bval = [&](int u) { return Ld<In>::cvt2(br[u]); };
 
@@ -181,7 +200,16 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
             const float mid = sMid[R * DK + c], gn = sRef[NRB * DK + c];
             tExpRef[R * DK + c] = __expf(rR);
             tExpKh[R * DK + c] = __expf(gn - rR1);
+            tDiagE[R * DK + c] = __expf(rR - mid);
+            tDiagK[R * DK + c] = __expf(mid - rR1);
             if (fmaxf(rR - mid, mid - rR1) > LIM) atomicOr(&sFlag[R], 1);
+        }
+        for (int idx = t; idx < PL::NDEC * DK; idx += NT) {
+            const int pr = idx / DK, c = idx % DK;
+            int R = 2;
+            while ((R - 1) * R / 2 <= pr) ++R;   // pair row pr: R with (R-2)(R-1)/2 <= pr < (R-1)R/2
+            const int S = pr - (R - 2) * (R - 1) / 2;
+            tDec[pr * DK + c] = __expf(sRef[R * DK + c] - sRef[(S + 1) * DK + c]);
         }
         // e1_r = e^{g_r - ref_R} forward, e2_r = e^{ref_{R+1} - g_r} backward,
         // as running products of alpha within the 16-row block
@@ -255,28 +283,21 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
         // runs whatever the execution mask, on registers the skipped path
         // never loaded. Exact blocks get zero operands here.
         f4 acc = f4zero();
-#pragma unroll
+        // (not unrolled: nine jobs of unrolled slow-path operand code overflow the instruction cache)
+#pragma unroll 1
         for (int kb = 0; kb < NKB; ++kb) {
-            frag a, bb;
-            if (fast) {
-                a = lds_row_frag<Op>(sK + (16 * S + m16) * LDE, kb * KB, g4);
-                bb = lds_row_frag<Op>(src + (16 * R + m16) * LDE, kb * KB, g4);
-            } else {
-#pragma unroll
-                for (int i4 = 0; i4 < NE; ++i4) {
-                    const int ch = kb * KB + kofs(g4, i4);
-                    float kv = 0.f, xv = 0.f;
-                    if (!exact) {
-                        kv = (float)sK[(16 * S + m16) * LDE + ch];
-                        xv = (float)src[(16 * R + m16) * LDE + ch];
-                        if (R == S) {
-                            const float mid = sMid[R * DK + ch];
-                            xv *= __expf(sRef[R * DK + ch] - mid);
-                            kv *= __expf(mid - sRef[(R + 1) * DK + ch]);
-                        } else if (R > S + 1) kv *= __expf(sRef[R * DK + ch] - sRef[(S + 1) * DK + ch]);
-                    }
-                    a[i4] = (Op)kv;
-                    bb[i4] = (Op)xv;
+            frag a = lds_row_frag<Op>(sK + (16 * S + m16) * LDE, kb * KB, g4);
+            frag bb = lds_row_frag<Op>(src + (16 * R + m16) * LDE, kb * KB, g4);
+            if (!fast) {
+                // block factors (row-fragment reads, 4 channels per table read)
+                if (exact) {
+                    a = scale_frag(a, nullptr, 0, g4);
+                    bb = scale_frag(bb, nullptr, 0, g4);
+                } else if (R == S) {
+                    bb = scale_frag(bb, tDiagE + R * DK, kb * KB, g4);
+                    a = scale_frag(a, tDiagK + R * DK, kb * KB, g4);
+                } else if (R > S + 1) {
+                    a = scale_frag(a, tDec + ((R - 2) * (R - 1) / 2 + S) * DK, kb * KB, g4);
                 }
             }
             acc = M::mma(a, bb, acc);
