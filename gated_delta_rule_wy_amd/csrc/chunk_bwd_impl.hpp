@@ -812,50 +812,78 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
 #pragma unroll
         for (int ct = 0; ct < CWT; ++ct) {
             const int cl = 16 * ct + m16, c = c0 + cl, ctg = cs * CWT + ct;
-            // (M o Dec) x for rows of block R
-            auto rows = [&](const float *Mt, const float *Xt, const float *Xm) {
-                f4 y = f4zero();
-                for (int S = 0; S < R; ++S) {
-                    const f4 a = *reinterpret_cast<const f4 *>(Mt + (16 * R + m16) * LDF + 16 * S + 4 * g4);
-                    const f4 bx = *reinterpret_cast<const f4 *>(Xt + cl * LDF + 16 * S + 4 * g4);
-                    const f4 p = MF::mma(a, bx, f4zero());
-                    const float ref = sRef[(S + 1) * DK + c];
+            // g of the lane's four rows of block R (rows r for Y, rows s for Z)
+            float gR[4];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) y[ii] += p[ii] * __expf(sg[(16 * R + 4 * g4 + ii) * LDC + cl] - ref);
+            for (int ii = 0; ii < 4; ++ii) gR[ii] = sg[(16 * R + 4 * g4 + ii) * LDC + cl];
+            const float midR = sMid[R * DK + c];
+            // Y1 = (dP o Dec) x and Y2 = (dA o Dec) x for rows of block R, in
+            // one loop: the two products share the right operand and the decay
+            // factors, and give the wave two independent chains
+            f4 Y1 = f4zero(), Y2 = f4zero();
+            for (int S = 0; S < R; ++S) {
+                const f4 bx = *reinterpret_cast<const f4 *>(XtT + cl * LDF + 16 * S + 4 * g4);
+                const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * S + 4 * g4);
+                const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * S + 4 * g4);
+                const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
+                const float ref = sRef[(S + 1) * DK + c];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(gR[ii] - ref);
+                    Y1[ii] += p1[ii] * f;
+                    Y2[ii] += p2[ii] * f;
                 }
-                const f4 a = *reinterpret_cast<const f4 *>(Mt + (16 * R + m16) * LDF + 16 * R + 4 * g4);
-                const f4 bx = *reinterpret_cast<const f4 *>(Xm + cl * LDF + 16 * R + 4 * g4);
-                const f4 p = MF::mma(a, bx, f4zero());
-                const float mid = sMid[R * DK + c];
+            }
+            {
+                const f4 bx = *reinterpret_cast<const f4 *>(XmT + cl * LDF + 16 * R + 4 * g4);
+                const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * R + 4 * g4);
+                const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * R + 4 * g4);
+                const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) y[ii] += p[ii] * __expf(sg[(16 * R + 4 * g4 + ii) * LDC + cl] - mid);
-                return y;
-            };
-            // (M o Dec)^T y for rows s of block S = R
-            auto cols = [&](const float *Mt, const float *Yt, const float *Ym) {
-                f4 z = f4zero();
-                for (int Rr = R + 1; Rr < 4; ++Rr) {
-                    f4 a;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) a[e] = Mt[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
-                    const f4 by = *reinterpret_cast<const f4 *>(Yt + cl * LDF + 16 * Rr + 4 * g4);
-                    const f4 p = MF::mma(a, by, f4zero());
-                    const float ref = sRef[Rr * DK + c];
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) z[ii] += p[ii] * __expf(ref - sg[(16 * R + 4 * g4 + ii) * LDC + cl]);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(gR[ii] - midR);
+                    Y1[ii] += p1[ii] * f;
+                    Y2[ii] += p2[ii] * f;
                 }
-                f4 a;
+            }
+            // Z1 = (dP o Dec)^T q and Z2 = (dA o Dec)^T (b k) for rows s of
+            // block S = R, in one loop with shared decay factors
+            f4 Z1 = f4zero(), Z2 = f4zero();
+            for (int Rr = R + 1; Rr < 4; ++Rr) {
+                f4 a1, a2;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = Mt[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
-                const f4 by = *reinterpret_cast<const f4 *>(Ym + cl * LDF + 16 * R + 4 * g4);
-                const f4 p = MF::mma(a, by, f4zero());
-                const float mid = sMid[R * DK + c];
+                for (int e = 0; e < 4; ++e) {
+                    a1[e] = sdP[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
+                    a2[e] = sdA[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
+                }
+                const f4 b1 = *reinterpret_cast<const f4 *>(QtT + cl * LDF + 16 * Rr + 4 * g4);
+                const f4 b2 = *reinterpret_cast<const f4 *>(BtT + cl * LDF + 16 * Rr + 4 * g4);
+                const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
+                const float ref = sRef[Rr * DK + c];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) z[ii] += p[ii] * __expf(mid - sg[(16 * R + 4 * g4 + ii) * LDC + cl]);
-                return z;
-            };
-            const f4 Y1 = rows(sdP, XtT, XmT), Y2 = rows(sdA, XtT, XmT);
-            const f4 Z1 = cols(sdP, QtT, QmT), Z2 = cols(sdA, BtT, BmT);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(ref - gR[ii]);
+                    Z1[ii] += p1[ii] * f;
+                    Z2[ii] += p2[ii] * f;
+                }
+            }
+            {
+                f4 a1, a2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a1[e] = sdP[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
+                    a2[e] = sdA[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
+                }
+                const f4 b1 = *reinterpret_cast<const f4 *>(QmT + cl * LDF + 16 * R + 4 * g4);
+                const f4 b2 = *reinterpret_cast<const f4 *>(BmT + cl * LDF + 16 * R + 4 * g4);
+                const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(midR - gR[ii]);
+                    Z1[ii] += p1[ii] * f;
+                    Z2[ii] += p2[ii] * f;
+                }
+            }
             const float gn = sRef[4 * DK + c];
             float khk = 0.f;
 #pragma unroll
