@@ -489,7 +489,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                      B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
                      B_G = B_QM + CW * LDF, B_DG = B_G + 64 * LDC, B_GAM = B_DG + 64 * LDC, B_KHK = B_GAM + DK,
                      B_END = B_KHK + DK;                                            // floats
-    constexpr size_t B_BYTES = B_END * 4 + 3 * 64 * CW * sizeof(In);
+    constexpr int LDR = 64 + 4;                           // raw inputs of the slice, transposed
+    constexpr size_t B_BYTES = B_END * 4 + 3 * CW * LDR * sizeof(In);
     constexpr size_t REGION = (A_END * sizeof(Op) > B_BYTES ? A_END * sizeof(Op) : B_BYTES);
     __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[256];
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
     float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sdG = fb + B_DG;
     float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
-    In *sqv = (In *)(fb + B_END), *skv = sqv + 64 * CW, *sbv = skv + 64 * CW;
+    In *sqT = (In *)(fb + B_END), *skT = sqT + CW * LDR, *sbT = skT + CW * LDR;
 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
@@ -754,19 +755,25 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     }
 
     // ---- phase B, key channels in slices of CW ----
-    // (software-pipelined like phase A: log alpha, q, k, b of the next slice
-    // load while this one is worked on)
-    constexpr int NBU = 64 * CW / 256;
-    struct BR { float l[NBU]; In q[NBU], k[NBU], b[NBU]; };
+    // Thread t owns channel bcl = t % CW of the slice and the SL consecutive
+    // rows from r0 = SL * (t / CW). Log alpha, q, k, b of the next slice load
+    // while this one is worked on; the cumulative log decay is scanned down
+    // the thread's rows in registers and across the row segments through LDS;
+    // the decay-scaled operands and the raw inputs are written transposed,
+    // four rows per store.
+    constexpr int SL = 64 * CW / 256, NIT = SL / 4;
+    static_assert(256 % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
+    struct alignas(4 * sizeof(In)) In4 { In v[4]; };
+    struct BR { float l[SL]; In q[SL], k[SL], b[SL]; };
+    const int bcl = t % CW, bs = t / CW, r0 = SL * bs;
     auto bload = [&](BR &R_, int cs) {
 #pragma unroll
-        for (int u = 0; u < NBU; ++u) {
-            const int x = t + 256 * u, r = x / CW, cl = x % CW;
-            const size_t o = tok_k(min(r, n - 1)) + cs * CW + cl;
-            R_.l[u] = la[o];
-            R_.q[u] = q[o];
-            R_.k[u] = k[o];
-            R_.b[u] = b[o];
+        for (int i = 0; i < SL; ++i) {
+            const size_t o = tok_k(min(r0 + i, n - 1)) + cs * CW + bcl;
+            R_.l[i] = la[o];
+            R_.q[i] = q[o];
+            R_.k[i] = k[o];
+            R_.b[i] = b[o];
         }
     };
     BR ba, bb2;
@@ -776,36 +783,59 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         const int c0 = cs * CW;
         BR &bc = (cs & 1) ? bb2 : ba;
         BR &bn = (cs & 1) ? ba : bb2;
-        __syncthreads();
+        // (the previous slice's readers of sPart finished inside its reverse
+        // scan, and its readers of the other phase-B regions before that)
+        float gl[SL], tot = 0.f;
 #pragma unroll
-        for (int u = 0; u < NBU; ++u) {
-            const int x = t + 256 * u, r = x / CW, cl = x % CW;
-            sg[r * LDC + cl] = r < n ? bc.l[u] : 0.f;
+        for (int i = 0; i < SL; ++i) {
+            gl[i] = r0 + i < n ? bc.l[i] : 0.f;
+            tot += gl[i];
         }
+        sPart[bs * CW + bcl] = tot;
         if (cs + 1 < NCS) bload(bn, cs + 1);
         __syncthreads();
-        col_scan64<CW, false>(sg, LDC, sPart, t);
-        static_assert((64 * CW) % 256 == 0, "whole rounds of the workgroup");
+        {
+            float acc = 0.f;
+            for (int s2 = 0; s2 < bs; ++s2) acc += sPart[s2 * CW + bcl];
 #pragma unroll
-        for (int u = 0; u < 64 * CW / 256; ++u) {
-            const int x = t + 256 * u;
-            const int r = x / CW, cl = x % CW, c = c0 + cl, R = r >> 4;
-            const bool ok = r < n;
-            const In zero_ = (In)0;
-            const In kr_ = ok ? bc.k[u] : zero_, qr_ = ok ? bc.q[u] : zero_, br_ = ok ? bc.b[u] : zero_;
-            const float kv = in2f<In>(kr_), qv = in2f<In>(qr_), bv = in2f<In>(br_);
-            const float gv = sg[r * LDC + cl];
-            const float e1 = __expf(sRef[(R + 1) * DK + c] - gv), em = __expf(sMid[R * DK + c] - gv);
-            const float e2 = __expf(gv - sRef[R * DK + c]), en = __expf(gv - sMid[R * DK + c]);
-            XtT[cl * LDF + r] = kv * e1;
-            XmT[cl * LDF + r] = kv * em;
-            BtT[cl * LDF + r] = bv * kv * e2;   // row side of (dA o Dec)^T (b k), like q
-            BmT[cl * LDF + r] = bv * kv * en;
-            QtT[cl * LDF + r] = qv * e2;
-            QmT[cl * LDF + r] = qv * en;
-            sqv[r * CW + cl] = qr_;
-            skv[r * CW + cl] = kr_;
-            sbv[r * CW + cl] = br_;
+            for (int i = 0; i < SL; ++i) { acc += gl[i]; gl[i] = acc; }
+        }
+        const In zero_ = (In)0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int rb = r0 + 4 * it, R = rb >> 4, c = c0 + bcl;
+            const float rf1 = sRef[(R + 1) * DK + c], rf0 = sRef[R * DK + c], md = sMid[R * DK + c];
+            f4 xt, xm, bt, bm, qt, qm;
+            In4 q4, k4, b4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * it + e;
+                const bool ok = rb + e < n;
+                const In kr_ = ok ? bc.k[i] : zero_, qr_ = ok ? bc.q[i] : zero_, br_ = ok ? bc.b[i] : zero_;
+                const float kv = in2f<In>(kr_), qv = in2f<In>(qr_), bv = in2f<In>(br_);
+                const float gv = gl[i];
+                sg[(rb + e) * LDC + bcl] = gv;
+                const float e1 = __expf(rf1 - gv), em = __expf(md - gv);
+                const float e2 = __expf(gv - rf0), en = __expf(gv - md);
+                xt[e] = kv * e1;
+                xm[e] = kv * em;
+                bt[e] = bv * kv * e2;   // row side of (dA o Dec)^T (b k), like q
+                bm[e] = bv * kv * en;
+                qt[e] = qv * e2;
+                qm[e] = qv * en;
+                q4.v[e] = qr_;
+                k4.v[e] = kr_;
+                b4.v[e] = br_;
+            }
+            *reinterpret_cast<f4 *>(XtT + bcl * LDF + rb) = xt;
+            *reinterpret_cast<f4 *>(XmT + bcl * LDF + rb) = xm;
+            *reinterpret_cast<f4 *>(BtT + bcl * LDF + rb) = bt;
+            *reinterpret_cast<f4 *>(BmT + bcl * LDF + rb) = bm;
+            *reinterpret_cast<f4 *>(QtT + bcl * LDF + rb) = qt;
+            *reinterpret_cast<f4 *>(QmT + bcl * LDF + rb) = qm;
+            *reinterpret_cast<In4 *>(sqT + bcl * LDR + rb) = q4;
+            *reinterpret_cast<In4 *>(skT + bcl * LDR + rb) = k4;
+            *reinterpret_cast<In4 *>(sbT + bcl * LDR + rb) = b4;
         }
         __syncthreads();
         const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
@@ -886,11 +916,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             }
             const float gn = sRef[4 * DK + c];
             float khk = 0.f;
+            const In4 q4 = *reinterpret_cast<const In4 *>(sqT + cl * LDR + 16 * R + 4 * g4);
+            const In4 k4 = *reinterpret_cast<const In4 *>(skT + cl * LDR + 16 * R + 4 * g4);
+            const In4 b4 = *reinterpret_cast<const In4 *>(sbT + cl * LDR + 16 * R + 4 * g4);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * R + 4 * g4 + ii;
-                const float gv = sg[r * LDC + cl], eg = __expf(gv), egn = __expf(gn - gv);
-                const float qv = in2f<In>(sqv[r * CW + cl]), kv = in2f<In>(skv[r * CW + cl]), bv = in2f<In>(sbv[r * CW + cl]);
+                const float gv = gR[ii], eg = __expf(gv), egn = __expf(gn - gv);
+                const float qv = in2f<In>(q4.v[ii]), kv = in2f<In>(k4.v[ii]), bv = in2f<In>(b4.v[ii]);
                 const float dqv = F1[ctg][ii] * eg + Y1[ii];
                 const float dEe = -F2[ctg][ii] * eg + Y2[ii];
                 const float dkm = Z1[ii] + Z2[ii];
