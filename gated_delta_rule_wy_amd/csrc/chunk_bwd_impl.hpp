@@ -839,81 +839,72 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         }
         __syncthreads();
         const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
+        // Y1 = (dP o Dec) x, Y2 = (dA o Dec) x for the rows of block R and
+        // Z = (dP o Dec)^T q + (dA o Dec)^T (b k) for the rows s of block R,
+        // for all CWT channel tiles of the slice at once: the left operands
+        // (rows or columns of dP and dA) are shared by the tiles, the decay
+        // factors by the paired products
+        float gR[CWT][4], midR[CWT];
+        f4 Y1[CWT], Y2[CWT], Z[CWT];
+#pragma unroll
+        for (int ct = 0; ct < CWT; ++ct) {
+            const int cl = 16 * ct + m16;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) gR[ct][ii] = sg[(16 * R + 4 * g4 + ii) * LDC + cl];
+            midR[ct] = sMid[R * DK + c0 + cl];
+            Y1[ct] = f4zero();
+            Y2[ct] = f4zero();
+            Z[ct] = f4zero();
+        }
+        // row side: off-diagonal blocks S < R through ref_{S+1}, then the
+        // diagonal block around its middle row
+        for (int S = 0; S <= R; ++S) {
+            const bool dg = S == R;
+            const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * S + 4 * g4);
+            const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * S + 4 * g4);
+            const float *X = dg ? XmT : XtT;
+#pragma unroll
+            for (int ct = 0; ct < CWT; ++ct) {
+                const int cl = 16 * ct + m16;
+                const f4 bx = *reinterpret_cast<const f4 *>(X + cl * LDF + 16 * S + 4 * g4);
+                const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
+                const float ref = dg ? midR[ct] : sRef[(S + 1) * DK + c0 + cl];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(gR[ct][ii] - ref);
+                    Y1[ct][ii] += p1[ii] * f;
+                    Y2[ct][ii] += p2[ii] * f;
+                }
+            }
+        }
+        // column side: the diagonal block around its middle row, then the
+        // off-diagonal blocks Rb > R through ref_Rb
+        for (int Rb = R; Rb < 4; ++Rb) {
+            const bool dg = Rb == R;
+            f4 a1, a2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a1[e] = sdP[(16 * Rb + 4 * g4 + e) * LDF + 16 * R + m16];
+                a2[e] = sdA[(16 * Rb + 4 * g4 + e) * LDF + 16 * R + m16];
+            }
+            const float *Q_ = dg ? QmT : QtT, *B_ = dg ? BmT : BtT;
+#pragma unroll
+            for (int ct = 0; ct < CWT; ++ct) {
+                const int cl = 16 * ct + m16;
+                const f4 b1 = *reinterpret_cast<const f4 *>(Q_ + cl * LDF + 16 * Rb + 4 * g4);
+                const f4 b2 = *reinterpret_cast<const f4 *>(B_ + cl * LDF + 16 * Rb + 4 * g4);
+                const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
+                const float ref = dg ? midR[ct] : sRef[Rb * DK + c0 + cl];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float f = __expf(ref - gR[ct][ii]);
+                    Z[ct][ii] += p1[ii] * f + p2[ii] * f;
+                }
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < CWT; ++ct) {
             const int cl = 16 * ct + m16, c = c0 + cl, ctg = cs * CWT + ct;
-            // g of the lane's four rows of block R (rows r for Y, rows s for Z)
-            float gR[4];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) gR[ii] = sg[(16 * R + 4 * g4 + ii) * LDC + cl];
-            const float midR = sMid[R * DK + c];
-            // Y1 = (dP o Dec) x and Y2 = (dA o Dec) x for rows of block R, in
-            // one loop: the two products share the right operand and the decay
-            // factors, and give the wave two independent chains
-            f4 Y1 = f4zero(), Y2 = f4zero();
-            for (int S = 0; S < R; ++S) {
-                const f4 bx = *reinterpret_cast<const f4 *>(XtT + cl * LDF + 16 * S + 4 * g4);
-                const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * S + 4 * g4);
-                const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * S + 4 * g4);
-                const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
-                const float ref = sRef[(S + 1) * DK + c];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const float f = __expf(gR[ii] - ref);
-                    Y1[ii] += p1[ii] * f;
-                    Y2[ii] += p2[ii] * f;
-                }
-            }
-            {
-                const f4 bx = *reinterpret_cast<const f4 *>(XmT + cl * LDF + 16 * R + 4 * g4);
-                const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * R + 4 * g4);
-                const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * R + 4 * g4);
-                const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const float f = __expf(gR[ii] - midR);
-                    Y1[ii] += p1[ii] * f;
-                    Y2[ii] += p2[ii] * f;
-                }
-            }
-            // Z1 = (dP o Dec)^T q and Z2 = (dA o Dec)^T (b k) for rows s of
-            // block S = R, in one loop with shared decay factors
-            f4 Z1 = f4zero(), Z2 = f4zero();
-            for (int Rr = R + 1; Rr < 4; ++Rr) {
-                f4 a1, a2;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a1[e] = sdP[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
-                    a2[e] = sdA[(16 * Rr + 4 * g4 + e) * LDF + 16 * R + m16];
-                }
-                const f4 b1 = *reinterpret_cast<const f4 *>(QtT + cl * LDF + 16 * Rr + 4 * g4);
-                const f4 b2 = *reinterpret_cast<const f4 *>(BtT + cl * LDF + 16 * Rr + 4 * g4);
-                const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
-                const float ref = sRef[Rr * DK + c];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const float f = __expf(ref - gR[ii]);
-                    Z1[ii] += p1[ii] * f;
-                    Z2[ii] += p2[ii] * f;
-                }
-            }
-            {
-                f4 a1, a2;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a1[e] = sdP[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
-                    a2[e] = sdA[(16 * R + 4 * g4 + e) * LDF + 16 * R + m16];
-                }
-                const f4 b1 = *reinterpret_cast<const f4 *>(QmT + cl * LDF + 16 * R + 4 * g4);
-                const f4 b2 = *reinterpret_cast<const f4 *>(BmT + cl * LDF + 16 * R + 4 * g4);
-                const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const float f = __expf(midR - gR[ii]);
-                    Z1[ii] += p1[ii] * f;
-                    Z2[ii] += p2[ii] * f;
-                }
-            }
             const float gn = sRef[4 * DK + c];
             float khk = 0.f;
             const In4 q4 = *reinterpret_cast<const In4 *>(sqT + cl * LDR + 16 * R + 4 * g4);
@@ -922,11 +913,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * R + 4 * g4 + ii;
-                const float gv = gR[ii], eg = __expf(gv), egn = __expf(gn - gv);
+                const float gv = gR[ct][ii], eg = __expf(gv), egn = __expf(gn - gv);
                 const float qv = in2f<In>(q4.v[ii]), kv = in2f<In>(k4.v[ii]), bv = in2f<In>(b4.v[ii]);
-                const float dqv = F1[ctg][ii] * eg + Y1[ii];
-                const float dEe = -F2[ctg][ii] * eg + Y2[ii];
-                const float dkm = Z1[ii] + Z2[ii];
+                const float dqv = F1[ctg][ii] * eg + Y1[ct][ii];
+                const float dEe = -F2[ctg][ii] * eg + Y2[ct][ii];
+                const float dkm = Z[ct][ii];
                 const float dkh = F3[ctg][ii] * egn;
                 const float dkv = dkm + dkh + dEe * bv;
                 const float dbv = dEe * kv;
