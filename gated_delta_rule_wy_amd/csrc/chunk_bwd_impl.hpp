@@ -740,6 +740,24 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         if (t < DK)
             for (int jj = 0; jj < VS; ++jj) gam += (float)Gr[t * LDV + jj] * (float)Sj[t * LDV + jj];
     }
+    // the first phase-B slice's inputs load while phase A finishes
+    constexpr int SL = 64 * CW / 256, NIT = SL / 4;
+    static_assert(256 % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
+    struct alignas(4 * sizeof(In)) In4 { In v[4]; };
+    struct BR { float l[SL]; In q[SL], k[SL], b[SL]; };
+    const int bcl = t % CW, bs = t / CW, r0 = SL * bs;
+    auto bload = [&](BR &R_, int cs) {
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+            const size_t o = tok_k(min(r0 + i, n - 1)) + cs * CW + bcl;
+            R_.l[i] = la[o];
+            R_.q[i] = q[o];
+            R_.k[i] = k[o];
+            R_.b[i] = b[o];
+        }
+    };
+    BR ba, bb2;
+    bload(ba, 0);
     __syncthreads();   // phase A's LDS is free from here
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -761,23 +779,6 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     // the thread's rows in registers and across the row segments through LDS;
     // the decay-scaled operands and the raw inputs are written transposed,
     // four rows per store.
-    constexpr int SL = 64 * CW / 256, NIT = SL / 4;
-    static_assert(256 % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
-    struct alignas(4 * sizeof(In)) In4 { In v[4]; };
-    struct BR { float l[SL]; In q[SL], k[SL], b[SL]; };
-    const int bcl = t % CW, bs = t / CW, r0 = SL * bs;
-    auto bload = [&](BR &R_, int cs) {
-#pragma unroll
-        for (int i = 0; i < SL; ++i) {
-            const size_t o = tok_k(min(r0 + i, n - 1)) + cs * CW + bcl;
-            R_.l[i] = la[o];
-            R_.q[i] = q[o];
-            R_.k[i] = k[o];
-            R_.b[i] = b[o];
-        }
-    };
-    BR ba, bb2;
-    bload(ba, 0);
 #pragma unroll
     for (int cs = 0; cs < NCS; ++cs) {
         const int c0 = cs * CW;
