@@ -406,11 +406,11 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
 // LDS tile with row stride ld, by all 256 threads of the workgroup: thread t
 // takes column t % NCOL and one segment of rows; segment totals pass through
 // `part` (256 floats). Contains two barriers.
-template <int NCOL, bool REV>
+template <int NCOL, bool REV, int NT>
 __device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int t)
 {
-    constexpr int SEGS = 256 / NCOL, SL = 64 / SEGS;
-    static_assert(SEGS * NCOL == 256 && SEGS * SL == 64, "256 threads over 64 rows");
+    constexpr int SEGS = NT / NCOL, SL = 64 / SEGS;
+    static_assert(SEGS * NCOL == NT && SEGS * SL == 64, "NT threads over 64 rows");
     const int c = t % NCOL, sg = t / NCOL;
     const int r0 = REV ? 64 - SL * (sg + 1) : SL * sg;
     float x[SL], tot = 0.f;
@@ -431,7 +431,9 @@ __device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int 
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk gradients, one workgroup (4 waves) per (chunk, head), from the
+// Per-chunk gradients, one workgroup per (chunk, head) of one or two halves
+// of 4 waves (wave w & 3 owns the 16-row block; with two halves each takes
+// every other work unit of a step, so that two waves share a SIMD), from the
 // forward's chunk start state S_c and Delta, the reverse pass's end gradient
 // G, the forward block's P and T, dO and the raw inputs. With g the chunk's
 // cumulative log decay (g_n its last row) and, per channel,
@@ -454,8 +456,17 @@ __device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int 
 // <= 1), diagonal blocks around the block's middle row (bounded in fp32 for
 // log alpha >= -7 per token), then the elementwise gradients and the reverse
 // cumulative sum.
-template <typename In, typename Op, int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_grad_kernel(
+template <typename Op, int DK, int DV> struct GradShape {
+    static constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
+    static constexpr int VT = VS / 16, CT = DK / 16;
+    static constexpr int CW = DK < 32 ? DK : 32;          // key channels per phase-B slice
+    static constexpr int CWT = CW / 16;
+    // two halves of four waves when every step splits evenly between them
+    static constexpr int NT = (VT % 2 == 0 && CT % 2 == 0 && CWT % 2 == 0) ? 512 : 256;
+};
+
+template <typename In, typename Op, int DK, int DV, int NT>
+__global__ __launch_bounds__(NT) void chunk_grad_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v, const float *__restrict__ la,
     const In *__restrict__ b, const In *__restrict__ w, const float *__restrict__ dO, Seqs sq, int H,
     const uint8_t *__restrict__ bops, const Op *__restrict__ sbuf, const Op *__restrict__ dbuf,
@@ -467,11 +478,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     using BL = BBlk<Op, DK>;
     using frag = typename M::frag;
     constexpr int KB = M::KB, NE = M::NE, NKB = BL::NKB, NSB = BL::NSB;
-    constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
-    constexpr int NVS = DV / VS, VT = VS / 16, VKB = VS / KB > 0 ? VS / KB : 1;
-    constexpr int CT = DK / 16;
-    constexpr int CW = DK < 32 ? DK : 32;                 // key channels per phase-B slice
-    constexpr int NCS = DK / CW, CWT = CW / 16;
+    using GS = GradShape<Op, DK, DV>;
+    constexpr int VS = GS::VS, NVS = DV / VS, VT = GS::VT, VKB = VS / KB > 0 ? VS / KB : 1;
+    constexpr int CT = GS::CT, CW = GS::CW, NCS = DK / CW, CWT = GS::CWT;
+    // work units of a step are dealt to the halves of the workgroup in turn:
+    // value tiles vt = hv + HV i, dA/dP column blocks st = STH hv + i, key
+    // channel tiles ct = hv + HV i (in phase B, of the slice)
+    constexpr int HV = NT / 256, VTH = VT / HV, STH = 4 / HV, CTH = CT / HV, CWH = CWT / HV;
+    static_assert(VT % HV == 0 && CT % HV == 0 && CWT % HV == 0, "whole units per half");
     static_assert(VS % KB == 0 || VS < KB, "slice width");
     // LDS: persistent tables, then phase A and phase B regions over the same bytes
     constexpr int VSP = VS < KB ? KB : VS;                // slice width padded to a k-block (zeros)
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     constexpr int LDR = 64 + 4;                           // raw inputs of the slice, transposed
     constexpr size_t B_BYTES = B_END * 4 + 3 * CW * LDR * sizeof(In);
     constexpr size_t REGION = (A_END * sizeof(Op) > B_BYTES ? A_END * sizeof(Op) : B_BYTES);
-    __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[256];
+    __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[NT];
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
     Op *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
@@ -504,7 +518,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
     In *sqT = (In *)(fb + B_END), *skT = sqT + CW * LDR, *sbT = skT + CW * LDR;
 
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wv = (t >> 6) & 3, hv = t >> 8, m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
     const int i = sq.m.seq_of(j);
@@ -522,21 +536,21 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     {
         constexpr int LDL = DK + 1;
         static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
-        constexpr int NU = 64 * DK / 256;
+        constexpr int NU = 64 * DK / NT;
         float lv[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int x = t + 256 * u, r = x / DK, c = x % DK;
+            const int x = t + NT * u, r = x / DK, c = x % DK;
             lv[u] = la[tok_k(min(r, n - 1)) + c];
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int x = t + 256 * u, r = x / DK, c = x % DK;
+            const int x = t + NT * u, r = x / DK, c = x % DK;
             fb[r * LDL + c] = r < n ? lv[u] : 0.f;
         }
         __syncthreads();
-        col_scan64<DK, false>(fb, LDL, sPart, t);
-        for (int c = t; c < DK; c += 256) {
+        col_scan64<DK, false, NT>(fb, LDL, sPart, t);
+        for (int c = t; c < DK; c += NT) {
             sRef[c] = 0.f;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
@@ -559,12 +573,12 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     for (int kb = 0; kb < NKB; ++kb)
         KHf[kb] = *reinterpret_cast<const frag *>(bblk + BL::oKH + ((size_t)(wv * NKB + kb) * 64 + lane) * 16);
     if constexpr (VSP > VS) {   // padding columns of the slice tiles stay zero
-        for (int x = t; x < DK * (VSP - VS); x += 256) {
+        for (int x = t; x < DK * (VSP - VS); x += NT) {
             const int c = x / (VSP - VS), jj = VS + x % (VSP - VS);
             Gr[c * LDV + jj] = (Op)0.f;
             Sj[c * LDV + jj] = (Op)0.f;
         }
-        for (int x = t; x < 64 * (VSP - VS); x += 256) {
+        for (int x = t; x < 64 * (VSP - VS); x += NT) {
             const int r = x / (VSP - VS), jj = VS + x % (VSP - VS);
             Dj[r * LDV + jj] = (Op)0.f;
             Oj[r * LDV + jj] = (Op)0.f;
@@ -572,11 +586,11 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)0.f;
         }
     }
-    f4 accA[4], accP[4], F1[CT], F2[CT], F3[CT];
+    f4 accA[STH], accP[STH], F1[CTH], F2[CTH], F3[CTH];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
+    for (int x = 0; x < STH; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
 #pragma unroll
-    for (int x = 0; x < CT; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
+    for (int x = 0; x < CTH; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
     float gam = 0.f;
     // value-column slices, software-pipelined: the next slice's loads (G,
     // S_c, Delta, dO, and v, w for dv and dw) are issued before this slice's
@@ -585,21 +599,21 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     // (rt * DV/16 + ct) * 256; lane l = n + 16g holds rows 4g..4g+3 of
     // column n): one 4-element load per lane and tile
     typedef Op op4 __attribute__((ext_vector_type(4)));
-    constexpr int NG = (DK * VS / 4 + 255) / 256, ND = (64 * VS / 4 + 255) / 256;
+    constexpr int NG = (DK * VS / 4 + NT - 1) / NT, ND = (64 * VS / 4 + NT - 1) / NT;
     static_assert((DK * VS / 4) % 64 == 0 && (64 * VS / 4) % 64 == 0, "whole tiles");
     // x = tile * 64 + lane over the slice's tiles (row tile major)
     auto tile_at = [&](int x, int &rt, int &ctl, int &ln) { ln = x & 63; rt = (x >> 6) / VT; ctl = (x >> 6) % VT; };
     struct SR {
         op4 g[NG], s[NG], d[ND];
         f4 o[ND];
-        In vv[VT][4], ww[VT][4];
+        In vv[VTH][4], ww[VTH][4];
     };
     auto sload = [&](SR &R_, int vs) {
         const int j0 = vs * VS;
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
             int rt, ctl, ln;
-            tile_at(min(t + 256 * u, DK * VS / 4 - 1), rt, ctl, ln);
+            tile_at(min(t + NT * u, DK * VS / 4 - 1), rt, ctl, ln);
             const size_t o = ((size_t)rt * (DV / 16) + j0 / 16 + ctl) * 256 + ln * 4;
             R_.g[u] = *reinterpret_cast<const op4 *>(Gp + o);
             R_.s[u] = *reinterpret_cast<const op4 *>(Sc + o);
@@ -607,24 +621,24 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
 #pragma unroll
         for (int u = 0; u < ND; ++u) {
             int rt, ctl, ln;
-            tile_at(min(t + 256 * u, 64 * VS / 4 - 1), rt, ctl, ln);
+            tile_at(min(t + NT * u, 64 * VS / 4 - 1), rt, ctl, ln);
             R_.d[u] = *reinterpret_cast<const op4 *>(Dl + ((size_t)rt * (DV / 16) + j0 / 16 + ctl) * 256 + ln * 4);
-            const int x = min(t + 256 * u, 64 * VS / 4 - 1), r = x / (VS / 4), jj = 4 * (x % (VS / 4));
+            const int x = min(t + NT * u, 64 * VS / 4 - 1), r = x / (VS / 4), jj = 4 * (x % (VS / 4));
             R_.o[u] = *reinterpret_cast<const f4 *>(dO + tok_v(min(r, n - 1)) + j0 + jj);
         }
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
+        for (int i = 0; i < VTH; ++i)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const size_t o = tok_v(min(16 * wv + 4 * g4 + ii, n - 1)) + j0 + 16 * vt + m16;
-                R_.vv[vt][ii] = v[o];
-                R_.ww[vt][ii] = w[o];
+                const size_t o = tok_v(min(16 * wv + 4 * g4 + ii, n - 1)) + j0 + 16 * (hv + HV * i) + m16;
+                R_.vv[i][ii] = v[o];
+                R_.ww[i][ii] = w[o];
             }
     };
     auto sstore = [&](const SR &R_) {
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
-            const int x = t + 256 * u;
+            const int x = t + NT * u;
             if (x >= DK * VS / 4) break;
             int rt, ctl, ln;
             tile_at(x, rt, ctl, ln);
@@ -639,7 +653,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         }
 #pragma unroll
         for (int u = 0; u < ND; ++u) {
-            const int x = t + 256 * u;
+            const int x = t + NT * u;
             if (x >= 64 * VS / 4) break;
             int rt, ctl, ln;
             tile_at(x, rt, ctl, ln);
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         }
 #pragma unroll
         for (int u = 0; u < ND * 4; ++u) {
-            const int x = t + 256 * (u / 4), r = x / (VS / 4), jj = 4 * (x % (VS / 4)) + (u % 4);
+            const int x = t + NT * (u / 4), r = x / (VS / 4), jj = 4 * (x % (VS / 4)) + (u % 4);
             if (x >= 64 * VS / 4) break;
             const float of = r < n ? R_.o[u / 4][u % 4] : 0.f;
             const Op o = (Op)of;
@@ -670,7 +684,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         __syncthreads();
         // dDelta row tile wv: P^T dO + Khat G
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
+        for (int i = 0; i < VTH; ++i) {
+            const int vt = hv + HV * i;
             f4 acc = f4zero();
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
@@ -691,7 +706,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         __syncthreads();
         // dX row tile wv: T^T dDelta; dv, dw
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
+        for (int i = 0; i < VTH; ++i) {
+            const int vt = hv + HV * i;
             f4 acc = f4zero();
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
@@ -707,8 +723,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
                 if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)(acc[ii] - (float)hi);
                 if (r < n) {
                     const size_t o = tok_v(r) + j0 + jj;
-                    dv_[o] = acc[ii] * in2f<In>(cur.ww[vt][ii]);
-                    dw[o] = acc[ii] * in2f<In>(cur.vv[vt][ii]);
+                    dv_[o] = acc[ii] * in2f<In>(cur.ww[i][ii]);
+                    dw[o] = acc[ii] * in2f<In>(cur.vv[i][ii]);
                 }
             }
         }
@@ -721,28 +737,30 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             const frag ao = lds_row_frag<Op>(Oj + (16 * wv + m16) * LDV, kb * KB, g4);
             const frag ad = lds_row_frag<Op>(Dj + (16 * wv + m16) * LDV, kb * KB, g4);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int i = 0; i < STH; ++i) {
+                const int st = STH * hv + i;
                 const frag bd = lds_row_frag<Op>(Dj + (16 * st + m16) * LDV, kb * KB, g4);
-                accA[st] = M::mma(ax, bd, accA[st]);
-                if constexpr (SPLIT) accA[st] = M::mma(axl, bd, accA[st]);
-                accP[st] = M::mma(ao, bd, accP[st]);
+                accA[i] = M::mma(ax, bd, accA[i]);
+                if constexpr (SPLIT) accA[i] = M::mma(axl, bd, accA[i]);
+                accP[i] = M::mma(ao, bd, accP[i]);
             }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
+            for (int i = 0; i < CTH; ++i) {
+                const int ct = hv + HV * i;
                 const frag bs = lds_row_frag<Op>(Sj + (16 * ct + m16) * LDV, kb * KB, g4);
                 const frag bg = lds_row_frag<Op>(Gr + (16 * ct + m16) * LDV, kb * KB, g4);
-                F1[ct] = M::mma(ao, bs, F1[ct]);
-                F2[ct] = M::mma(ax, bs, F2[ct]);
-                if constexpr (SPLIT) F2[ct] = M::mma(axl, bs, F2[ct]);
-                F3[ct] = M::mma(ad, bg, F3[ct]);
+                F1[i] = M::mma(ao, bs, F1[i]);
+                F2[i] = M::mma(ax, bs, F2[i]);
+                if constexpr (SPLIT) F2[i] = M::mma(axl, bs, F2[i]);
+                F3[i] = M::mma(ad, bg, F3[i]);
             }
         }
         if (t < DK)
             for (int jj = 0; jj < VS; ++jj) gam += (float)Gr[t * LDV + jj] * (float)Sj[t * LDV + jj];
     }
     // the first phase-B slice's inputs load while phase A finishes
-    constexpr int SL = 64 * CW / 256, NIT = SL / 4;
-    static_assert(256 % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
+    constexpr int SL = 64 * CW / NT, NIT = SL / 4;
+    static_assert(NT % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
     struct alignas(4 * sizeof(In)) In4 { In v[4]; };
     struct BR { float l[SL]; In q[SL], k[SL], b[SL]; };
     const int bcl = t % CW, bs = t / CW, r0 = SL * bs;
@@ -760,12 +778,12 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
     bload(ba, 0);
     __syncthreads();   // phase A's LDS is free from here
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int i = 0; i < STH; ++i)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int r = 16 * wv + 4 * g4 + ii, s_ = 16 * st + m16;
-            sdA[r * LDF + s_] = r > s_ ? -accA[st][ii] : 0.f;
-            sdP[r * LDF + s_] = r >= s_ ? accP[st][ii] : 0.f;
+            const int r = 16 * wv + 4 * g4 + ii, s_ = 16 * (STH * hv + i) + m16;
+            sdA[r * LDF + s_] = r > s_ ? -accA[i][ii] : 0.f;
+            sdP[r * LDF + s_] = r >= s_ ? accP[i][ii] : 0.f;
         }
     if (t < DK) {
         sGam[t] = gam * __expf(sRef[4 * DK + t]);
@@ -842,14 +860,14 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
         const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
         // Y1 = (dP o Dec) x, Y2 = (dA o Dec) x for the rows of block R and
         // Z = (dP o Dec)^T q + (dA o Dec)^T (b k) for the rows s of block R,
-        // for all CWT channel tiles of the slice at once: the left operands
-        // (rows or columns of dP and dA) are shared by the tiles, the decay
-        // factors by the paired products
-        float gR[CWT][4], midR[CWT];
-        f4 Y1[CWT], Y2[CWT], Z[CWT];
+        // for the half's channel tiles ct = hv + HV j of the slice at once:
+        // the left operands (rows or columns of dP and dA) are shared by the
+        // tiles, the decay factors by the paired products
+        float gR[CWH][4], midR[CWH];
+        f4 Y1[CWH], Y2[CWH], Z[CWH];
 #pragma unroll
-        for (int ct = 0; ct < CWT; ++ct) {
-            const int cl = 16 * ct + m16;
+        for (int ct = 0; ct < CWH; ++ct) {
+            const int cl = 16 * (hv + HV * ct) + m16;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) gR[ct][ii] = sg[(16 * R + 4 * g4 + ii) * LDC + cl];
             midR[ct] = sMid[R * DK + c0 + cl];
@@ -865,8 +883,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * S + 4 * g4);
             const float *X = dg ? XmT : XtT;
 #pragma unroll
-            for (int ct = 0; ct < CWT; ++ct) {
-                const int cl = 16 * ct + m16;
+            for (int ct = 0; ct < CWH; ++ct) {
+                const int cl = 16 * (hv + HV * ct) + m16;
                 const f4 bx = *reinterpret_cast<const f4 *>(X + cl * LDF + 16 * S + 4 * g4);
                 const f4 p1 = MF::mma(a1, bx, f4zero()), p2 = MF::mma(a2, bx, f4zero());
                 const float ref = dg ? midR[ct] : sRef[(S + 1) * DK + c0 + cl];
@@ -890,8 +908,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             }
             const float *Q_ = dg ? QmT : QtT, *B_ = dg ? BmT : BtT;
 #pragma unroll
-            for (int ct = 0; ct < CWT; ++ct) {
-                const int cl = 16 * ct + m16;
+            for (int ct = 0; ct < CWH; ++ct) {
+                const int cl = 16 * (hv + HV * ct) + m16;
                 const f4 b1 = *reinterpret_cast<const f4 *>(Q_ + cl * LDF + 16 * Rb + 4 * g4);
                 const f4 b2 = *reinterpret_cast<const f4 *>(B_ + cl * LDF + 16 * Rb + 4 * g4);
                 const f4 p1 = MF::mma(a1, b1, f4zero()), p2 = MF::mma(a2, b2, f4zero());
@@ -904,8 +922,10 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             }
         }
 #pragma unroll
-        for (int ct = 0; ct < CWT; ++ct) {
-            const int cl = 16 * ct + m16, c = c0 + cl, ctg = cs * CWT + ct;
+        for (int ct = 0; ct < CWH; ++ct) {
+            // (F1..F3 hold the half's key channel tiles hv + HV i; this one is
+            // tile cs CWT + hv + HV ct of the head)
+            const int cl = 16 * (hv + HV * ct) + m16, c = c0 + cl, ctg = cs * CWH + ct;
             const float gn = sRef[4 * DK + c];
             float khk = 0.f;
             const In4 q4 = *reinterpret_cast<const In4 *>(sqT + cl * LDR + 16 * R + 4 * g4);
@@ -934,10 +954,10 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(
             atomicAdd(&sKhK[c], khk);
         }
         __syncthreads();
-        col_scan64<CW, true>(sdG, LDC, sPart, t);
+        col_scan64<CW, true, NT>(sdG, LDC, sPart, t);
 #pragma unroll
-        for (int u = 0; u < 64 * CW / 256; ++u) {
-            const int x = t + 256 * u, r = x / CW, cl = x % CW, c = c0 + cl;
+        for (int u = 0; u < 64 * CW / NT; ++u) {
+            const int x = t + NT * u, r = x / CW, cl = x % CW, c = c0 + cl;
             if (r < n) dla[tok_k(r) + c] = sdG[r * LDC + cl] + sKhK[c] + sGam[c];
         }
     }
@@ -1006,8 +1026,9 @@ static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (bp.fwd.max_chunks > 0) {
         prof_before("gdn2_chunk_grad", st);
-        hipLaunchKernelGGL((chunk_grad_kernel<In, Op, DK, DV>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
-                           dim3(256), 0, st, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
+        constexpr int NTG = GradShape<Op, DK, DV>::NT;
+        hipLaunchKernelGGL((chunk_grad_kernel<In, Op, DK, DV, NTG>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
+                           dim3(NTG), 0, st, (const In *)a.q, (const In *)a.k, (const In *)a.v, a.log_alpha,
                            (const In *)a.b, (const In *)a.w, a.dO, sq, a.H, (const uint8_t *)bops,
                            (const Op *)(ws + bp.off_states),
                            (const Op *)(ws + bp.off_delta), (const Op *)gbuf, a.dq, a.dk_, a.dv_, a.dlog_alpha, a.db,
