@@ -530,38 +530,18 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     auto tok_k = [&](int r) { return ((size_t)(t0 + r) * H + h) * DK; };
     auto tok_v = [&](int r) { return ((size_t)(t0 + r) * H + h) * DV; };
 
-    // ---- phase 0: references of the 16-row blocks, per channel ----
-    // (log alpha staged through LDS with coalesced loads; the running sums
-    // then read LDS, not memory)
-    {
-        constexpr int LDL = DK + 1;
-        static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
-        constexpr int NU = 64 * DK / NT;
-        float lv[NU];
+    // log alpha of the chunk for phase 0, then (arriving during phase 0)
+    // this wave's fragments of the forward block and the first value
+    // slice's inputs
+    constexpr int LDL = DK + 1;
+    static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
+    constexpr int NU = 64 * DK / NT;
+    float lv[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int x = t + NT * u, r = x / DK, c = x % DK;
-            lv[u] = la[tok_k(min(r, n - 1)) + c];
-        }
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int x = t + NT * u, r = x / DK, c = x % DK;
-            fb[r * LDL + c] = r < n ? lv[u] : 0.f;
-        }
-        __syncthreads();
-        col_scan64<DK, false, NT>(fb, LDL, sPart, t);
-        for (int c = t; c < DK; c += NT) {
-            sRef[c] = 0.f;
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                sRef[(R + 1) * DK + c] = fb[(16 * R + 15) * LDL + c];
-                sMid[R * DK + c] = fb[(16 * R + 7) * LDL + c];
-            }
-        }
-        __syncthreads();
+    for (int u = 0; u < NU; ++u) {
+        const int x = t + NT * u, r = x / DK, c = x % DK;
+        lv[u] = la[tok_k(min(r, n - 1)) + c];
     }
-
-    // ---- phase A ----
     // A-fragments of this wave's 16 chunk rows of P^T, T^T and Khat
     frag PTf[NSB], TTf[NSB], KHf[NKB];
 #pragma unroll
@@ -572,26 +552,6 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
         KHf[kb] = *reinterpret_cast<const frag *>(bblk + BL::oKH + ((size_t)(wv * NKB + kb) * 64 + lane) * 16);
-    if constexpr (VSP > VS) {   // padding columns of the slice tiles stay zero
-        for (int x = t; x < DK * (VSP - VS); x += NT) {
-            const int c = x / (VSP - VS), jj = VS + x % (VSP - VS);
-            Gr[c * LDV + jj] = (Op)0.f;
-            Sj[c * LDV + jj] = (Op)0.f;
-        }
-        for (int x = t; x < 64 * (VSP - VS); x += NT) {
-            const int r = x / (VSP - VS), jj = VS + x % (VSP - VS);
-            Dj[r * LDV + jj] = (Op)0.f;
-            Oj[r * LDV + jj] = (Op)0.f;
-            Xj[r * LDV + jj] = (Op)0.f;
-            if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)0.f;
-        }
-    }
-    f4 accA[STH], accP[STH], F1[CTH], F2[CTH], F3[CTH];
-#pragma unroll
-    for (int x = 0; x < STH; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
-#pragma unroll
-    for (int x = 0; x < CTH; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
-    float gam = 0.f;
     // value-column slices, software-pipelined: the next slice's loads (G,
     // S_c, Delta, dO, and v, w for dv and dw) are issued before this slice's
     // work, into a second set of registers
@@ -635,6 +595,52 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                 R_.ww[i][ii] = w[o];
             }
     };
+    SR ra, rb;
+    sload(ra, 0);
+
+    // ---- phase 0: references of the 16-row blocks, per channel ----
+    // (log alpha staged through LDS with coalesced loads; the running sums
+    // then read LDS, not memory)
+    {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int x = t + NT * u, r = x / DK, c = x % DK;
+            fb[r * LDL + c] = r < n ? lv[u] : 0.f;
+        }
+        __syncthreads();
+        col_scan64<DK, false, NT>(fb, LDL, sPart, t);
+        for (int c = t; c < DK; c += NT) {
+            sRef[c] = 0.f;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                sRef[(R + 1) * DK + c] = fb[(16 * R + 15) * LDL + c];
+                sMid[R * DK + c] = fb[(16 * R + 7) * LDL + c];
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- phase A ----
+    if constexpr (VSP > VS) {   // padding columns of the slice tiles stay zero
+        for (int x = t; x < DK * (VSP - VS); x += NT) {
+            const int c = x / (VSP - VS), jj = VS + x % (VSP - VS);
+            Gr[c * LDV + jj] = (Op)0.f;
+            Sj[c * LDV + jj] = (Op)0.f;
+        }
+        for (int x = t; x < 64 * (VSP - VS); x += NT) {
+            const int r = x / (VSP - VS), jj = VS + x % (VSP - VS);
+            Dj[r * LDV + jj] = (Op)0.f;
+            Oj[r * LDV + jj] = (Op)0.f;
+            Xj[r * LDV + jj] = (Op)0.f;
+            if constexpr (SPLIT) Xjl[r * LDV + jj] = (Op)0.f;
+        }
+    }
+    f4 accA[STH], accP[STH], F1[CTH], F2[CTH], F3[CTH];
+#pragma unroll
+    for (int x = 0; x < STH; ++x) { accA[x] = f4zero(); accP[x] = f4zero(); }
+#pragma unroll
+    for (int x = 0; x < CTH; ++x) { F1[x] = f4zero(); F2[x] = f4zero(); F3[x] = f4zero(); }
+    float gam = 0.f;
     auto sstore = [&](const SR &R_) {
 #pragma unroll
         for (int u = 0; u < NG; ++u) {
@@ -671,8 +677,6 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
             if constexpr (SPLIT) OTl[jj * LDP + r] = (Op)(of - (float)o);
         }
     };
-    SR ra, rb;
-    sload(ra, 0);
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs) {
         const int j0 = vs * VS;
