@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     __shared__ __attribute__((aligned(16))) Op sArea[PH1 > PH2 ? PH1 : PH2];
     Op *sWt = sArea, *sQp = sArea + DK * LDW, *sX = sArea + DK * LDW + 64 * LDQ;
 
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
     const uint8_t *blk = ops + ((size_t)h * sq.max_chunks + j) * L::bytes;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
     const int chain = (kq / NSL) * 8 + (Lid & 7);
     if (chain >= sq.m.N * H) return;
     const int i = chain / H, h = chain % H;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     const int col0 = 16 * NC * js;
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
     const int tb = sq.t0(i), te = sq.t1(i);
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
     In *sqT = (In *)(fb + B_END), *skT = sqT + CW * LDR, *sbT = skT + CW * LDR;
 
-    const int t = threadIdx.x, lane = t & 63, wv = (t >> 6) & 3, hv = t >> 8, m16 = lane & 15, g4 = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wv = wave_id() & 3, hv = wave_id() >> 2, m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
     const int i = sq.m.seq_of(j);

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
     // chunks dealt last to first, all heads of a chunk together (as chunk_prep_kernel)
     const int t = threadIdx.x;
     const int h = (int)(blockIdx.x % (unsigned)H), j = sq.max_chunks - 1 - (int)(blockIdx.x / (unsigned)H);
-    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     if (blockIdx.x == 0)
         for (int x = t; x < nprog; x += NT) prog[x] = 0;
     if (j >= min(sq.m.template nchunks<CS>(), sq.max_chunks)) return;

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // to still sit in the last-level cache).
     const int t = threadIdx.x;
     const int h = (int)(blockIdx.x % (unsigned)H), j = sq.max_chunks - 1 - (int)(blockIdx.x / (unsigned)H);
-    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     if (blockIdx.x == 0)
         for (int x = t; x < nprog; x += 256) prog[x] = 0;
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
@@ -863,7 +863,7 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
     const int PL = NL + ((gates & kGateW) ? 1 : 2) * CS * RL;
     constexpr int NW = 8;                                         // waves
     __shared__ uint32_t sSink[NW * 64];
-    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int t = threadIdx.x, wv = wave_id(), lane = t & 63;
     lptr_t scratch = (lptr_t)(sSink + wv * 64);
     auto done = [&]() {
         return __builtin_amdgcn_readfirstlane(
@@ -967,7 +967,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const int i = chain / H, h = chain % H;
 
     const int t = threadIdx.x;
-    const int lane = t & 63, wv = t >> 6, m16 = lane & 15, g4 = lane >> 4;
+    const int lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     const int col0 = 16 * NC * js;            // first value column of the slice
     const size_t sbase = ((size_t)i * H + h) * DK * DV;
     const int tb = sq.t0(i), te = sq.t1(i);

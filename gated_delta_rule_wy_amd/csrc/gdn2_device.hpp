@@ -103,6 +103,13 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ f4 mma16(const f4 &a, const f4 &b, f4 c) { return mma(a, b, c); }
 };
 
+// Index of the calling wave within its workgroup as a scalar (wave-uniform)
+// value. Conditions and loop bounds derived from it then compile to scalar
+// branches, which really skip what they guard: a matrix instruction issued
+// under an empty execution mask still runs, so skipping it by masking lanes
+// alone is not enough.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 // Sum over aligned groups of G lanes (G = 8, 16, 32 or 64), the result in
 // every lane of the group; all 64 lanes must be active. Within rows of 16
 // lanes: DPP swaps (xor 1, xor 2, then the half-row and row mirrors, which
