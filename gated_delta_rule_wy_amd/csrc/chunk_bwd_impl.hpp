@@ -48,7 +48,7 @@ template <typename Op, int DK> struct BBlk {
 // a P A-fragment the B-fragment of P^T. (-W)^T and Q+ go through LDS.
 template <typename Op, int DK>
 __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restrict__ ops, uint8_t *__restrict__ bops,
-                                                          Seqs sq, int H)
+                                                          Seqs sq, int H, int *__restrict__ prog, int nprog)
 {
     using M = Mma<Op>;
     using L = Blk<Op, DK>;
@@ -67,6 +67,8 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
 
     const int t = threadIdx.x, lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
     const int h = (int)(blockIdx.x % (unsigned)H), j = (int)(blockIdx.x / (unsigned)H);
+    if (blockIdx.x == 0)   // progress counters of the reverse pass's prefetch workgroups
+        for (int x = t; x < nprog; x += 256) prog[x] = 0;
     if (j >= min(sq.m.nchunks(), sq.max_chunks)) return;
     const uint8_t *blk = ops + ((size_t)h * sq.max_chunks + j) * L::bytes;
     uint8_t *bb = bops + ((size_t)h * sq.max_chunks + j) * BL::bytes;
@@ -197,6 +199,58 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
 }
 
 // ---------------------------------------------------------------------------
+// L2 prefetch workgroups of the reverse pass, as for the forward pass (see
+// pass_prefetch): wave k of a prefetch workgroup takes steps k, k + 8, ...
+// (step s handles chunk nch - 1 - s), waits while it is more than
+// 3 + kPfWindow steps ahead of the chain's progress counter, skips steps
+// closer than 3, and reads one dword per line of its share of the step's
+// N^T, R^T and gamma and of the chunk's dO rows into an LDS sink. Every loop
+// and wait is bounded; the pass never waits for these workgroups.
+template <typename Op, int DK, int DV>
+__device__ __forceinline__ void rpass_prefetch(const uint8_t *bops0, const float *dO, const int *prog, int chain,
+                                               int h, int H, int pf, int npf, int nch, int tb, int te)
+{
+    using BL = BBlk<Op, DK>;
+    constexpr int NNR = (int)(BL::oPT / 128);         // lines of N^T and R^T
+    constexpr int NGL = (DK * 4 + 127) / 128;         // lines of gamma
+    constexpr int RL = (DV * 4 + 127) / 128;          // lines per dO row (or the one holding it)
+    constexpr int PL = NNR + NGL + 64 * RL;
+    constexpr int NW = 8;
+    __shared__ uint32_t sSink[NW * 64];
+    const int t = threadIdx.x, wv = wave_id(), lane = t & 63;
+    lptr_t scratch = (lptr_t)(sSink + wv * 64);
+    auto done = [&]() {
+        return __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(prog + chain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    };
+    for (int k = wv; k < nch; k += NW) {
+        int d = done();
+        for (int s = 0; k > d + 3 + kPfWindow && s < kPfMaxSleeps; ++s) {
+            __builtin_amdgcn_s_sleep(4);
+            d = done();
+        }
+        while (k < d + 3) k += NW;
+        if (k >= nch) break;
+        const int c = nch - 1 - k;
+        const uint8_t *blk = bops0 + (size_t)c * BL::bytes;
+        for (int l = pf + npf * lane; l < PL; l += npf * 64) {
+            const uint8_t *a;
+            if (l < NNR) {
+                a = blk + (size_t)l * 128;
+            } else if (l < NNR + NGL) {
+                a = blk + BL::oG + (size_t)(l - NNR) * 128;
+            } else {
+                const int x = l - NNR - NGL, row = x / RL, part = x % RL;
+                const int tok = min(tb + 64 * c + row, te - 1);
+                a = reinterpret_cast<const uint8_t *>(dO + ((size_t)tok * H + h) * DV) + part * 128;
+            }
+            __builtin_amdgcn_global_load_lds((gptr_t)a, scratch, 4, 0, 0);
+        }
+    }
+    __syncthreads();   // drains the line reads before the workgroup ends
+}
+
+// ---------------------------------------------------------------------------
 // Reverse state pass. Workgroup = (chain, slice of 16*NC value columns), 8
 // waves: state waves 0..3 hold the gradient G of their key rows (fp32 in
 // registers), loader waves 4..7 stage dO of the next chunk (hi + lo f16, the
@@ -206,7 +260,8 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
 template <typename Op, int DK, int DV, int NC>
 __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restrict__ dO, const float *__restrict__ dST,
                                                           float *__restrict__ dS0, Seqs sq, int H,
-                                                          const uint8_t *__restrict__ bops, Op *__restrict__ gbuf)
+                                                          const uint8_t *__restrict__ bops, Op *__restrict__ gbuf,
+                                                          int *__restrict__ prog, int npf)
 {
     using M = Mma<Op>;
     using BL = BBlk<Op, DK>;
@@ -218,9 +273,11 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
     __shared__ __attribute__((aligned(16))) Op sG[2][NC][NCT * 64 * 4];
     __shared__ __attribute__((aligned(16))) Op sD[2][NC][2 * NSB * 64 * NE];
 
+    // XCD-aware numbering: the slices and prefetch workgroups of chain c sit
+    // on XCD c % 8
     const int Lid = blockIdx.x;
-    const int kq = Lid >> 3, js = kq % NSL;
-    const int chain = (kq / NSL) * 8 + (Lid & 7);
+    const int kq = Lid >> 3, role = kq % (NSL + npf), js = role;
+    const int chain = (kq / (NSL + npf)) * 8 + (Lid & 7);
     if (chain >= sq.m.N * H) return;
     const int i = chain / H, h = chain % H;
     const int t = threadIdx.x, lane = t & 63, wv = wave_id(), m16 = lane & 15, g4 = lane >> 4;
@@ -232,6 +289,11 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
     const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
     // step k handles chunk nch - 1 - k
     auto bblk = [&](int k) { return bops + (slot0 + max(nch - 1 - k, 0)) * BL::bytes; };
+    if (role >= NSL) {
+        rpass_prefetch<Op, DK, DV>(bops + slot0 * BL::bytes, dO, prog, chain, h, H, role - NSL, npf, nch, tb, te);
+        return;
+    }
+    const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
 
     if (wv < 4) {
         __builtin_amdgcn_s_setprio(3);
@@ -312,6 +374,7 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
                 }
             }
             if constexpr (RING) fload(pre, bblk(k + 2));
+            if (report) __hip_atomic_store(prog + chain, k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         };
         int k = 0;
         if constexpr (RING) {
@@ -999,10 +1062,11 @@ static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st
     sq.gates = 0;
     const uint8_t *ops = ws + bp.fwd.plan_bytes + bp.fwd.prog_bytes;
     uint8_t *bops = ws + bp.off_bblocks;
+    int *prog = (int *)(ws + bp.fwd.plan_bytes);
     if (bp.fwd.max_chunks > 0) {
         prof_before("gdn2_chunk_bprep", st);
         hipLaunchKernelGGL((chunk_bprep_kernel<Op, DK>), dim3((unsigned)((long long)bp.fwd.max_chunks * a.H)),
-                           dim3(256), 0, st, ops, bops, sq, a.H);
+                           dim3(256), 0, st, ops, bops, sq, a.H, prog, (int)((long long)a.N * a.H));
         prof_after(st);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -1011,20 +1075,24 @@ static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st
     const long long chains = (long long)a.N * a.H, groups = (chains + 7) / 8;
     constexpr int NSL1 = DV / 16;
     const bool two = NSL1 % 2 == 0 && 8LL * NSL1 * groups > cus;
-    const long long grid = 8LL * (two ? NSL1 / 2 : NSL1) * groups;
+    const int nsl = two ? NSL1 / 2 : NSL1;
+    // prefetch workgroups per chain where the chip has slots to spare, as for the forward pass
+    const int npfc = (int)std::min<long long>(kMaxPrefetchWgs, cus / (8 * groups) - nsl);
+    const int npf = (npfc < 2 || bp.fwd.max_chunks == 0) ? 0 : npfc;
+    const long long grid = 8LL * (nsl + npf) * groups;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     Op *gbuf = (Op *)(ws + bp.off_grads);
     prof_before("gdn2_chunk_rpass", st);
     if constexpr (NSL1 % 2 == 0) {
         if (two)
             hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 2>), dim3((unsigned)grid), dim3(512), 0, st, a.dO,
-                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf, prog, npf);
         else
             hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 1>), dim3((unsigned)grid), dim3(512), 0, st, a.dO,
-                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+                               a.dST, a.dS0, sq, a.H, (const uint8_t *)bops, gbuf, prog, npf);
     } else {
         hipLaunchKernelGGL((chunk_rpass_kernel<Op, DK, DV, 1>), dim3((unsigned)grid), dim3(512), 0, st, a.dO, a.dST,
-                           a.dS0, sq, a.H, (const uint8_t *)bops, gbuf);
+                           a.dS0, sq, a.H, (const uint8_t *)bops, gbuf, prog, npf);
     }
     prof_after(st);
     if ((err = hipGetLastError()) != hipSuccess) return err;
