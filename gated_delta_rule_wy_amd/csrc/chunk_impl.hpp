@@ -861,12 +861,19 @@ static constexpr int kPfMaxSleeps = 64;
 typedef const __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
 
-template <typename In, int DV, size_t BYTES, int CS = 64>
+// Byte ranges [X0, X1) and [Y0, Y1) of the block (line-aligned, Y0 >= X1)
+// are left out: the saving pass of the backward reads no Q+ and no P.
+template <typename In, int DV, size_t BYTES, int CS = 64, size_t X0 = 0, size_t X1 = 0, size_t Y0 = 0,
+          size_t Y1 = 0>
 __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, const In *w, const int *prog,
                                               int chain, int h, int H, int pf, int npf, int nch, int tb, int te,
                                               int gates)
 {
-    constexpr int NL = (int)(BYTES / 128);                        // block lines
+    static_assert(X0 % 128 == 0 && X1 % 128 == 0 && Y0 % 128 == 0 && Y1 % 128 == 0 && X0 <= X1 &&
+                  (Y0 == Y1 || Y0 >= X1) && Y0 <= Y1, "line-aligned, ordered ranges");
+    constexpr int XL0 = (int)(X0 / 128), XN = (int)((X1 - X0) / 128), YL0 = (int)(Y0 / 128) - XN,
+                  YN = (int)((Y1 - Y0) / 128);
+    constexpr int NL = (int)(BYTES / 128) - XN - YN;              // block lines fetched
     constexpr int RB = DV * (int)sizeof(In);                      // bytes per v / w row
     constexpr int RL = (RB + 127) / 128;                          // lines per row
     // lines per chunk: the block, then the v rows and (per-channel gates) the w rows
@@ -890,7 +897,8 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
         for (int l = pf + npf * lane; l < PL; l += npf * 64) {
             const uint8_t *a;
             if (l < NL) {
-                a = blk0 + (size_t)c * BYTES + (size_t)l * 128;
+                const int lb = l + (l >= XL0 ? XN : 0);          // line of the block
+                a = blk0 + (size_t)c * BYTES + (size_t)(lb + (lb - XN >= YL0 && l >= XL0 ? YN : 0)) * 128;
             } else {
                 const int k = l - NL, which = k / (CS * RL), row = (k / RL) % CS, part = k % RL;
                 const int tok = min(tb + CS * c + row, te - 1);
@@ -986,8 +994,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const int nch = min((te - tb + CS - 1) >> LCS, max(0, sq.max_chunks - cbeg));
     auto blk_of = [&](int c) { return ops + ((size_t)h * sq.max_chunks + cbeg + min(c, nch - 1)) * L::bytes; };
     if (role >= NSL) {
-        pass_prefetch<In, DV, L::bytes, CS>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v, w, prog, chain,
-                                            h, H, role - NSL, npf, nch, tb, te, sq.gates);
+        constexpr size_t X0 = SAVE ? L::oQ : 0, X1 = SAVE ? L::oK : 0, Y0 = SAVE ? L::oP : 0, Y1 = SAVE ? L::oT : 0;
+        pass_prefetch<In, DV, L::bytes, CS, X0, X1, Y0, Y1>(ops + ((size_t)h * sq.max_chunks + cbeg) * L::bytes, v,
+                                                            w, prog, chain, h, H, role - NSL, npf, nch, tb, te,
+                                                            sq.gates);
         return;
     }
     const bool report = npf > 0 && js == 0 && t == 0;   // progress for the prefetch workgroups
