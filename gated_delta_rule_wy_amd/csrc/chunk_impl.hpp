@@ -1364,7 +1364,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 }
 
 
-static constexpr int kMaxPrefetchWgs = 4;   // more gave no gain, and a full chip leaves no slack
+static constexpr int kMaxPrefetchWgs = 8;   // (4 -> 8: saving pass 0.63 -> 0.56 ms, forward pass no change)
 
 // compute units of the current device, queried once per device
 static hipError_t device_cus(int *cus)
