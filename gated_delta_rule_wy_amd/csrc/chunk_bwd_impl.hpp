@@ -82,6 +82,17 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
         wf[u] = *reinterpret_cast<const frag *>(blk + L::oW + (size_t)x * 16);
         qfs[u] = *reinterpret_cast<const frag *>(blk + L::oQ + (size_t)x * 16);
     }
+    // (the P, T and Khat^T fragments for the transposed copies, loaded with the rest)
+    constexpr int NPU = (L::NTRI * 64 + 255) / 256, NKU = NCT * NSB * 64 / 256;
+    frag pfs[NPU], tfs[NPU], kfs[NKU];
+#pragma unroll
+    for (int u = 0; u < NPU; ++u) {
+        const int x = min(t + 256 * u, L::NTRI * 64 - 1);
+        pfs[u] = *reinterpret_cast<const frag *>(blk + L::oP + (size_t)x * 16);
+        tfs[u] = *reinterpret_cast<const frag *>(blk + L::oT + (size_t)x * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) kfs[u] = *reinterpret_cast<const frag *>(blk + L::oK + (size_t)(t + 256 * u) * 16);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
         const int x = t + 256 * u;
@@ -97,8 +108,12 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     if (t < DK) reinterpret_cast<float *>(bb + BL::oG)[t] = reinterpret_cast<const float *>(blk + L::oG)[t];
     __syncthreads();
 
-    // N^T tiles (at, bt): contraction over the chunk rows
-    for (int tile = wv; tile < NCT * NCT; tile += 4) {
+    // N^T tiles (at, bt): contraction over the chunk rows (a fixed trip
+    // count, so that the fragment loads of all the wave's tiles issue together)
+#pragma unroll
+    for (int kt = 0; kt < (NCT * NCT + 3) / 4; ++kt) {
+        const int tile = wv + 4 * kt;
+        if ((NCT * NCT) % 4 != 0 && tile >= NCT * NCT) break;   // (wave-uniform)
         const int at = tile / NCT, bt = tile % NCT;
         f4 acc = f4zero();
 #pragma unroll
@@ -119,8 +134,9 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     __syncthreads();
 
     // R^T tiles (at, rt): Q+^T plus (-W)^T P^T (P lower triangular)
-    for (int tile = wv; tile < NCT * 4; tile += 4) {
-        const int at = tile / 4, rt = tile % 4;
+#pragma unroll
+    for (int at = 0; at < NCT; ++at) {
+        const int rt = wv;
         f4 acc = f4zero();
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
@@ -150,16 +166,6 @@ __global__ __launch_bounds__(256) void chunk_bprep_kernel(const uint8_t *__restr
     for (int x = t; x < 64 * LDP; x += 256) { PT[x] = (Op)0.f; TT[x] = (Op)0.f; }
     __syncthreads();
     {
-        constexpr int NPU = (L::NTRI * 64 + 255) / 256, NKU = NCT * NSB * 64 / 256;
-        frag pfs[NPU], tfs[NPU], kfs[NKU];
-#pragma unroll
-        for (int u = 0; u < NPU; ++u) {
-            const int x = min(t + 256 * u, L::NTRI * 64 - 1);
-            pfs[u] = *reinterpret_cast<const frag *>(blk + L::oP + (size_t)x * 16);
-            tfs[u] = *reinterpret_cast<const frag *>(blk + L::oT + (size_t)x * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < NKU; ++u) kfs[u] = *reinterpret_cast<const frag *>(blk + L::oK + (size_t)(t + 256 * u) * 16);
 #pragma unroll
         for (int u = 0; u < NPU; ++u) {
             const int x = t + 256 * u;
