@@ -570,12 +570,14 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     // phase B (floats, then the raw inputs of the slice in the input type)
     constexpr size_t B_DA = 0, B_DP = B_DA + 64 * LDF, B_XT = B_DP + 64 * LDF, B_XM = B_XT + CW * LDF,
                      B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
-                     B_G = B_QM + CW * LDF, B_DG = B_G + 64 * LDC, B_GAM = B_DG + 64 * LDC, B_KHK = B_GAM + DK,
+                     B_DG = B_QM + CW * LDF, B_GAM = B_DG + 64 * LDC, B_KHK = B_GAM + DK,
                      B_END = B_KHK + DK;                                            // floats
     constexpr int LDR = 64 + 4;                           // raw inputs of the slice, transposed
     constexpr size_t B_BYTES = B_END * 4 + 3 * CW * LDR * sizeof(In);
     constexpr size_t REGION = (A_END * sizeof(Op) > B_BYTES ? A_END * sizeof(Op) : B_BYTES);
-    __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[NT];
+    // g (the chunk's cumulative log decay, all channels) from phase 0 to the end
+    constexpr int LDL = DK + 1;
+    __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[NT], sGc[64 * LDL];
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
     Op *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     Op *OTl = (Op *)smem + A_OTL, *Xjl = (Op *)smem + A_XJL, *DTl = (Op *)smem + A_DTL;
     float *fb = (float *)smem;
     float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
-    float *QtT = fb + B_QT, *QmT = fb + B_QM, *sg = fb + B_G, *sdG = fb + B_DG;
+    float *QtT = fb + B_QT, *QmT = fb + B_QM, *sdG = fb + B_DG;
     float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
     In *sqT = (In *)(fb + B_END), *skT = sqT + CW * LDR, *sbT = skT + CW * LDR;
 
@@ -602,8 +604,6 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     // log alpha of the chunk for phase 0, then (arriving during phase 0)
     // this wave's fragments of the forward block and the first value
     // slice's inputs
-    constexpr int LDL = DK + 1;
-    static_assert(64 * LDL * 4 <= REGION, "log alpha tile fits the shared region");
     constexpr int NU = 64 * DK / NT;
     float lv[NU];
 #pragma unroll
@@ -667,23 +667,23 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     SR ra, rb;
     sload(ra, 0);
 
-    // ---- phase 0: references of the 16-row blocks, per channel ----
-    // (log alpha staged through LDS with coalesced loads; the running sums
-    // then read LDS, not memory)
+    // ---- phase 0: g and the references of the 16-row blocks, per channel ----
+    // (log alpha staged through LDS with coalesced loads and summed down the
+    // rows in place; phase B reads g from there)
     {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int x = t + NT * u, r = x / DK, c = x % DK;
-            fb[r * LDL + c] = r < n ? lv[u] : 0.f;
+            sGc[r * LDL + c] = r < n ? lv[u] : 0.f;
         }
         __syncthreads();
-        col_scan64<DK, false, NT>(fb, LDL, sPart, t);
+        col_scan64<DK, false, NT>(sGc, LDL, sPart, t);
         for (int c = t; c < DK; c += NT) {
             sRef[c] = 0.f;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                sRef[(R + 1) * DK + c] = fb[(16 * R + 15) * LDL + c];
-                sMid[R * DK + c] = fb[(16 * R + 7) * LDL + c];
+                sRef[(R + 1) * DK + c] = sGc[(16 * R + 15) * LDL + c];
+                sMid[R * DK + c] = sGc[(16 * R + 7) * LDL + c];
             }
         }
         __syncthreads();
@@ -835,13 +835,12 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     constexpr int SL = 64 * CW / NT, NIT = SL / 4;
     static_assert(NT % CW == 0 && SL % 4 == 0, "whole four-row groups per thread");
     struct alignas(4 * sizeof(In)) In4 { In v[4]; };
-    struct BR { float l[SL]; In q[SL], k[SL], b[SL]; };
+    struct BR { In q[SL], k[SL], b[SL]; };
     const int bcl = t % CW, bs = t / CW, r0 = SL * bs;
     auto bload = [&](BR &R_, int cs) {
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
             const size_t o = tok_k(min(r0 + i, n - 1)) + cs * CW + bcl;
-            R_.l[i] = la[o];
             R_.q[i] = q[o];
             R_.k[i] = k[o];
             R_.b[i] = b[o];
@@ -865,33 +864,17 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
 
     // ---- phase B, key channels in slices of CW ----
     // Thread t owns channel bcl = t % CW of the slice and the SL consecutive
-    // rows from r0 = SL * (t / CW). Log alpha, q, k, b of the next slice load
-    // while this one is worked on; the cumulative log decay is scanned down
-    // the thread's rows in registers and across the row segments through LDS;
-    // the decay-scaled operands and the raw inputs are written transposed,
-    // four rows per store.
+    // rows from r0 = SL * (t / CW). q, k, b of the next slice load while this
+    // one is worked on; g comes from phase 0; the decay-scaled operands and
+    // the raw inputs are written transposed, four rows per store.
 #pragma unroll
     for (int cs = 0; cs < NCS; ++cs) {
         const int c0 = cs * CW;
         BR &bc = (cs & 1) ? bb2 : ba;
         BR &bn = (cs & 1) ? ba : bb2;
-        // (the previous slice's readers of sPart finished inside its reverse
-        // scan, and its readers of the other phase-B regions before that)
-        float gl[SL], tot = 0.f;
-#pragma unroll
-        for (int i = 0; i < SL; ++i) {
-            gl[i] = r0 + i < n ? bc.l[i] : 0.f;
-            tot += gl[i];
-        }
-        sPart[bs * CW + bcl] = tot;
+        // (the previous slice's readers of the phase-B regions finished before
+        // its reverse scan)
         if (cs + 1 < NCS) bload(bn, cs + 1);
-        __syncthreads();
-        {
-            float acc = 0.f;
-            for (int s2 = 0; s2 < bs; ++s2) acc += sPart[s2 * CW + bcl];
-#pragma unroll
-            for (int i = 0; i < SL; ++i) { acc += gl[i]; gl[i] = acc; }
-        }
         const In zero_ = (In)0;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -905,8 +888,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                 const bool ok = rb + e < n;
                 const In kr_ = ok ? bc.k[i] : zero_, qr_ = ok ? bc.q[i] : zero_, br_ = ok ? bc.b[i] : zero_;
                 const float kv = in2f<In>(kr_), qv = in2f<In>(qr_), bv = in2f<In>(br_);
-                const float gv = gl[i];
-                sg[(rb + e) * LDC + bcl] = gv;
+                const float gv = sGc[(rb + e) * LDL + c];
                 const float e1 = __expf(rf1 - gv), em = __expf(md - gv);
                 const float e2 = __expf(gv - rf0), en = __expf(gv - md);
                 xt[e] = kv * e1;
@@ -942,7 +924,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
         for (int ct = 0; ct < CWH; ++ct) {
             const int cl = 16 * (hv + HV * ct) + m16;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) gR[ct][ii] = sg[(16 * R + 4 * g4 + ii) * LDC + cl];
+            for (int ii = 0; ii < 4; ++ii) gR[ct][ii] = sGc[(16 * R + 4 * g4 + ii) * LDL + c0 + cl];
             midR[ct] = sMid[R * DK + c0 + cl];
             Y1[ct] = f4zero();
             Y2[ct] = f4zero();
