@@ -1295,6 +1295,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         }
             }
             __syncthreads();   // (1)
+            if (!SAVE && c > 0) store_o(c - 1);
             if constexpr (!SAVE) pre.load(blk_of(c + PD), wo, lane);
             uv_load(upre, c + PD);
             if constexpr (PRO) conv_u(unext, sln, sl);
@@ -1302,7 +1303,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 __syncthreads();   // (2)
                 return;
             }
-            if (c > 0) store_o(c - 1);
             f4 oacc[RPW][NC];
             if (RT::ALL || rows) {
 #pragma unroll
