@@ -472,9 +472,9 @@ __global__ __launch_bounds__(512) void chunk_rpass_kernel(const float *__restric
 }
 
 // Inclusive running sums down (REV: up) the 64 rows of NCOL columns of an
-// LDS tile with row stride ld, by all 256 threads of the workgroup: thread t
+// LDS tile with row stride ld, by all NT threads of the workgroup: thread t
 // takes column t % NCOL and one segment of rows; segment totals pass through
-// `part` (256 floats). Contains two barriers.
+// `part` (NT floats). Contains two barriers.
 template <int NCOL, bool REV, int NT>
 __device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int t)
 {
