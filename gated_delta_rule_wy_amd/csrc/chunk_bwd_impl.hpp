@@ -752,8 +752,8 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
         SR &cur = (vs & 1) ? rb : ra;
         SR &nxt = (vs & 1) ? ra : rb;
         __syncthreads();   // previous slice's readers are done
-        sstore(cur);
         if (vs + 1 < NVS) sload(nxt, vs + 1);
+        sstore(cur);
         __syncthreads();
         // dDelta row tile wv: P^T dO + Khat G
 #pragma unroll
