@@ -1296,11 +1296,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             }
             __syncthreads();   // (1)
             // The previous chunk's o tile goes out here, ahead of this
-            // step's loads, with per-channel gates; with one w per token and
-            // head (fewer loads) after them instead. Each order is the faster
-            // one for its form (pass at T = 64K, H = 16: 0.802 -> 0.777 ms and
-            // 0.790 against 0.823 ms).
-            if (!SAVE && !WSC && c > 0) store_o(c - 1);
+            // step's loads, with per-channel gates given as they are; with one
+            // w per token and head (fewer loads) or with the fused prologue
+            // (raw v staged and convolved here) after them instead. Each order
+            // is the faster one for its form (pass at T = 64K, H = 16: 0.802 ->
+            // 0.777 ms; 0.790 against 0.823 ms; 0.892 against 0.922 ms).
+            if (!SAVE && !WSC && !PRO && c > 0) store_o(c - 1);
             if constexpr (!SAVE) pre.load(blk_of(c + PD), wo, lane);
             uv_load(upre, c + PD);
             if constexpr (PRO) conv_u(unext, sln, sl);
@@ -1308,7 +1309,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 __syncthreads();   // (2)
                 return;
             }
-            if (WSC && c > 0) store_o(c - 1);
+            if ((WSC || PRO) && c > 0) store_o(c - 1);
             f4 oacc[RPW][NC];
             if (RT::ALL || rows) {
 #pragma unroll
