@@ -64,6 +64,23 @@ def traffic_for(kernel: str, workload: str):
     return e['fetch_bytes'] + e['write_bytes']
 
 
+def mfma_summary(model_flop_frac):
+    """Matrix-core use of the T = 64K prefill step: the algorithmic (model)
+    FLOP fraction measured here, and the rocprof MFMA-busy fraction of each
+    kernel from the committed counter summary when it was taken on the
+    current kernel sources (else null)."""
+    out = {'peak_tflops': PEAK_MFMA_F16_TFLOPS, 'model_flop_frac': model_flop_frac, 'busy_frac': None}
+    path = os.path.join(ROOT, 'profiles', 'mfma.json')
+    if os.path.exists(path):
+        with open(path) as f:
+            d = json.load(f)
+        if d.get('source_sha') == src_hash():
+            out['busy_frac'] = d.get('busy_frac')
+            out['issued_tflops'] = d.get('issued_tflops')
+            out['counters'] = d.get('counters')
+    return out
+
+
 def roofline(kernel, alg_bytes, avg_ms, workload):
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     return {'bound': 'hbm', 'kernel': kernel, 'achieved': round(achieved, 1), 'peak': PEAK_HBM_GBS,
@@ -126,6 +143,7 @@ def bench_prefill(args, torch, gdn2, gi):
                           'achieved': round(step_bytes / (ms * 1e-3) / 1e9, 1), 'peak': PEAK_HBM_GBS,
                           'unit': 'GB/s', 'frac': round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         'kernels_ms': {k: round(v, 5) for k, v in avg.items()},
+        'model_flop_frac': round(TH * flops_per_token_head(dk, dv) / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
     }
 
     # The same workload with gates of one value per token-head: the Kimi Delta
@@ -209,6 +227,63 @@ def bench_prefill(args, torch, gdn2, gi):
                                 'tokens': n_s}
         log(f'[bench] oracle {n_s} tokens in {dt:.1f}s; parity {res["parity_sample"]}')
     del q, k, v, b, w, la, o, ws, b1, la1, o1, ST1
+    torch.cuda.empty_cache()
+    return res
+
+
+PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense f16 / bf16 matrix peak, TFLOP/s
+
+
+def flops_per_token_head(dk, dv, C=64):
+    """Algorithmic work of the chunk method per token and head: the state
+    products (6 dk dv), the C x C blocks over dk and dv, triangular halves
+    counted once (C (3 dk + 2 dv) + C^2 / 3)."""
+    return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C // 3
+
+
+def bench_prefill_config(args, torch, gdn2, gi, name):
+    """tokens/s of one more prefill workload (its own launch configuration)."""
+    c = gi.WORKLOADS[name]
+    t0 = time.time()
+    p = gi.workload(name, threads=nthreads())
+    log(f'[bench] generated {name} ({p.tokens} tokens x {p.H} heads) in {time.time() - t0:.1f}s')
+    dev = torch.device('cuda:0')
+    bf = torch.bfloat16
+    shp = (p.B, -1, p.H)
+    to = lambda x, dt: torch.from_numpy(x).to(dev).to(dt).reshape(*shp, x.shape[-1])
+    q, k, v, b, w = (to(x, bf) for x in (p.q, p.k, p.v, p.b, p.w))
+    la = to(p.log_alpha, torch.float32)
+    del p.q, p.k, p.v, p.b, p.w, p.log_alpha
+    S0 = torch.from_numpy(p.S0).to(dev) if p.S0 is not None else None
+    cu = torch.from_numpy(p.cu_seqlens).to(dev) if p.varlen else None
+    o = torch.empty(*q.shape[:3], p.dv, device=dev)
+    ST = torch.empty(p.N, p.H, p.dk, p.dv, device=dev)
+    ws = torch.empty(gdn2.workspace_bytes(p.B, p.T, p.N, p.H, p.dk, p.dv, bf, p.varlen), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: gdn2.chunk_fwd(q, k, v, la, b, w, S0, cu, out=o, final_state=ST, workspace=ws)
+    steps = max(5, args.steps // 2) if p.varlen else args.steps
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    gdn2.profile_begin(steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    prof = gdn2.profile_end()
+    TH = p.tokens * p.H
+    nbytes = TH * (3 * p.dk * 2 + p.dk * 4 + 2 * p.dv * 2 + p.dv * 4) + (2 if S0 is not None else 1) * \
+        p.N * p.H * p.dk * p.dv * 4
+    fl = TH * flops_per_token_head(p.dk, p.dv)
+    log(f'[bench] {name}: {ms:.3f} ms/step, {p.tokens / (ms * 1e-3) / 1e6:.1f} M tokens/s')
+    res = {'workload': name, 'tokens': p.tokens, 'H': p.H, 'sequences': p.N, 'steps': steps,
+           'ms_per_step': round(ms, 4), 'value': round(p.tokens / (ms * 1e-3), 1), 'unit': 'tokens/s',
+           'alg_bytes_per_step': int(nbytes),
+           'step_roofline_frac': round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           'model_flop_frac': round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+           'kernels_ms': {kk: round(vv[1] / vv[0], 5) for kk, vv in prof.items() if vv[0]}}
+    del q, k, v, b, w, la, o, ws, ST, S0
     torch.cuda.empty_cache()
     return res
 
@@ -411,6 +486,8 @@ def main():
                     help='skip the fused-prologue (raw-input) timings')
     ap.add_argument('--no-gate-forms', action='store_true',
                     help='skip the scalar-gate (KDA, Gated DeltaNet) prefill timings')
+    ap.add_argument('--no-other-configs', action='store_true',
+                    help='skip the B=4 x T=4096 and packed varlen (H=32) prefill timings')
     ap.add_argument('--no-chunk-sizes', action='store_true',
                     help='skip the chunk-size (32 / 64 / 128 tokens) prefill timings')
     ap.add_argument('--copy-calibration-mib', type=int, default=0,
@@ -451,6 +528,7 @@ def main():
     if 'cpu_baseline' in pre:
         out['cpu_baseline'] = pre['cpu_baseline']
     out['step_roofline'] = pre['step_roofline']
+    out['mfma'] = mfma_summary(pre['model_flop_frac'])
     out['kernels_ms'] = pre['kernels_ms']
     out['gate_forms'] = pre['gate_forms']
     out['chunk_sizes'] = pre['chunk_sizes']
@@ -460,6 +538,9 @@ def main():
         out['backward'] = pre['backward']
     if 'parity_sample' in pre:
         out['parity_sample'] = pre['parity_sample']
+    if not args.no_other_configs:
+        out['other_prefill'] = [bench_prefill_config(args, torch, gdn2, gi, n)
+                                for n in ('prefill_b4_t4096', 'varlen_32seq')]
     if not args.no_decode:
         out['decode'] = bench_decode(args, torch, gdn2, gi)
     print(json.dumps(out), flush=True)

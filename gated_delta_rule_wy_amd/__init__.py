@@ -230,7 +230,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     set_stream()
     wsb = workspace.numel() * workspace.element_size()
-    if chunk == CHUNK:
+    if chunk == CHUNK and gates == GDN2_GATES_PER_CHANNEL:
+        st = _lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                 _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
+                                 B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace), wsb)
+        where = 'gdn2_chunk_fwd'
+    elif chunk == CHUNK:
         st = _lib.gdn2_chunk_fwd_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
                                        _ptr(S0), _ptr(out), _ptr(ST), _ptr(cu_seqlens),
                                        B, T, N, H, dk, dv, code, GDN2_F32, _ptr(workspace), wsb)
@@ -266,10 +271,16 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
     else:
         _check(out, 'out', (N, H, dv), torch.float32, dev)
     set_stream()
-    st = _lib.gdn2_decode_step_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
-                                     _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
+    if gates == GDN2_GATES_PER_CHANNEL:
+        st = _lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                   _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
+        where = 'gdn2_decode_step'
+    else:
+        st = _lib.gdn2_decode_step_gates(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), gates,
+                                         _ptr(S), _ptr(out), N, H, dk, dv, code, GDN2_F32)
+        where = 'gdn2_decode_step_gates'
     if st != GDN2_OK:
-        raise Gdn2Error(st, 'gdn2_decode_step_gates')
+        raise Gdn2Error(st, where)
     return out
 
 

@@ -150,23 +150,30 @@ const char *gdn2_status_string(int status)
     return "GDN2: unknown status";
 }
 
-static int chunk_check(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype, int varlen,
+static int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const void *b, const void *w, int gates, const gdn2_short_conv *conv, const float *S0,
+                          void *o, float *ST, const int32_t *cu_seqlens, int B, int T, int N, int H, int dk,
+                          int dv, int in_dtype, int out_dtype, void *workspace,
+                          size_t workspace_bytes, int chunk = 64);
+
+static int chunk_check(int B, int T, int N, int H, int dk, int dv, int in_dtype, int varlen,
                        gdn2::ChunkPlan *plan, int chunk = 64)
 {
     if (chunk != 32 && chunk != 64 && chunk != 128) return GDN2_ERR_INVALID;
     if (B <= 0 || T < 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
     if (in_dtype != GDN2_F32 && in_dtype != GDN2_BF16) return GDN2_ERR_INVALID;
     if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID;
-    if ((long long)B * T * H * (dk > dv ? dk : dv) > 0x7fffffffLL * 16LL) return GDN2_ERR_UNSUPPORTED;
-    if ((long long)B * T > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN2_ERR_UNSUPPORTED;
     if (H > 65535) return GDN2_ERR_UNSUPPORTED;   // grid y dimension
+    if ((long long)B * T > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    // (each factor is bounded above, so the product cannot overflow)
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > 0x7fffffffLL * 16LL) return GDN2_ERR_UNSUPPORTED;
     if (!gdn2::chunk_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, plan, chunk))
         return GDN2_ERR_UNSUPPORTED;
     return GDN2_OK;
 }
 
-size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype,
+size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, int dv, int in_dtype,
                                             int varlen, int chunk)
 {
     gdn2::ChunkPlan plan;
@@ -175,7 +182,7 @@ size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, 
 }
 
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
-                                      gdn2_dtype in_dtype, int varlen)
+                                      int in_dtype, int varlen)
 {
     gdn2::ChunkPlan plan;
     if (chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan) != GDN2_OK) return 0;
@@ -185,12 +192,13 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv
 int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                    const void *b, const void *w, const float *S0, void *o, float *ST,
                    const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                   gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                   int in_dtype, int out_dtype, void *workspace,
                    size_t workspace_bytes)
 {
     return gdn2_chunk_fwd_gates(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, S0, o, ST, cu_seqlens, B, T,
                                 N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes);
 }
+
 
 // The convolution parameters of a *_prologue call: weights required, biases
 // optional, history in / out each all-or-none.
@@ -217,8 +225,8 @@ static int conv_args(const gdn2_short_conv *c, gdn2::Prologue *p)
 static int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                           const void *b, const void *w, int gates, const gdn2_short_conv *conv, const float *S0,
                           void *o, float *ST, const int32_t *cu_seqlens, int B, int T, int N, int H, int dk,
-                          int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
-                          size_t workspace_bytes, int chunk = 64)
+                          int dv, int in_dtype, int out_dtype, void *workspace,
+                          size_t workspace_bytes, int chunk)
 {
     if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     gdn2::ChunkPlan plan;
@@ -254,7 +262,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
 int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
                          const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
                          const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                         int in_dtype, int out_dtype, void *workspace,
                          size_t workspace_bytes)
 {
     return chunk_fwd_impl(q, k, v, log_alpha, b, w, gates, nullptr, S0, o, ST, cu_seqlens, B, T, N, H, dk, dv,
@@ -263,7 +271,7 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
 
 int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
                          const void *w, const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B,
-                         int T, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                         int T, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
                          int chunk, void *workspace, size_t workspace_bytes)
 {
     return chunk_fwd_impl(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, nullptr, S0, o, ST, cu_seqlens, B, T,
@@ -273,7 +281,7 @@ int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const floa
 int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
                             const void *b_logit, const void *w_logit, const gdn2_short_conv *conv,
                             const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B, int T,
-                            int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                            int N, int H, int dk, int dv, int in_dtype, int out_dtype,
                             void *workspace, size_t workspace_bytes)
 {
     if (!conv) return GDN2_ERR_INVALID;
@@ -283,14 +291,14 @@ int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_
 
 int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
-                     int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+                     int dv, int in_dtype, int out_dtype)
 {
     return gdn2_decode_step_gates(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, S, o, N, H, dk, dv, in_dtype,
                                   out_dtype);
 }
 
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
-                                      gdn2_dtype in_dtype, int varlen)
+                                      int in_dtype, int varlen)
 {
     gdn2::ChunkPlan plan;
     if (chunk_check(B, T, N, H, dk, dv, in_dtype, varlen, &plan) != GDN2_OK) return 0;
@@ -302,7 +310,7 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv
 int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
                    const void *b, const void *w, const float *S0, const float *dO, const float *dST,
                    const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                   gdn2_dtype in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                   int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
                    float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes)
 {
     gdn2::ChunkPlan plan;
@@ -341,7 +349,7 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
 
 static int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                        const void *b, const void *w, int gates, const gdn2_short_conv *conv, float *S, void *o,
-                       int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+                       int N, int H, int dk, int dv, int in_dtype, int out_dtype)
 {
     if (gates & ~(GDN2_GATE_B_PER_HEAD | GDN2_GATE_W_PER_HEAD | GDN2_GATE_ALPHA_PER_HEAD)) return GDN2_ERR_INVALID;
     if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0) return GDN2_ERR_INVALID;
@@ -369,14 +377,14 @@ static int decode_impl(const void *q, const void *k, const void *v, const float 
 
 int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
                            const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
-                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+                           int dv, int in_dtype, int out_dtype)
 {
     return decode_impl(q, k, v, log_alpha, b, w, gates, nullptr, S, o, N, H, dk, dv, in_dtype, out_dtype);
 }
 
 int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
                               const void *b_logit, const void *w_logit, const gdn2_short_conv *conv, float *S,
-                              void *o, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype)
+                              void *o, int N, int H, int dk, int dv, int in_dtype, int out_dtype)
 {
     if (!conv) return GDN2_ERR_INVALID;
     return decode_impl(q_raw, k_raw, v_raw, log_alpha, b_logit, w_logit, GDN2_GATES_PER_CHANNEL, conv, S, o, N, H,

@@ -842,6 +842,53 @@ template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, i
     *reinterpret_cast<op4 *>(dst + lane * 4) = y;
 }
 
+// ---- per-column scales of the f16 tiles ------------------------------------
+// The pass rounds the state S, the writes U = w * v and the corrected writes
+// Delta to f16 for the matrix cores. Value columns of the state evolve
+// independently (the transition acts on the key axis only), so column j of
+// each may be carried as X[:, j] / sigma_j with its own power of two sigma_j:
+// every product is then an exact multiple of the unscaled one. A scale maps
+// its bound B into [2^9, 2^10): far from f16's overflow at 2^16 and from its
+// subnormals below 2^-14, whatever the magnitude of the state (unscaled, a
+// state near 1e-6 kept ~4 significant bits and one past 65504 became inf).
+//  * S_{c+1}: B = max|S_c[:, j]| + CS max|Delta_c[:, j]| (keys of at most
+//    unit norm, every decay factor <= 1), from maxima exchanged in LDS during
+//    step c;
+//  * U: each 32-row block (one contraction step of T U) from its own values;
+//  * Delta_c: the largest of the two above, per column; |Delta| is the
+//    token recurrence's corrected write, within a few times |U| + |S|.
+// 2^e with B / 2^e in [2^9, 2^10) for B > 0, |e| <= 100; 0 for B = 0 (a
+// quantity that is all zero takes no part in the max that forms sigma_D,
+// and scaling zeros by 1 / 0 below keeps them zero)
+__device__ __forceinline__ float pow2_scale(float B)
+{
+    const int e = min(max((int)((__float_as_uint(B) >> 23) & 0xFF) - 127 - 9, -100), 100);
+    return B > 0.f ? __uint_as_float((uint32_t)(e + 127) << 23) : 0.f;
+}
+// 1 / s for s = 2^e, |e| <= 100 (exact); 2^127 for s = 0, which only ever
+// multiplies zeros
+__device__ __forceinline__ float pow2_recip(float s) { return __uint_as_float(0x7F000000u - __float_as_uint(s)); }
+
+// max over the lanes n, n + 16, n + 32, n + 48 (the four row groups of one
+// accumulator-tile column), with gfx950's lane swaps: permlane16_swap pairs
+// each odd 16-lane row with the even row below it and permlane32_swap the
+// two halves; of the two results one is the lane's own value and the other
+// its partner's, whichever half the lane sits in
+__device__ __forceinline__ float colmax_lanes(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS running maximum of one step (non-negative floats compare as their bit
+// patterns)
+__device__ __forceinline__ void lds_umax(float *p, float x)
+{
+    atomicMax(reinterpret_cast<unsigned int *>(p), __float_as_uint(x));
+}
+
 // L2 prefetch workgroups. A pass workgroup holds a bounded number of
 // cache-line requests in flight, so its step time grows with the latency of
 // the level its operands come from. When the chip has workgroup slots to
@@ -913,10 +960,10 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
 
 //
 // PRO (fused prologue): v and w arrive raw. The output waves keep the raw v
-// rows of three chunks in LDS (slot c % 3): each step stages the next
+// rows of four chunks in LDS (slot c % 4): each step stages the next
 // chunk's rows, and forms this chunk's U = sigmoid(w) * ShortConv(v) from
 // its own row (registers) and the three before it (LDS, reaching into the
-// previous chunk's slot, or the history rows placed in slot 2 before the
+// previous chunk's slot, or the history rows placed in slot 3 before the
 // first chunk).
 //
 // SAVE (for the backward): no output; the state waves store each chunk's
@@ -963,6 +1010,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     // two for 128-token chunks (their fragment sets are twice the size)
     constexpr int RING = CS >= 128 ? 2 : 3;
     constexpr int PD = RING - 1;
+    // the output waves load one chunk further ahead (a ring of four; three
+    // with the fused prologue on two column tiles, whose registers would not
+    // hold a fourth): v and w arrive from memory with a long latency
+    constexpr int ORING = CS >= 128 ? 2 : (PRO && NC == 2 ? 3 : 4);
+    constexpr int OPD = ORING - 1;
     constexpr int UR = CS >= 64 ? CS / 64 : 1;   // v / w rows per output-wave thread
     constexpr int LCS = __builtin_ctz(CS);
     static_assert(NSL >= 1 && NSL * 16 * NC == DV, "slice width must divide dv");
@@ -974,7 +1026,22 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
     __shared__ __attribute__((aligned(16))) float sO[2][CS * LDO];          // o tiles
     constexpr int LDV = 16 * NC;                                             // raw-v row stride (floats)
-    __shared__ __attribute__((aligned(16))) float sVr[PRO ? 3 : 1][PRO ? 64 * LDV : 4];   // PRO: raw v rows
+    __shared__ __attribute__((aligned(16))) float sVr[PRO ? ORING : 1][PRO ? 64 * LDV : 4];   // PRO: raw v rows
+    // f16 tiles carry per-column power-of-two scales (pow2_scale above);
+    // fp32 operands need none. The state tiles take sigma_S from the bound
+    // max|S_c| + CS max|Delta_c| on the next state; each 32-row block of U
+    // takes its own sigma_U from its values (one output wave stages one
+    // block, so no exchange is needed before the tile is written); Delta takes
+    // sigma_D = max(sigma_S, sigma_U of every block) per column.
+    constexpr bool SCL = std::is_same<Op, _Float16>::value;
+    constexpr int NCOL = 16 * NC;
+    // step maxima by parity of the chunk: [state | corrected writes][column]
+    __shared__ __attribute__((aligned(16))) float sMax[SCL ? 2 : 1][SCL ? 2 * NCOL : 4];
+    // state maxima before the first chunk: [wave][column]
+    __shared__ __attribute__((aligned(16))) float sMax0[SCL ? 4 : 1][SCL ? NCOL : 4];
+    // sigma_S by parity of the chunk, and sigma_U of the current chunk's U blocks
+    __shared__ __attribute__((aligned(16))) float sSigS[SCL ? 2 : 1][SCL ? NCOL : 4];
+    __shared__ __attribute__((aligned(16))) float sSigU[SCL ? NSB : 1][SCL ? NCOL : 4];
 
     // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
     // sit on XCD c % 8
@@ -1019,9 +1086,33 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         for (int ii = 0; ii < 4; ++ii)
                             Sr[q][u][ii] = S0[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16];
                     }
-                    lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
+                    if constexpr (!SCL) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
             }
+        // scale of column 16q + m16 for the current chunk (sigma and 1/sigma)
+        float sig[NC], isig[NC];
+#pragma unroll
+        for (int q = 0; q < NC; ++q) { sig[q] = 1.f; isig[q] = 1.f; }
+        // per-column max of |S| over this wave's tiles (in every lane of the column)
+        auto state_max = [&](int q) {
+            float m = 0.f;
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                if (NCT % 4 != 0 && wv * TPW + u >= NCT) continue;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) m = fmaxf(m, fabsf(Sr[q][u][ii]));
+            }
+            return colmax_lanes(m);
+        };
+        if constexpr (SCL) {
+            if (wv == 0)
+                for (int x = lane; x < 2 * NCOL; x += 64) sMax[0][x] = 0.f;
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const float m = state_max(q);
+                if (g4 == 0) sMax0[wv][16 * q + m16] = m;
+            }
+        }
         const bool rows = RT::active(wv);
         // last stored k-block of T / P for the wave's row tile j (RPW <= 2)
         const int sbm0 = (16 * RT::rt(wv, 0) + 15) / KB;
@@ -1038,6 +1129,27 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             }
         }
         if constexpr (PRO) __syncthreads();   // pairs with the output waves' staging of chunk 0
+        if constexpr (SCL) {
+            __syncthreads();   // the first chunk's state maxima
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                float m = 0.f;
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) m = fmaxf(m, sMax0[w4][16 * q + m16]);
+                sig[q] = pow2_scale(m);
+                isig[q] = pow2_recip(sig[q]);
+                if (g4 == 0) sSigS[0][16 * q + m16] = sig[q];
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (ct < NCT) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u] * isig[q]);
+                }
+                // the first chunk's state maximum for the step-0 bound (buffer 0,
+                // cleared before the barrier above)
+                const float ms = state_max(q);
+                if (g4 == 0) lds_umax(&sMax[0][16 * q + m16], ms);
+            }
+        }
         // The prefetch of chunk c+PD is split over the two windows in which
         // the state waves would otherwise wait for the output waves.
         const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
@@ -1054,15 +1166,46 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     }
             }
             __syncthreads();   // (1) state tiles and U ready
+            // sigma_U of the chunk's 32-row U blocks and sigma_D, for this lane's column
+            float sgu[NC][NSB], sgd[NC], isgd[NC];
+            if constexpr (SCL) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    sgd[q] = sig[q];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) {
+                        sgu[q][sb] = sSigU[sb][16 * q + m16];
+                        sgd[q] = fmaxf(sgd[q], sgu[q][sb]);
+                    }
+                    isgd[q] = pow2_recip(sgd[q]);
+                }
+            }
+            float mD[NC];   // per-column max of |Delta| over this wave's rows
+#pragma unroll
+            for (int q = 0; q < NC; ++q) mD[q] = 0.f;
             if (RT::ALL || rows) {
-                f4 acc[RPW][NC], accw[RPW][NC];
+                // T U per U block (each block has its own scale), then -W S
+                constexpr int NA = SCL ? NSB : 1;
+                f4 acc[RPW][NC][NA], accw[RPW][NC];
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) { acc[j][q] = f4zero(); accw[j][q] = f4zero(); }
+                    for (int q = 0; q < NC; ++q) {
+                        accw[j][q] = f4zero();
+#pragma unroll
+                        for (int a = 0; a < NA; ++a) acc[j][q][a] = f4zero();
+                    }
+                // every B fragment is read from LDS before the products, so
+                // that the reads overlap rather than each wait on its own
+                frag sfr[NC][NKB];
+#pragma unroll
+                for (int q = 0; q < NC; ++q)
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb) sfr[q][kb] = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
                     if (RPW == 1 && sb > sbmax(0)) break;
+                    const int a = SCL ? sb : 0;
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
                         const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
@@ -1070,52 +1213,126 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
-                            acc[j][q] = M::mma(cur.Ti[j][sb], uh, acc[j][q]);
-                            acc[j][q] = M::mma(cur.Ti[j][sb], ul, acc[j][q]);
+                            acc[j][q][a] = M::mma(cur.Ti[j][sb], uh, acc[j][q][a]);
+                            acc[j][q][a] = M::mma(cur.Ti[j][sb], ul, acc[j][q][a]);
                         }
                     }
                 }
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) {
-                        const frag sf = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
+                    for (int q = 0; q < NC; ++q)
 #pragma unroll
-                        for (int j = 0; j < RPW; ++j) accw[j][q] = M::mma(cur.nW[j][kb], sf, accw[j][q]);
-                    }
+                        for (int j = 0; j < RPW; ++j) accw[j][q] = M::mma(cur.nW[j][kb], sfr[q][kb], accw[j][q]);
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q)
-                        lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, acc[j][q] + accw[j][q]);
-                if constexpr (SAVE) {
-                    Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
+                    for (int q = 0; q < NC; ++q) {
+                        f4 d;   // Delta, unscaled
+                        if constexpr (SCL) {
+                            d = accw[j][q] * sig[q];
 #pragma unroll
-                    for (int q = 0; q < NC; ++q)
-                        tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, acc[0][q] + accw[0][q]);
+                            for (int a = 0; a < NA; ++a) d += acc[j][q][a] * sgu[q][a];
+#pragma unroll
+                            for (int ii = 0; ii < 4; ++ii) mD[q] = fmaxf(mD[q], fabsf(d[ii]));
+                            lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d * isgd[q]);
+                        } else {
+                            d = acc[j][q][0] + accw[j][q];
+                            lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d);
+                        }
+                        if constexpr (SAVE) {
+                            if (j == 0) {
+                                Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
+                                tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, d);
+                            }
+                        }
+                    }
+            }
+            // the prefetch goes out ahead of the maxima below: the compiler
+            // does not move global loads across their LDS atomics
+            pre.load_a(blk_of(c + PD), wv, lane);
+            float *mx = &sMax[SCL ? (c & 1) : 0][0];
+            if constexpr (SCL) {
+                // clear the other parity for the next chunk (its last readers
+                // passed barrier (1)); add this wave's maxima of Delta_c
+                if (wv == 0)
+                    for (int x = lane; x < 2 * NCOL; x += 64) sMax[(c + 1) & 1][x] = 0.f;
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    const float md = colmax_lanes(mD[q]);
+                    if (g4 == 0) lds_umax(mx + NCOL + 16 * q + m16, md);
                 }
             }
-            pre.load_a(blk_of(c + PD), wv, lane);
             __syncthreads();   // (2) Delta tiles ready
             frag Db[NC][NSB];
 #pragma unroll
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) Db[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+            if constexpr (SCL) {
+                // S <- gamma S + sigma_D Khat^T (Delta / sigma_D), products first
+                f4 kd[NC][TPW];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int ct = wv * TPW + u;
-                if (NCT % 4 != 0 && ct >= NCT) continue;
+                for (int u = 0; u < TPW; ++u) {
+                    if (NCT % 4 != 0 && wv * TPW + u >= NCT) continue;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) {
+                        f4 s = f4zero();
+#pragma unroll
+                        for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                        kd[q][u] = s;
+                    }
+                }
+                pre.load_b(blk_of(c + PD), wv, lane);
+                // the next chunk's sigma_S from the bound, read after the Delta
+                // fragments so that those reads do not wait behind these
+                float sign[NC], isign[NC];
 #pragma unroll
                 for (int q = 0; q < NC; ++q) {
-                    f4 s = Sr[q][u] * cur.gam[u];
-#pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
-                    Sr[q][u] = s;
-                    lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
+                    const int col = 16 * q + m16;
+                    sign[q] = pow2_scale(mx[col] + (float)CS * mx[NCOL + col]);
+                    isign[q] = pow2_recip(sign[q]);
                 }
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) {
+                        Sr[q][u] = Sr[q][u] * cur.gam[u] + kd[q][u] * sgd[q];
+                        lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u] * isign[q]);
+                    }
+                }
+                // sigma_S of the next chunk for the output waves (parity c + 1,
+                // last read during step c - 1) and the next chunk's state
+                // maximum for its bound (the other parity, cleared before barrier (2))
+                float *mxn = &sMax[(c + 1) & 1][0];
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    sig[q] = sign[q];
+                    isig[q] = isign[q];
+                    const float ms = state_max(q);
+                    if (g4 == 0) {
+                        sSigS[(c + 1) & 1][16 * q + m16] = sign[q];
+                        lds_umax(mxn + 16 * q + m16, ms);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int ct = wv * TPW + u;
+                    if (NCT % 4 != 0 && ct >= NCT) continue;
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) {
+                        f4 s = Sr[q][u] * cur.gam[u];
+#pragma unroll
+                        for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                        Sr[q][u] = s;
+                        lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
+                    }
+                }
+                pre.load_b(blk_of(c + PD), wv, lane);
             }
-            pre.load_b(blk_of(c + PD), wv, lane);
             // A device-scope store is written through to memory and, since
             // stores and loads retire in order, would hold up this wave's
             // later operand waits; the prefetch workgroups sit on the same
@@ -1163,8 +1380,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         const int sbm1 = RPW > 1 ? (16 * RT::rt(wo, 1) + 15) / KB : 0;
         auto sbmax = [&](int j) { return j == 0 ? sbm0 : sbm1; };
         // v / w tile coordinates of this thread (rows ur + 64 x, per column
-        // tile) and where its U values go
-        const int ur = to >> 2, uc = 4 * (to & 3);
+        // tile) and where its U values go: wave wo stages rows 32 (wo / 2) ..
+        // + 31 (one 32-row block of U, the depth of one product step) and
+        // columns 8 (wo % 2) .. + 7, four consecutive columns per lane
+        const int ur = 32 * (wo >> 1) + (lane >> 1), uc = 8 * (wo & 1) + 4 * (lane & 1);
         const bool urow = CS >= 64 || ur < CS;
         const size_t uoff0 = (size_t)h * DV + col0 + uc;
         const int usb = ur / KB, usl = ur % KB;
@@ -1180,15 +1399,20 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 for (int q = 0; q < NC; ++q)
                     u.q[q + NC * x].template load<WSC>(v, w, uv_off(c, x) + 16 * q, w_off(c, x), uv_ok(c, x));
         };
-        OF g0, g1, g2;
-        UV u0, u1, u2;
-        if constexpr (CS != 64) { g0.zero_tri(); g1.zero_tri(); g2.zero_tri(); }
+        OF g0, g1, g2, g3;
+        UV u0, u1, u2, u3;
+        if constexpr (CS != 64) { g0.zero_tri(); g1.zero_tri(); g2.zero_tri(); g3.zero_tri(); }
         if (nch > 0) {
-            if constexpr (!SAVE) g0.load(blk_of(0), wo, lane);
+            // v and w first: the loop reads the next chunk's rows at each step
+            // start, and the wait the compiler places at the loop's head also
+            // covers the first entry, which then finds them old enough
             uv_load(u0, 0);
-            if constexpr (RING == 3) {
-                if constexpr (!SAVE) g1.load(blk_of(1), wo, lane);
-                uv_load(u1, 1);
+            if constexpr (ORING >= 3) uv_load(u1, 1);
+            if constexpr (ORING == 4) uv_load(u2, 2);
+            if constexpr (!SAVE) {
+                g0.load(blk_of(0), wo, lane);
+                if constexpr (ORING >= 3) g1.load(blk_of(1), wo, lane);
+                if constexpr (ORING == 4) g2.load(blk_of(2), wo, lane);
             }
         }
         // PRO: taps and bias of the thread's columns (per column tile)
@@ -1206,6 +1430,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         // raw rows in LDS slot `slot` (and rows 61..63 of slot `pslot` for the
         // rows before it), its own row and w in registers; zero past the end
         f4 ucarry[PRO ? NC : 1];
+#pragma unroll
+        for (int q = 0; q < (PRO ? NC : 1); ++q) ucarry[q] = f4zero();
         auto conv_u = [&](const UV &u, int slot, int pslot) {
 #pragma unroll
             for (int q = 0; q < NC; ++q) {
@@ -1238,7 +1464,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             }
             if (nch > 0) {
                 stage_v(u0, 0);
-                // rows 61..63 of slot 2 stand for the three tokens before the
+                // rows 61..63 of the last slot stand for the three tokens before the
                 // sequence: the history, or zeros
                 if (ur >= 61) {
                     const In *hv = (const In *)cv.hist;
@@ -1250,13 +1476,36 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                             for (int e = 0; e < 4; ++e) x[e] = in2f<In>(hp[e]);
                         }
-                        *reinterpret_cast<f4 *>(&sVr[2][ur * LDV + 16 * q + uc]) = x;
+                        *reinterpret_cast<f4 *>(&sVr[ORING - 1][ur * LDV + 16 * q + uc]) = x;
                     }
                 }
             }
             __syncthreads();   // pairs with the state waves' barrier before their loop
-            if (nch > 0) conv_u(u0, 0, 2);
+            if (nch > 0) conv_u(u0, 0, ORING - 1);
         }
+        // U = w * v of one chunk (the prologue form keeps it in ucarry)
+        auto u_val = [&](const UV &u, int q, int x, int e) {
+            if constexpr (PRO) return ucarry[q][e];
+            else {
+                const UVTile<In> &uq = u.q[q + NC * x];
+                return uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+            }
+        };
+        // sigma_U of this wave's U block for column 16q + uc + e (rows ur + 64x),
+        // from the block's own values: the max over the wave's lanes of one
+        // parity (rotations by 2, 4, 8 within 16-lane rows, then the swaps)
+        auto u_scale = [&](const UV &u, int q, int x, int e) {
+            float m = urow ? fabsf(u_val(u, q, x, e)) : 0.f;
+            auto ror = [](float y, auto ctrl) {
+                return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), decltype(ctrl)::value, 0xF,
+                                                                  0xF, false));
+            };
+            m = fmaxf(m, ror(m, std::integral_constant<int, 0x122>{}));   // row_ror:2
+            m = fmaxf(m, ror(m, std::integral_constant<int, 0x124>{}));   // row_ror:4
+            m = fmaxf(m, ror(m, std::integral_constant<int, 0x128>{}));   // row_ror:8
+            return pow2_scale(colmax_lanes(m));
+        };
+        if constexpr (SCL) __syncthreads();   // pairs with the state waves' barrier for the first chunk's maxima
         // o tiles go through LDS (double-buffered) and leave as 16-byte
         // stores (CS * NC / 64 per thread) after the next barrier
         auto store_o = [&](int c) {
@@ -1270,31 +1519,50 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         *reinterpret_cast<const f4 *>(&sO[c & 1][row * LDO + 4 * q4]);
             }
         };
-        // `sl` = c % 3 (a constant at every call site). Under PRO, U of chunk
+        // `sl` = c % ORING (a constant at every call site). Under PRO, U of chunk
         // c was formed during the previous step (ucarry); this step stages
-        // the raw v rows of chunk c + 1 in slot (c + 1) % 3 before the first
+        // the raw v rows of chunk c + 1 in slot (c + 1) % ORING before the first
         // barrier and forms its U after it, where these waves would wait.
         auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &unext, UV &upre, int sl) {
-            const int sln = sl == 2 ? 0 : sl + 1;
+            const int sln = sl == ORING - 1 ? 0 : sl + 1;
             if constexpr (PRO) stage_v(unext, sln);
             if (urow) {
 #pragma unroll
                 for (int x = 0; x < UR; ++x)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q)
+                    for (int q = 0; q < NC; ++q) {
+                        f4 sgu;   // sigma_U of this block for the lane's four columns
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sgu[e] = SCL ? u_scale(ucur, q, x, e) : 1.f;
+                        const int sbx = usb + 64 * x / KB;
+                        if constexpr (SCL) {
+                            // one lane of each parity holds the wave's block scales
+                            // (every block of the chunk has rows in some wave)
+                            if (lane < 2) *reinterpret_cast<f4 *>(&sSigU[sbx][16 * q + uc]) = sgu;
+                        }
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const UVTile<In> &uq = ucur.q[q + NC * x];
-                            float uu;
-                            if constexpr (PRO) uu = ucarry[q][e];
-                            else uu = uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                            float uu = u_val(ucur, q, x, e);
+                            if constexpr (SCL) uu *= pow2_recip(sgu[e]);   // exact (a power of two)
                             const Op hi = (Op)uu;
-                            const int ln = (uc + e) + 16 * ug, sbx = usb + 64 * x / KB;
+                            const int ln = (uc + e) + 16 * ug;
                             sU[q][((0 * NSB + sbx) * 64 + ln) * NE + ui] = hi;
                             sU[q][((1 * NSB + sbx) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
                         }
+                    }
             }
             __syncthreads();   // (1)
+            // sigma_S and sigma_D of the o tile's column, for after barrier (2)
+            float sgs[NC], sgd[NC];
+            if constexpr (SCL && !SAVE) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    sgs[q] = sSigS[c & 1][16 * q + m16];
+                    sgd[q] = sgs[q];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) sgd[q] = fmaxf(sgd[q], sSigU[sb][16 * q + m16]);
+                }
+            }
             // The previous chunk's o tile goes out here, ahead of this
             // step's loads, with per-channel gates given as they are; with one
             // w per token and head (fewer loads) or with the fused prologue
@@ -1302,20 +1570,21 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             // is the faster one for its form (pass at T = 64K, H = 16: 0.802 ->
             // 0.777 ms; 0.790 against 0.823 ms; 0.892 against 0.922 ms).
             if (!SAVE && !WSC && !PRO && c > 0) store_o(c - 1);
-            if constexpr (!SAVE) pre.load(blk_of(c + PD), wo, lane);
-            uv_load(upre, c + PD);
+            if constexpr (!SAVE) pre.load(blk_of(c + OPD), wo, lane);
+            uv_load(upre, c + OPD);
             if constexpr (PRO) conv_u(unext, sln, sl);
             if constexpr (SAVE) {
                 __syncthreads();   // (2)
                 return;
             }
             if ((WSC || PRO) && c > 0) store_o(c - 1);
-            f4 oacc[RPW][NC];
+            // O = sigma_S Q+ (S / sigma_S) + sigma_D P (Delta / sigma_D)
+            f4 oacc[RPW][NC], oacd[RPW][NC];
             if (RT::ALL || rows) {
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) oacc[j][q] = f4zero();
+                    for (int q = 0; q < NC; ++q) { oacc[j][q] = f4zero(); oacd[j][q] = f4zero(); }
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -1336,21 +1605,35 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
-                            oacc[j][q] = M::mma(cur.Pm[j][sb], df, oacc[j][q]);
+                            if constexpr (SCL) oacd[j][q] = M::mma(cur.Pm[j][sb], df, oacd[j][q]);
+                            else oacc[j][q] = M::mma(cur.Pm[j][sb], df, oacc[j][q]);
                         }
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q)
+                    for (int q = 0; q < NC; ++q) {
+                        f4 ov = oacc[j][q];
+                        if constexpr (SCL) ov = ov * sgs[q] + oacd[j][q] * sgd[q];
 #pragma unroll
                         for (int ii = 0; ii < 4; ++ii)
-                            sO[c & 1][(16 * RT::rt(wo, j) + 4 * g4 + ii) * LDO + 16 * q + m16] = oacc[j][q][ii];
+                            sO[c & 1][(16 * RT::rt(wo, j) + 4 * g4 + ii) * LDO + 16 * q + m16] = ov[ii];
+                    }
             }
         };
         int c = 0;
-        if constexpr (RING == 3) {
+        if constexpr (ORING == 4) {
+            for (; c + 4 <= nch; c += 4) {
+                step(c, g0, g3, u0, u1, u3, 0);
+                step(c + 1, g1, g0, u1, u2, u0, 1);
+                step(c + 2, g2, g1, u2, u3, u1, 2);
+                step(c + 3, g3, g2, u3, u0, u2, 3);
+            }
+            if (c < nch) step(c, g0, g3, u0, u1, u3, 0);
+            if (c + 1 < nch) step(c + 1, g1, g0, u1, u2, u0, 1);
+            if (c + 2 < nch) step(c + 2, g2, g1, u2, u3, u1, 2);
+        } else if constexpr (ORING == 3) {
             for (; c + 3 <= nch; c += 3) {
                 step(c, g0, g2, u0, u1, u2, 0);
                 step(c + 1, g1, g0, u1, u2, u0, 1);

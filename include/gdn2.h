@@ -49,6 +49,9 @@ typedef enum {
     GDN2_ERR_HIP = 4          /* the HIP runtime reported an error            */
 } gdn2_status;
 
+/* Values of the in_dtype / out_dtype arguments. Those arguments are plain
+ * ints, so that any value a caller passes is well defined on the library's
+ * side; a value that is not one of these gives GDN2_ERR_INVALID. */
 typedef enum {
     GDN2_F32 = 0,
     GDN2_BF16 = 1
@@ -87,7 +90,7 @@ const char *gdn2_status_string(int status);
  * will pass cu_seqlens (then B must be 1 and T is the total token count).
  */
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
-                                      gdn2_dtype in_dtype, int varlen);
+                                      int in_dtype, int varlen);
 
 /*
  * Prefill forward over a batch, chunkwise (64-token chunks, WY form: the
@@ -110,11 +113,20 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv
  * Supported head dims: dk in {32, 64, 128} for bf16 inputs and
  * {16, 32, 64, 128} for f32 inputs; dv in {16, 32, 64, 128}.
  * workspace: device memory of at least gdn2_chunk_fwd_workspace_bytes(...).
+ *
+ * Value range (bf16 inputs, whose products run on f16 matrix cores): q_t
+ * and k_t must have at most unit L2 norm per token and head, as the layer's
+ * L2 normalisation gives them (bf16 rounding aside; "Gated DeltaNet-2 Guide",
+ * section "2. Normalization and Short Convolutions"). v, w, S0 and the state
+ * have no bound: every value column of the state, of w * v and of the
+ * corrected writes is carried through the f16 products with its own power of
+ * two scale, chosen each chunk, so large states stay finite and small ones
+ * keep full precision. fp32 inputs run on fp32 matrix cores.
  */
 int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                    const void *b, const void *w, const float *S0, void *o, float *ST,
                    const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                   gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                   int in_dtype, int out_dtype, void *workspace,
                    size_t workspace_bytes);
 
 /*
@@ -128,7 +140,7 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
 int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const float *log_alpha,
                          const void *b, const void *w, int gates, const float *S0, void *o, float *ST,
                          const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, void *workspace,
+                         int in_dtype, int out_dtype, void *workspace,
                          size_t workspace_bytes);
 
 /*
@@ -147,11 +159,11 @@ int gdn2_chunk_fwd_gates(const void *q, const void *k, const void *v, const floa
  * compute unit's 160 KB of LDS).
  */
 size_t gdn2_chunk_fwd_sized_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
-                                            gdn2_dtype in_dtype, int varlen, int chunk);
+                                            int in_dtype, int varlen, int chunk);
 int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const float *log_alpha,
                          const void *b, const void *w, const float *S0, void *o, float *ST,
                          const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                         gdn2_dtype in_dtype, gdn2_dtype out_dtype, int chunk, void *workspace,
+                         int in_dtype, int out_dtype, int chunk, void *workspace,
                          size_t workspace_bytes);
 
 /*
@@ -170,7 +182,7 @@ int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const floa
  */
 int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
-                     int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+                     int dv, int in_dtype, int out_dtype);
 
 /*
  * gdn2_decode_step with the gate layouts given by `gates`: b, w and
@@ -179,7 +191,7 @@ int gdn2_decode_step(const void *q, const void *k, const void *v, const float *l
  */
 int gdn2_decode_step_gates(const void *q, const void *k, const void *v, const float *log_alpha,
                            const void *b, const void *w, int gates, float *S, void *o, int N, int H, int dk,
-                           int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+                           int dv, int in_dtype, int out_dtype);
 
 /*
  * Fused input prologue. The layer computes the mixer's inputs from its
@@ -234,7 +246,7 @@ typedef struct gdn2_short_conv {
 int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
                             const void *b_logit, const void *w_logit, const gdn2_short_conv *conv,
                             const float *S0, void *o, float *ST, const int32_t *cu_seqlens, int B, int T,
-                            int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype,
+                            int N, int H, int dk, int dv, int in_dtype, int out_dtype,
                             void *workspace, size_t workspace_bytes);
 
 /*
@@ -246,7 +258,7 @@ int gdn2_chunk_fwd_prologue(const void *q_raw, const void *k_raw, const void *v_
  */
 int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *v_raw, const float *log_alpha,
                               const void *b_logit, const void *w_logit, const gdn2_short_conv *conv, float *S,
-                              void *o, int N, int H, int dk, int dv, gdn2_dtype in_dtype, gdn2_dtype out_dtype);
+                              void *o, int N, int H, int dk, int dv, int in_dtype, int out_dtype);
 
 /*
  * Backward of gdn2_chunk_fwd: the gradients of a scalar loss L with respect
@@ -272,12 +284,12 @@ int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *
  * tokens the decay factors stay inside fp32 range.
  */
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
-                                      gdn2_dtype in_dtype, int varlen);
+                                      int in_dtype, int varlen);
 
 int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
                    const void *b, const void *w, const float *S0, const float *dO, const float *dST,
                    const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                   gdn2_dtype in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                   int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
                    float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes);
 
 /*

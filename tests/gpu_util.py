@@ -61,7 +61,7 @@ def rel_max(x, ref):
     return err / rms if rms > 0 else err, err, rms
 
 
-def assert_close(x, ref, dtype, what):
+def assert_close(x, ref, dtype, what, quiet=False):
     """fp32 inputs: max-abs <= 1e-4. bf16 inputs: max-abs <= 2e-2 * RMS(ref)."""
     assert np.all(np.isfinite(x)), f'{what}: non-finite values'
     r, err, rms = rel_max(x, ref)
@@ -69,5 +69,6 @@ def assert_close(x, ref, dtype, what):
         assert err <= TOL_F32, f'{what}: max abs error {err:.3e} > {TOL_F32}'
     else:
         assert r <= TOL_BF16, f'{what}: max abs error {err:.3e} = {r:.3e} x RMS {rms:.3e} > {TOL_BF16}'
-    print(f'{what}: max abs err {err:.3e}, / RMS {r:.3e}', flush=True)
+    if not quiet:
+        print(f'{what}: max abs err {err:.3e}, / RMS {r:.3e}', flush=True)
     return r

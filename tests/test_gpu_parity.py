@@ -100,16 +100,48 @@ def test_edit_modes(mode):
     p.w[:] = wval
     if mode == 'preserve':
         p.log_alpha[:] = 0.0
-    if mode != 'erase':
-        check_prefill(p, f'mode {mode}')
-        return
-    # Pure erase drives the state to ~0 (RMS ~1e-6), where a bar relative to
-    # the reference RMS is meaningless; hold o to the relative bar and the
-    # vanished state to the absolute fp32 bar instead.
-    o, ST = run_prefill(p)
-    o_ref, ST_ref = oracle_prefill(p)
-    assert_close(o, o_ref, p.dtype, 'mode erase o')
-    assert_close(ST, ST_ref, 'f32', 'mode erase S_T (absolute)')
+    # Pure erase over 150 tokens drives the state towards 0 (RMS ~1e-6): the
+    # pass carries each value column with its own power-of-two scale, so the
+    # small state keeps full f16 precision and meets the relative bar too.
+    check_prefill(p, f'mode {mode}')
+
+
+def test_pure_erase_keeps_orthogonal_complement():
+    """Pure erase (b = 1, w = 0, alpha = 1) with fewer tokens (64) than key
+    channels (128): each step removes the state's component along k_t, so S_T
+    keeps S0's projection on the complement of the keys' span (RMS ~ 0.7 x
+    RMS(S0)), and a zero, unchanged or wrongly erased state fails the
+    relative bar (aifetchly, "The Four Modes of Expressive Memory Editing",
+    pure erase)."""
+    p = gi.prefill(610, [64, 40], H=2, dk=128, dv=128, dtype='bf16', s0_std=0.05, uniform=False)
+    p.b[:] = 1.0
+    p.w[:] = 0.0
+    p.log_alpha[:] = 0.0
+    o, ST = check_prefill(p, 'pure erase, T < dk')
+    # the complement of the keys' span survives: S_T is far from 0 and from S0
+    assert np.sqrt(np.mean(ST ** 2)) > 0.3 * np.sqrt(np.mean(p.S0 ** 2))
+    assert np.max(np.abs(ST - p.S0)) > 0.1 * np.sqrt(np.mean(p.S0 ** 2))
+
+
+@pytest.mark.parametrize('scale', ['large', 'small'])
+def test_state_beyond_f16_range(scale):
+    """A state and writes far outside f16's normal range: 'large' has
+    S0 ~ N(0, 3e4^2) and v ~ N(0, 1e3^2), so with no erase (b = 0) and almost
+    no decay (log alpha = -1e-5) the state and o pass 65504 (f16's largest
+    value) from the first chunk to the last; 'small' has S0 and v near 1e-6,
+    below f16's normal range (6.1e-5). bf16 inputs hold both, so the relative
+    bar applies to o and S_T."""
+    p = gi.prefill(620, [8192, 301], H=2, dk=128, dv=128, dtype='bf16', s0_std=1.0, uniform=False)
+    s0, sv = (3e4, 1e3) if scale == 'large' else (3e-6, 1e-6)
+    p.S0 = (p.S0 * np.float32(s0)).astype(np.float32)
+    p.v = gi.bf16_round(p.v * np.float32(sv))
+    p.b[:] = 0.0
+    p.log_alpha[:] = -1e-5
+    o, ST = check_prefill(p, f'state range {scale}')
+    if scale == 'large':
+        assert np.max(np.abs(ST)) > 65504.0 and np.max(np.abs(o)) > 65504.0
+    else:
+        assert np.max(np.abs(ST)) < 6.1e-5
 
 
 @pytest.mark.parametrize('dt,d,B,H,T', [('bf16', 128, 2, 1, 8401), ('f32', 64, 1, 2, 9000),
@@ -203,19 +235,26 @@ def test_decode_shapes(dk, dv, dt):
 
 def test_decode_workload_full_size():
     """256 sequences x 16 heads x d=128, fp32 state resident, bf16 step inputs
-    (the decode workload's launch configuration), three consecutive steps."""
+    (the decode workload's launch configuration): 100 consecutive steps, o
+    against the oracle at every step and the whole state after steps 1, 50
+    and 100."""
     c = gi.WORKLOADS['decode_n256']
     N, H, d = c['N'], c['H'], c['dk']
     S_np = gi.decode_state(c['seed'], N, H, d, d, c['s0_std'])
     S = dev(S_np, torch.float32)
-    for step in (1, 2, 3):
+    bf = torch.bfloat16
+    worst = 0.0
+    for step in range(1, 101):
         st = gi.decode_step(c['seed'], step, N, H, d, d)
-        bf = torch.bfloat16
         o = gdn2.decode_step(dev(st.q, bf), dev(st.k, bf), dev(st.v, bf), dev(st.log_alpha, torch.float32),
                              dev(st.b, bf), dev(st.w, bf), S)
         o_ref, S_np = oracle.decode_step(st.q, st.k, st.v, st.log_alpha, st.b, st.w, S_np, nthreads=threads())
-        assert_close(o.cpu().numpy(), o_ref, 'f32', f'decode workload step {step} o')
-    assert_close(S.cpu().numpy(), S_np, 'f32', 'decode workload S after 3 steps')
+        err = float(np.max(np.abs(o.cpu().numpy() - o_ref)))
+        assert err <= 1e-4, f'decode workload step {step} o: max abs error {err:.3e}'
+        worst = max(worst, err)
+        if step in (1, 50, 100):
+            assert_close(S.cpu().numpy(), S_np, 'f32', f'decode workload S after {step} steps')
+    print(f'decode workload: worst o error over 100 steps {worst:.3e}', flush=True)
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -230,11 +269,17 @@ def test_prefill_t65536_full():
     check_prefill(gi.workload('prefill_t65536', threads=threads()), 'prefill T=65536')
 
 
-def test_varlen_32seq_full_sampled():
+def test_varlen_32seq_full():
     """32 packed sequences (lengths U[512, 16384]), H=32, half the heads with
-    scalar gates; the GPU runs the whole packed batch, the oracle checks a
-    sample of sequences (shortest, longest and two others) on all heads."""
+    scalar gates, per-sequence S0: every sequence and head, o and S_T, against
+    the oracle over the whole packed batch."""
     p = gi.workload('varlen_32seq', threads=threads())
-    lens = np.diff(p.cu_seqlens)
-    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 17})
-    check_prefill(p, 'varlen 32 seqs', seqs=seqs)
+    o, ST = run_prefill(p)
+    o_ref, ST_ref = oracle_prefill(p)
+    for i in range(p.N):
+        s = slice(int(p.cu_seqlens[i]), int(p.cu_seqlens[i + 1]))
+        for h in range(p.H):
+            assert_close(o[s, h], o_ref[s, h], p.dtype, f'varlen seq {i} head {h} o', quiet=True)
+            assert_close(ST[i, h], ST_ref[i, h], p.dtype, f'varlen seq {i} head {h} S_T', quiet=True)
+    assert_close(o, o_ref, p.dtype, 'varlen 32 seqs o (all)')
+    assert_close(ST, ST_ref, p.dtype, 'varlen 32 seqs S_T (all)')
