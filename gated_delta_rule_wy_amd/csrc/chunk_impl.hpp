@@ -842,51 +842,65 @@ template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, i
     *reinterpret_cast<op4 *>(dst + lane * 4) = y;
 }
 
-// ---- per-column scales of the f16 tiles ------------------------------------
+// ---- tile scales of the f16 operands ---------------------------------------
 // The pass rounds the state S, the writes U = w * v and the corrected writes
 // Delta to f16 for the matrix cores. Value columns of the state evolve
-// independently (the transition acts on the key axis only), so column j of
-// each may be carried as X[:, j] / sigma_j with its own power of two sigma_j:
-// every product is then an exact multiple of the unscaled one. A scale maps
-// its bound B into [2^9, 2^10): far from f16's overflow at 2^16 and from its
-// subnormals below 2^-14, whatever the magnitude of the state (unscaled, a
-// state near 1e-6 kept ~4 significant bits and one past 65504 became inf).
-//  * S_{c+1}: B = max|S_c[:, j]| + CS max|Delta_c[:, j]| (keys of at most
-//    unit norm, every decay factor <= 1), from maxima exchanged in LDS during
-//    step c;
-//  * U: each 32-row block (one contraction step of T U) from its own values;
-//  * Delta_c: the largest of the two above, per column; |Delta| is the
-//    token recurrence's corrected write, within a few times |U| + |S|.
-// 2^e with B / 2^e in [2^9, 2^10) for B > 0, |e| <= 100; 0 for B = 0 (a
-// quantity that is all zero takes no part in the max that forms sigma_D,
-// and scaling zeros by 1 / 0 below keeps them zero)
-__device__ __forceinline__ float pow2_scale(float B)
-{
-    const int e = min(max((int)((__float_as_uint(B) >> 23) & 0xFF) - 127 - 9, -100), 100);
-    return B > 0.f ? __uint_as_float((uint32_t)(e + 127) << 23) : 0.f;
-}
-// 1 / s for s = 2^e, |e| <= 100 (exact); 2^127 for s = 0, which only ever
-// multiplies zeros
-__device__ __forceinline__ float pow2_recip(float s) { return __uint_as_float(0x7F000000u - __float_as_uint(s)); }
+// independently (the transition acts on the key axis only), so the columns
+// of a 16-column tile may be carried divided by a power of two 2^e of their
+// own: every product is then an exact multiple of the unscaled one. One
+// exponent per chunk and tile serves S_c, U_c and Delta_c = T U_c - W S_c
+// alike, so the products need no rescaling between them, and the state
+// registers hold S_c / 2^e too. The exponent maps a bound B on the three
+// into [2^9, 2^10): far from f16's overflow at 2^16 and from its subnormals
+// below 2^-14 (unscaled, a state near 1e-6 kept ~4 significant bits and one
+// past 65504 became inf). For chunk c + 1 (keys of at most unit norm, every
+// decay factor <= 1):
+//   |S_{c+1}| <= max|S_c| + CS max|Delta_c| <= 2 max(max|S_c|, CS max|Delta_c|),
+//   B = max(that, max|U_{c+1}|),
+// the maxima gathered in LDS during step c. A tile far below the largest of
+// the three keeps its relative precision down to 2^-14 of 2^9.
 
-// max over the lanes n, n + 16, n + 32, n + 48 (the four row groups of one
-// accumulator-tile column), with gfx950's lane swaps: permlane16_swap pairs
-// each odd 16-lane row with the even row below it and permlane32_swap the
-// two halves; of the two results one is the lane's own value and the other
-// its partner's, whichever half the lane sits in
-__device__ __forceinline__ float colmax_lanes(float x)
+// exponent e of the scale for a bound B >= 0 given as its bits: B / 2^e in
+// [2^9, 2^10), clamped to [-100, 100] (B = 0 and subnormal B give -100)
+__device__ __forceinline__ int scale_exp(uint32_t Bbits)
 {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return min(max((int)(Bbits >> 23) - 127 - 9, -100), 100);
+}
+// 2^e for e in [-126, 127] (exact)
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Maxima of magnitudes as bit patterns: for non-negative floats the
+// unsigned order is the float order, so the lane exchanges below and the
+// LDS atomics take them as integers.
+// max over each 16-lane row, in every lane of the row (quad swaps, then the
+// row's half mirror and mirror)
+__device__ __forceinline__ uint32_t rowmax16(uint32_t m)
+{
+    auto dpp = [](uint32_t y, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, decltype(ctrl)::value, 0xF, 0xF, true);
+    };
+    m = max(m, dpp(m, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+    m = max(m, dpp(m, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+    m = max(m, dpp(m, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+    return max(m, dpp(m, std::integral_constant<int, 0x140>{}));   // row_mirror
+}
+// max over the whole wave, in every lane: the rows, then across them with
+// gfx950's lane swaps (permlane16_swap pairs each odd 16-lane row with the
+// even row below it and permlane32_swap the two halves; of the two results
+// one is the lane's own value and the other its partner's)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x)
+{
+    x = rowmax16(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max(b[0], b[1]);
 }
 
-// LDS running maximum of one step (non-negative floats compare as their bit
-// patterns)
-__device__ __forceinline__ void lds_umax(float *p, float x)
+// LDS running maximum, on magnitude bit patterns
+__device__ __forceinline__ void lds_umax(float *p, uint32_t x)
 {
-    atomicMax(reinterpret_cast<unsigned int *>(p), __float_as_uint(x));
+    atomicMax(reinterpret_cast<unsigned int *>(p), x);
 }
 
 // L2 prefetch workgroups. A pass workgroup holds a bounded number of
@@ -1027,21 +1041,25 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     __shared__ __attribute__((aligned(16))) float sO[2][CS * LDO];          // o tiles
     constexpr int LDV = 16 * NC;                                             // raw-v row stride (floats)
     __shared__ __attribute__((aligned(16))) float sVr[PRO ? ORING : 1][PRO ? 64 * LDV : 4];   // PRO: raw v rows
-    // f16 tiles carry per-column power-of-two scales (pow2_scale above);
-    // fp32 operands need none. The state tiles take sigma_S from the bound
-    // max|S_c| + CS max|Delta_c| on the next state; each 32-row block of U
-    // takes its own sigma_U from its values (one output wave stages one
-    // block, so no exchange is needed before the tile is written); Delta takes
-    // sigma_D = max(sigma_S, sigma_U of every block) per column.
+    // f16 tiles carry a power-of-two scale per chunk and 16-column tile
+    // (scale_exp above); fp32 operands need none
     constexpr bool SCL = std::is_same<Op, _Float16>::value;
-    constexpr int NCOL = 16 * NC;
-    // step maxima by parity of the chunk: [state | corrected writes][column]
-    __shared__ __attribute__((aligned(16))) float sMax[SCL ? 2 : 1][SCL ? 2 * NCOL : 4];
-    // state maxima before the first chunk: [wave][column]
-    __shared__ __attribute__((aligned(16))) float sMax0[SCL ? 4 : 1][SCL ? NCOL : 4];
-    // sigma_S by parity of the chunk, and sigma_U of the current chunk's U blocks
-    __shared__ __attribute__((aligned(16))) float sSigS[SCL ? 2 : 1][SCL ? NCOL : 4];
-    __shared__ __attribute__((aligned(16))) float sSigU[SCL ? NSB : 1][SCL ? NCOL : 4];
+    // bound for the next chunk's scale, [parity of the step that forms it][tile]
+    // [16-lane row of the contributing lanes] (distinct words per row: LDS
+    // atomics of one wave to one word become a loop over its lanes)
+    __shared__ __attribute__((aligned(16))) float sM[2][NC][4];
+    // the first chunk's maxima, [wave][tile]
+    __shared__ __attribute__((aligned(16))) float sM0[8][NC];
+    auto first_exp = [&](int q) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) m = max(m, __float_as_uint(sM0[x][q]));
+        return scale_exp(__builtin_amdgcn_readfirstlane(m));
+    };
+    auto next_exp = [&](int c, int q) {
+        const uint4 m = *reinterpret_cast<const uint4 *>(&sM[c & 1][q][0]);
+        return scale_exp(__builtin_amdgcn_readfirstlane(max(max(m.x, m.y), max(m.z, m.w))));
+    };
 
     // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
     // sit on XCD c % 8
@@ -1089,29 +1107,30 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     if constexpr (!SCL) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
             }
-        // scale of column 16q + m16 for the current chunk (sigma and 1/sigma)
-        float sig[NC], isig[NC];
+        // exponent of the current chunk's scale, per column tile (uniform)
+        int esc[NC];
 #pragma unroll
-        for (int q = 0; q < NC; ++q) { sig[q] = 1.f; isig[q] = 1.f; }
-        // per-column max of |S| over this wave's tiles (in every lane of the column)
-        auto state_max = [&](int q) {
-            float m = 0.f;
+        for (int q = 0; q < NC; ++q) esc[q] = 0;
+        // max of |S| (of the registers as they stand) over this lane's values in tile q
+        auto state_lmax = [&](int q) {
+            float m = 0.f;   // (|x| is a free source modifier of the float max)
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 if (NCT % 4 != 0 && wv * TPW + u >= NCT) continue;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) m = fmaxf(m, fabsf(Sr[q][u][ii]));
             }
-            return colmax_lanes(m);
+            return m;
         };
         if constexpr (SCL) {
-            if (wv == 0)
-                for (int x = lane; x < 2 * NCOL; x += 64) sMax[0][x] = 0.f;
+            // this wave's part of the first chunk's maxima (S_0; the output
+            // waves put U_0's), and step 0's bound buffer cleared
 #pragma unroll
             for (int q = 0; q < NC; ++q) {
-                const float m = state_max(q);
-                if (g4 == 0) sMax0[wv][16 * q + m16] = m;
+                const uint32_t m = wave_umax(__float_as_uint(state_lmax(q)));
+                if (lane == 0) sM0[wv][q] = __uint_as_float(m);
             }
+            if (wv == 0 && lane < 4 * NC) (&sM[0][0][0])[lane] = 0.f;
         }
         const bool rows = RT::active(wv);
         // last stored k-block of T / P for the wave's row tile j (RPW <= 2)
@@ -1130,24 +1149,18 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         }
         if constexpr (PRO) __syncthreads();   // pairs with the output waves' staging of chunk 0
         if constexpr (SCL) {
-            __syncthreads();   // the first chunk's state maxima
+            __syncthreads();   // the first chunk's maxima
 #pragma unroll
             for (int q = 0; q < NC; ++q) {
-                float m = 0.f;
-#pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) m = fmaxf(m, sMax0[w4][16 * q + m16]);
-                sig[q] = pow2_scale(m);
-                isig[q] = pow2_recip(sig[q]);
-                if (g4 == 0) sSigS[0][16 * q + m16] = sig[q];
+                esc[q] = first_exp(q);
+                const float r = exp2i(-esc[q]);
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {
                     const int ct = wv * TPW + u;
-                    if (ct < NCT) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u] * isig[q]);
+                    if (ct >= NCT) continue;
+                    Sr[q][u] = Sr[q][u] * r;
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
-                // the first chunk's state maximum for the step-0 bound (buffer 0,
-                // cleared before the barrier above)
-                const float ms = state_max(q);
-                if (g4 == 0) lds_umax(&sMax[0][16 * q + m16], ms);
             }
         }
         // The prefetch of chunk c+PD is split over the two windows in which
@@ -1162,39 +1175,27 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     for (int u = 0; u < TPW; ++u) {
                         const int ct = wv * TPW + u;
                         if (NCT % 4 != 0 && ct >= NCT) continue;
-                        tile_store<Op>(sp + ((size_t)ct * (DV / 16) + NC * js + q) * 256, lane, Sr[q][u]);
+                        tile_store<Op>(sp + ((size_t)ct * (DV / 16) + NC * js + q) * 256, lane,
+                                       SCL ? Sr[q][u] * exp2i(esc[q]) : Sr[q][u]);
                     }
             }
             __syncthreads();   // (1) state tiles and U ready
-            // sigma_U of the chunk's 32-row U blocks and sigma_D, for this lane's column
-            float sgu[NC][NSB], sgd[NC], isgd[NC];
+            // clear the other parity's bound for the next step (its last
+            // readers passed barrier (1))
             if constexpr (SCL) {
-#pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    sgd[q] = sig[q];
-#pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) {
-                        sgu[q][sb] = sSigU[sb][16 * q + m16];
-                        sgd[q] = fmaxf(sgd[q], sgu[q][sb]);
-                    }
-                    isgd[q] = pow2_recip(sgd[q]);
-                }
+                if (wv == 0 && lane < 4 * NC) (&sM[(c + 1) & 1][0][0])[lane] = 0.f;
             }
-            float mD[NC];   // per-column max of |Delta| over this wave's rows
+            // this lane's max |S_c| and max |Delta_c| per tile (in units of the scale)
+            float mS[NC], mD[NC];
 #pragma unroll
-            for (int q = 0; q < NC; ++q) mD[q] = 0.f;
+            for (int q = 0; q < NC; ++q) { mS[q] = 0.f; mD[q] = 0.f; }
             if (RT::ALL || rows) {
-                // T U per U block (each block has its own scale), then -W S
-                constexpr int NA = SCL ? NSB : 1;
-                f4 acc[RPW][NC][NA], accw[RPW][NC];
+                // T U, then -W S (both divided by the chunk's scale)
+                f4 acc[RPW][NC], accw[RPW][NC];
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) {
-                        accw[j][q] = f4zero();
-#pragma unroll
-                        for (int a = 0; a < NA; ++a) acc[j][q][a] = f4zero();
-                    }
+                    for (int q = 0; q < NC; ++q) { acc[j][q] = f4zero(); accw[j][q] = f4zero(); }
                 // every B fragment is read from LDS before the products, so
                 // that the reads overlap rather than each wait on its own
                 frag sfr[NC][NKB];
@@ -1205,7 +1206,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
                     if (RPW == 1 && sb > sbmax(0)) break;
-                    const int a = SCL ? sb : 0;
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
                         const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
@@ -1213,8 +1213,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
-                            acc[j][q][a] = M::mma(cur.Ti[j][sb], uh, acc[j][q][a]);
-                            acc[j][q][a] = M::mma(cur.Ti[j][sb], ul, acc[j][q][a]);
+                            acc[j][q] = M::mma(cur.Ti[j][sb], uh, acc[j][q]);
+                            acc[j][q] = M::mma(cur.Ti[j][sb], ul, acc[j][q]);
                         }
                     }
                 }
@@ -1224,43 +1224,46 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     for (int q = 0; q < NC; ++q)
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) accw[j][q] = M::mma(cur.nW[j][kb], sfr[q][kb], accw[j][q]);
+                // the state maxima, while the products run
+                if constexpr (SCL) {
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) mS[q] = state_lmax(q);
+                }
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        f4 d;   // Delta, unscaled
+                        const f4 d = acc[j][q] + accw[j][q];
                         if constexpr (SCL) {
-                            d = accw[j][q] * sig[q];
-#pragma unroll
-                            for (int a = 0; a < NA; ++a) d += acc[j][q][a] * sgu[q][a];
 #pragma unroll
                             for (int ii = 0; ii < 4; ++ii) mD[q] = fmaxf(mD[q], fabsf(d[ii]));
-                            lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d * isgd[q]);
-                        } else {
-                            d = acc[j][q][0] + accw[j][q];
-                            lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d);
                         }
+                        lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d);
                         if constexpr (SAVE) {
                             if (j == 0) {
                                 Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
-                                tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane, d);
+                                tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane,
+                                               SCL ? d * exp2i(esc[q]) : d);
                             }
                         }
                     }
+            } else if constexpr (SCL) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) mS[q] = state_lmax(q);
             }
             // the prefetch goes out ahead of the maxima below: the compiler
             // does not move global loads across their LDS atomics
             pre.load_a(blk_of(c + PD), wv, lane);
-            float *mx = &sMax[SCL ? (c & 1) : 0][0];
             if constexpr (SCL) {
-                // clear the other parity for the next chunk (its last readers
-                // passed barrier (1)); add this wave's maxima of Delta_c
-                if (wv == 0)
-                    for (int x = lane; x < 2 * NCOL; x += 64) sMax[(c + 1) & 1][x] = 0.f;
+                // this wave's part of the bound on S_{c+1}: 2 max(|S_c|, CS |Delta_c|),
+                // unscaled, per 16-lane row, added by the rows' first lanes
+                uint32_t mr[NC];
 #pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    const float md = colmax_lanes(mD[q]);
-                    if (g4 == 0) lds_umax(mx + NCOL + 16 * q + m16, md);
+                for (int q = 0; q < NC; ++q)
+                    mr[q] = rowmax16(__float_as_uint(fmaxf(mS[q], (float)CS * mD[q]) * exp2i(esc[q] + 1)));
+                if (m16 == 0) {
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) lds_umax(&sM[c & 1][q][g4], mr[q]);
                 }
             }
             __syncthreads();   // (2) Delta tiles ready
@@ -1269,69 +1272,49 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) Db[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+            // the next chunk's exponents, read after the Delta fragments so
+            // that those reads do not wait behind these
+            int en[NC];
             if constexpr (SCL) {
-                // S <- gamma S + sigma_D Khat^T (Delta / sigma_D), products first
-                f4 kd[NC][TPW];
 #pragma unroll
-                for (int u = 0; u < TPW; ++u) {
-                    if (NCT % 4 != 0 && wv * TPW + u >= NCT) continue;
+                for (int q = 0; q < NC; ++q) en[q] = next_exp(c, q);
+            }
+            // S_{c+1} = gamma S_c + Khat^T Delta_c, in units of the chunk's
+            // scale: the products accumulate onto the decayed state
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) {
-                        f4 s = f4zero();
-#pragma unroll
-                        for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
-                        kd[q][u] = s;
-                    }
-                }
-                pre.load_b(blk_of(c + PD), wv, lane);
-                // the next chunk's sigma_S from the bound, read after the Delta
-                // fragments so that those reads do not wait behind these
-                float sign[NC], isign[NC];
+            for (int u = 0; u < TPW; ++u) {
+                const int ct = wv * TPW + u;
+                if (NCT % 4 != 0 && ct >= NCT) continue;
 #pragma unroll
                 for (int q = 0; q < NC; ++q) {
-                    const int col = 16 * q + m16;
-                    sign[q] = pow2_scale(mx[col] + (float)CS * mx[NCOL + col]);
-                    isign[q] = pow2_recip(sign[q]);
+                    f4 s = Sr[q][u] * cur.gam[u];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                    Sr[q][u] = s;
+                    if constexpr (!SCL) lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
+                }
+            }
+            pre.load_b(blk_of(c + PD), wv, lane);
+            if constexpr (SCL) {
+                // into the next chunk's units (a power of two: exact). Always
+                // multiplied: a branch that skipped this where the exponent
+                // stays gave wrong, run-to-run varying states (its untaken path
+                // reused the product registers a few instructions after the
+                // matrix instruction that writes them).
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    const float r = exp2i(min(max(esc[q] - en[q], -126), 127));
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u) Sr[q][u] = Sr[q][u] * r;
+                    esc[q] = en[q];
                 }
 #pragma unroll
                 for (int u = 0; u < TPW; ++u) {
                     const int ct = wv * TPW + u;
                     if (NCT % 4 != 0 && ct >= NCT) continue;
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) {
-                        Sr[q][u] = Sr[q][u] * cur.gam[u] + kd[q][u] * sgd[q];
-                        lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u] * isign[q]);
-                    }
+                    for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
                 }
-                // sigma_S of the next chunk for the output waves (parity c + 1,
-                // last read during step c - 1) and the next chunk's state
-                // maximum for its bound (the other parity, cleared before barrier (2))
-                float *mxn = &sMax[(c + 1) & 1][0];
-#pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    sig[q] = sign[q];
-                    isig[q] = isign[q];
-                    const float ms = state_max(q);
-                    if (g4 == 0) {
-                        sSigS[(c + 1) & 1][16 * q + m16] = sign[q];
-                        lds_umax(mxn + 16 * q + m16, ms);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < TPW; ++u) {
-                    const int ct = wv * TPW + u;
-                    if (NCT % 4 != 0 && ct >= NCT) continue;
-#pragma unroll
-                    for (int q = 0; q < NC; ++q) {
-                        f4 s = Sr[q][u] * cur.gam[u];
-#pragma unroll
-                        for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
-                        Sr[q][u] = s;
-                        lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
-                    }
-                }
-                pre.load_b(blk_of(c + PD), wv, lane);
             }
             // A device-scope store is written through to memory and, since
             // stores and loads retire in order, would hold up this wave's
@@ -1366,9 +1349,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 for (int u = 0; u < TPW; ++u) {
                     const int ct = wv * TPW + u;
                     if (ct >= NCT) continue;
+                    const f4 x = SCL ? Sr[q][u] * exp2i(esc[q]) : Sr[q][u];
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii)
-                        ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = Sr[q][u][ii];
+                        ST[sbase + (size_t)(16 * ct + 4 * g4 + ii) * DV + col0 + 16 * q + m16] = x[ii];
                 }
         }
     } else {
@@ -1380,10 +1364,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         const int sbm1 = RPW > 1 ? (16 * RT::rt(wo, 1) + 15) / KB : 0;
         auto sbmax = [&](int j) { return j == 0 ? sbm0 : sbm1; };
         // v / w tile coordinates of this thread (rows ur + 64 x, per column
-        // tile) and where its U values go: wave wo stages rows 32 (wo / 2) ..
-        // + 31 (one 32-row block of U, the depth of one product step) and
-        // columns 8 (wo % 2) .. + 7, four consecutive columns per lane
-        const int ur = 32 * (wo >> 1) + (lane >> 1), uc = 8 * (wo & 1) + 4 * (lane & 1);
+        // tile) and where its U values go: four lanes per row, so that one
+        // load instruction takes 16 rows of 32 bytes (rows of 16 bytes from
+        // twice the rows made the pass 30% slower). A 32-row block of U (the
+        // depth of one product step) is staged by waves 2b and 2b + 1.
+        const int ur = to >> 2, uc = 4 * (to & 3);
         const bool urow = CS >= 64 || ur < CS;
         const size_t uoff0 = (size_t)h * DV + col0 + uc;
         const int usb = ur / KB, usl = ur % KB;
@@ -1483,29 +1468,51 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             __syncthreads();   // pairs with the state waves' barrier before their loop
             if (nch > 0) conv_u(u0, 0, ORING - 1);
         }
-        // U = w * v of one chunk (the prologue form keeps it in ucarry)
+        // U = w * v of one chunk (the prologue form keeps it in ucarry), to be
+        // multiplied by u_ok: 1, or 0 for a row past the end (a factor per
+        // lane and tile rather than a select per value, which the compiler
+        // turns into branches)
         auto u_val = [&](const UV &u, int q, int x, int e) {
             if constexpr (PRO) return ucarry[q][e];
             else {
                 const UVTile<In> &uq = u.q[q + NC * x];
-                return uq.ok ? in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]) : 0.f;
+                return in2f<In>(uq.w[e]) * in2f<In>(uq.v[e]);
             }
         };
-        // sigma_U of this wave's U block for column 16q + uc + e (rows ur + 64x),
-        // from the block's own values: the max over the wave's lanes of one
-        // parity (rotations by 2, 4, 8 within 16-lane rows, then the swaps)
-        auto u_scale = [&](const UV &u, int q, int x, int e) {
-            float m = urow ? fabsf(u_val(u, q, x, e)) : 0.f;
-            auto ror = [](float y, auto ctrl) {
-                return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), decltype(ctrl)::value, 0xF,
-                                                                  0xF, false));
-            };
-            m = fmaxf(m, ror(m, std::integral_constant<int, 0x122>{}));   // row_ror:2
-            m = fmaxf(m, ror(m, std::integral_constant<int, 0x124>{}));   // row_ror:4
-            m = fmaxf(m, ror(m, std::integral_constant<int, 0x128>{}));   // row_ror:8
-            return pow2_scale(colmax_lanes(m));
+        auto u_ok = [&](const UV &u, int q, int x) {
+            if constexpr (PRO) return 1.f;
+            else return u.q[q + NC * x].ok ? 1.f : 0.f;
         };
-        if constexpr (SCL) __syncthreads();   // pairs with the state waves' barrier for the first chunk's maxima
+        // max |U| over this lane's values of tile q (rows ur + 64 x)
+        auto u_lmax = [&](const UV &u, int q) {
+            float mf = 0.f;
+            if (urow) {
+#pragma unroll
+                for (int x = 0; x < UR; ++x) {
+                    float mx = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(u_val(u, q, x, e)));
+                    mf = fmaxf(mf, mx * u_ok(u, q, x));
+                }
+            }
+            return __float_as_uint(mf);
+        };
+        // exponent of the current chunk's scale per column tile, as the state
+        // waves hold it (both read the same maxima)
+        int eo[NC];
+#pragma unroll
+        for (int q = 0; q < NC; ++q) eo[q] = 0;
+        if constexpr (SCL) {
+            // this wave's part of the first chunk's maxima (U_0; ucarry with the prologue)
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                const uint32_t m = nch > 0 ? wave_umax(u_lmax(u0, q)) : 0u;
+                if (lane == 0) sM0[4 + wo][q] = __uint_as_float(m);
+            }
+            __syncthreads();   // pairs with the state waves' barrier for the first chunk's maxima
+#pragma unroll
+            for (int q = 0; q < NC; ++q) eo[q] = first_exp(q);
+        }
         // o tiles go through LDS (double-buffered) and leave as 16-byte
         // stores (CS * NC / 64 per thread) after the next barrier
         auto store_o = [&](int c) {
@@ -1531,19 +1538,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 for (int x = 0; x < UR; ++x)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        f4 sgu;   // sigma_U of this block for the lane's four columns
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sgu[e] = SCL ? u_scale(ucur, q, x, e) : 1.f;
+                        // u_ok over the chunk's scale (a power of two: exact)
+                        const float f = SCL ? exp2i(-eo[q]) * u_ok(ucur, q, x) : u_ok(ucur, q, x);
                         const int sbx = usb + 64 * x / KB;
-                        if constexpr (SCL) {
-                            // one lane of each parity holds the wave's block scales
-                            // (every block of the chunk has rows in some wave)
-                            if (lane < 2) *reinterpret_cast<f4 *>(&sSigU[sbx][16 * q + uc]) = sgu;
-                        }
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            float uu = u_val(ucur, q, x, e);
-                            if constexpr (SCL) uu *= pow2_recip(sgu[e]);   // exact (a power of two)
+                            const float uu = u_val(ucur, q, x, e) * f;
                             const Op hi = (Op)uu;
                             const int ln = (uc + e) + 16 * ug;
                             sU[q][((0 * NSB + sbx) * 64 + ln) * NE + ui] = hi;
@@ -1552,17 +1552,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     }
             }
             __syncthreads();   // (1)
-            // sigma_S and sigma_D of the o tile's column, for after barrier (2)
-            float sgs[NC], sgd[NC];
-            if constexpr (SCL && !SAVE) {
-#pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    sgs[q] = sSigS[c & 1][16 * q + m16];
-                    sgd[q] = sgs[q];
-#pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) sgd[q] = fmaxf(sgd[q], sSigU[sb][16 * q + m16]);
-                }
-            }
             // The previous chunk's o tile goes out here, ahead of this
             // step's loads, with per-channel gates given as they are; with one
             // w per token and head (fewer loads) or with the fused prologue
@@ -1573,18 +1562,38 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             if constexpr (!SAVE) pre.load(blk_of(c + OPD), wo, lane);
             uv_load(upre, c + OPD);
             if constexpr (PRO) conv_u(unext, sln, sl);
+            // this wave's part of the bound for the next chunk's scale: max |U|
+            // of the next chunk (loaded two steps ago, or formed just above
+            // with the prologue; with a ring of two it is the load just
+            // issued), per 16-lane row, added by the rows' first lanes
+            auto next_umax = [&]() {
+                if constexpr (SCL) {
+                    uint32_t mr[NC];
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) mr[q] = rowmax16(u_lmax(ORING >= 3 ? unext : upre, q));
+                    if (m16 == 0) {
+#pragma unroll
+                        for (int q = 0; q < NC; ++q) lds_umax(&sM[c & 1][q][g4], mr[q]);
+                    }
+                }
+            };
             if constexpr (SAVE) {
+                next_umax();
                 __syncthreads();   // (2)
+                if constexpr (SCL) {
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) eo[q] = next_exp(c, q);
+                }
                 return;
             }
             if ((WSC || PRO) && c > 0) store_o(c - 1);
-            // O = sigma_S Q+ (S / sigma_S) + sigma_D P (Delta / sigma_D)
-            f4 oacc[RPW][NC], oacd[RPW][NC];
+            // O = 2^e (Q+ (S / 2^e) + P (Delta / 2^e))
+            f4 oacc[RPW][NC];
             if (RT::ALL || rows) {
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) { oacc[j][q] = f4zero(); oacd[j][q] = f4zero(); }
+                    for (int q = 0; q < NC; ++q) oacc[j][q] = f4zero();
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -1594,6 +1603,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         for (int j = 0; j < RPW; ++j) oacc[j][q] = M::mma(cur.Qp[j][kb], sf, oacc[j][q]);
                     }
             }
+            next_umax();
             __syncthreads();   // (2)
             if (RT::ALL || rows) {
 #pragma unroll
@@ -1605,21 +1615,30 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
-                            if constexpr (SCL) oacd[j][q] = M::mma(cur.Pm[j][sb], df, oacd[j][q]);
-                            else oacc[j][q] = M::mma(cur.Pm[j][sb], df, oacc[j][q]);
+                            oacc[j][q] = M::mma(cur.Pm[j][sb], df, oacc[j][q]);
                         }
                     }
                 }
+            }
+            int en[NC];
+            if constexpr (SCL) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) en[q] = next_exp(c, q);
+            }
+            if (RT::ALL || rows) {
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        f4 ov = oacc[j][q];
-                        if constexpr (SCL) ov = ov * sgs[q] + oacd[j][q] * sgd[q];
+                        const f4 ov = SCL ? oacc[j][q] * exp2i(eo[q]) : oacc[j][q];
 #pragma unroll
                         for (int ii = 0; ii < 4; ++ii)
                             sO[c & 1][(16 * RT::rt(wo, j) + 4 * g4 + ii) * LDO + 16 * q + m16] = ov[ii];
                     }
+            }
+            if constexpr (SCL) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) eo[q] = en[q];
             }
         };
         int c = 0;
