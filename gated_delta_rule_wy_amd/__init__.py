@@ -28,7 +28,7 @@ GDN2_GATES_PER_CHANNEL, GDN2_GATE_B_PER_HEAD, GDN2_GATE_W_PER_HEAD, GDN2_GATE_AL
 CHUNK = 64
 
 EXPORTS = ('gdn2_set_stream', 'gdn2_get_stream', 'gdn2_status_string',
-           'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_gates',
+           'gdn2_chunk_fwd_workspace_bytes', 'gdn2_chunk_fwd', 'gdn2_chunk_fwd_noalloc', 'gdn2_chunk_fwd_gates',
            'gdn2_chunk_fwd_sized_workspace_bytes', 'gdn2_chunk_fwd_sized',
            'gdn2_decode_step', 'gdn2_decode_step_gates',
            'gdn2_chunk_fwd_prologue', 'gdn2_decode_step_prologue',
@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn2_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn2_chunk_fwd.argtypes = [vp] * 10 + [i] * 8 + [vp, sz]
     lib.gdn2_chunk_fwd.restype = i
+    lib.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 10 + [i] * 8
+    lib.gdn2_chunk_fwd_noalloc.restype = i
     lib.gdn2_chunk_fwd_gates.argtypes = [vp] * 6 + [i] + [vp] * 4 + [i] * 8 + [vp, sz]
     lib.gdn2_chunk_fwd_gates.restype = i
     lib.gdn2_chunk_fwd_sized_workspace_bytes.argtypes = [i] * 9

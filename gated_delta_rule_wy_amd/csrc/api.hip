@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 namespace {
@@ -199,6 +200,53 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                                 N, H, dk, dv, in_dtype, out_dtype, workspace, workspace_bytes);
 }
 
+} // extern "C"
+
+// Workspace of gdn2_chunk_fwd_noalloc, for callers that cannot allocate:
+// one copy per device, held until the process ends, shared by every call on
+// that device (calls that overlap on one device race on it).
+static constexpr size_t kScratchBytes = (size_t)GDN2_NOALLOC_WORKSPACE_MAX;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up with that
+// device current on its first use and kept per device. (In host code the
+// array's name stands for a host-side shadow, not for device memory.)
+static int scratch_address(void **out)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<void *> addr[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return GDN2_ERR_HIP;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN2_ERR_HIP;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return GDN2_OK;
+}
+
+extern "C" {
+
+int gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, const float *S0, void *o, float *ST,
+                           const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                           int in_dtype, int out_dtype)
+{
+    const size_t need = gdn2_chunk_fwd_workspace_bytes(B, T, N, H, dk, dv, in_dtype, cu_seqlens != nullptr);
+    if (need == 0 || need > kScratchBytes) {
+        // invalid sizes report their own status; valid ones over the limit
+        // report the workspace (nothing is launched either way)
+        const int st = chunk_fwd_impl(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, nullptr, S0, o, ST,
+                                      cu_seqlens, B, T, N, H, dk, dv, in_dtype, out_dtype, nullptr, 0);
+        return st == GDN2_OK ? GDN2_ERR_WORKSPACE : st;
+    }
+    void *ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st != GDN2_OK) return st;
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, GDN2_GATES_PER_CHANNEL, nullptr, S0, o, ST, cu_seqlens, B, T,
+                          N, H, dk, dv, in_dtype, out_dtype, ws, kScratchBytes);
+}
 
 // The convolution parameters of a *_prologue call: weights required, biases
 // optional, history in / out each all-or-none.

@@ -130,6 +130,25 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                    size_t workspace_bytes);
 
 /*
+ * gdn2_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, which instead lives in a fixed
+ * device array of GDN2_NOALLOC_WORKSPACE_MAX bytes inside the library, one
+ * per device, held until the process ends. Nothing is allocated or freed
+ * during the call. Sizes whose workspace (gdn2_chunk_fwd_workspace_bytes)
+ * exceeds GDN2_NOALLOC_WORKSPACE_MAX give GDN2_ERR_WORKSPACE, with nothing
+ * launched; e.g. 4 x 4096 tokens x 16 heads at d = 128 fit (254 MB). Every
+ * call on one device shares that device's array: calls that can overlap on
+ * one device (other streams, other host threads) race and must be
+ * serialised by the caller. Results are those of gdn2_chunk_fwd.
+ */
+#define GDN2_NOALLOC_WORKSPACE_MAX (256u << 20)
+int gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const void *b, const void *w, const float *S0, void *o, float *ST,
+                           const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                           int in_dtype, int out_dtype);
+
+/*
  * gdn2_chunk_fwd with the gate layouts given by `gates` (gdn2_gate_layout
  * bits): b is [tokens, H] when GDN2_GATE_B_PER_HEAD is set, w is [tokens, H]
  * with GDN2_GATE_W_PER_HEAD and log_alpha is [tokens, H] with
