@@ -386,11 +386,14 @@ def bench_prefill_prologue(args, torch, gdn2, gi, ws):
             'kernels_ms': {k: round(v[1] / v[0], 5) for k, v in prof.items() if v[0]}}
 
 
-def bench_decode(args, torch, gdn2, gi):
-    name = 'decode_n256'
+def bench_decode(args, torch, gdn2, gi, name='decode_n256', cycles=1):
+    """Decode steps on the resident state. `cycles` > 1 replays the workload's
+    step inputs that many times (the large state's inputs are drawn for a few
+    steps only; the state, not the inputs, is what each step streams)."""
     c = gi.WORKLOADS[name]
     N, H, d = c['N'], c['H'], c['dk']
-    steps = args.decode_steps
+    extras = name == 'decode_n256'
+    steps = args.decode_steps if extras else c['steps']
     dev = torch.device('cuda:0')
     bf = torch.bfloat16
     from concurrent.futures import ThreadPoolExecutor
@@ -404,14 +407,16 @@ def bench_decode(args, torch, gdn2, gi):
     S = torch.from_numpy(S_np).to(dev)
     o = torch.empty(N, H, d, device=dev)
     log(f'[bench] generated {steps} decode steps in {time.time() - t0:.1f}s')
-    step = lambda s: gdn2.decode_step(q[s], k[s], v[s], la[s], b[s], w[s], S, out=o)
+    step = lambda s: gdn2.decode_step(q[s % steps], k[s % steps], v[s % steps], la[s % steps], b[s % steps],
+                                      w[s % steps], S, out=o)
+    timed = steps * cycles
     for s in range(min(10, steps)):
         step(s)
     torch.cuda.synchronize()
-    gdn2.profile_begin(steps)
+    gdn2.profile_begin(timed)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
+    for s in range(timed):
         step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -419,12 +424,16 @@ def bench_decode(args, torch, gdn2, gi):
     n, tot = prof['gdn2_decode']
     avg = tot / n
     per_chain = 2 * d * d * 4 + (3 * d + 2 * d) * 2 + d * 4 + d * 4   # S r+w, q k b v w, log alpha, o
-    res = {'metric': 'decode steps/s', 'value': steps / (t1 - t0), 'unit': 'steps/s',
-           'steps': steps, 'ms_per_step': round((t1 - t0) * 1e3 / steps, 5),
+    res = {'metric': 'decode steps/s', 'value': timed / (t1 - t0), 'unit': 'steps/s',
+           'steps': timed, 'ms_per_step': round((t1 - t0) * 1e3 / timed, 5),
            'config': {'workload': name, 'N': N, 'H': H, 'dk': d, 'dv': d,
-                      'state': 'fp32 [N,H,dk,dv] resident, updated in place', 'inputs': 'bf16, fresh per step'},
+                      'state': f'fp32 [N,H,dk,dv] resident ({N * H * d * d * 4 / 2**30:.2f} GiB), updated in place',
+                      'inputs': 'bf16, fresh per step' if cycles == 1 else
+                                f'bf16, {steps} distinct steps replayed {cycles} times'},
            'roofline': roofline('gdn2_decode', per_chain * N * H, avg, name)}
-    log(f'[bench] decode {res["ms_per_step"]} ms/step, kernel {avg * 1e3:.1f} us')
+    log(f'[bench] decode {name}: {res["ms_per_step"]} ms/step, kernel {avg * 1e3:.1f} us')
+    if not extras:
+        return res
     if not args.no_prologue:
         # raw inputs (q, k, v before the short convolution, gate logits) with
         # the convolution history updated in place
@@ -543,6 +552,7 @@ def main():
                                 for n in ('prefill_b4_t4096', 'varlen_32seq')]
     if not args.no_decode:
         out['decode'] = bench_decode(args, torch, gdn2, gi)
+        out['decode_large_state'] = bench_decode(args, torch, gdn2, gi, 'decode_n1024', cycles=10)
     print(json.dumps(out), flush=True)
 
 

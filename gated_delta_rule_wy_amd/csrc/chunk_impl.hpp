@@ -857,8 +857,10 @@ template <typename Op> __device__ __forceinline__ void lds_tile_store(Op *dst, i
 // decay factor <= 1):
 //   |S_{c+1}| <= max|S_c| + CS max|Delta_c| <= 2 max(max|S_c|, CS max|Delta_c|),
 //   B = max(that, max|U_{c+1}|),
-// the maxima gathered in LDS during step c. A tile far below the largest of
-// the three keeps its relative precision down to 2^-14 of 2^9.
+// each wave's maxima put in LDS slots during step c (U's at the start of
+// the step, the state's and Delta's once Delta is formed) and read by all
+// after the second barrier. A tile far below the largest of the three keeps
+// its relative precision down to 2^-14 of 2^9.
 
 // exponent e of the scale for a bound B >= 0 given as its bits: B / 2^e in
 // [2^9, 2^10), clamped to [-100, 100] (B = 0 and subnormal B give -100)
@@ -870,8 +872,8 @@ __device__ __forceinline__ int scale_exp(uint32_t Bbits)
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
 // Maxima of magnitudes as bit patterns: for non-negative floats the
-// unsigned order is the float order, so the lane exchanges below and the
-// LDS atomics take them as integers.
+// unsigned order is the float order, so the lane exchanges below take them
+// as integers.
 // max over each 16-lane row, in every lane of the row (quad swaps, then the
 // row's half mirror and mirror)
 __device__ __forceinline__ uint32_t rowmax16(uint32_t m)
@@ -895,12 +897,6 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x)
     x = max(a[0], a[1]);
     const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
     return max(b[0], b[1]);
-}
-
-// LDS running maximum, on magnitude bit patterns
-__device__ __forceinline__ void lds_umax(float *p, uint32_t x)
-{
-    atomicMax(reinterpret_cast<unsigned int *>(p), x);
 }
 
 // L2 prefetch workgroups. A pass workgroup holds a bounded number of
@@ -1044,10 +1040,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     // f16 tiles carry a power-of-two scale per chunk and 16-column tile
     // (scale_exp above); fp32 operands need none
     constexpr bool SCL = std::is_same<Op, _Float16>::value;
-    // bound for the next chunk's scale, [parity of the step that forms it][tile]
-    // [16-lane row of the contributing lanes] (distinct words per row: LDS
-    // atomics of one wave to one word become a loop over its lanes)
-    __shared__ __attribute__((aligned(16))) float sM[2][NC][4];
+    // each wave's part of the bound for the next chunk's scale, [parity of
+    // the step that forms it][tile][wave] (plain stores: every slot is
+    // rewritten each step)
+    __shared__ __attribute__((aligned(16))) float sM[2][NC][8];
     // the first chunk's maxima, [wave][tile]
     __shared__ __attribute__((aligned(16))) float sM0[8][NC];
     auto first_exp = [&](int q) {
@@ -1057,8 +1053,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         return scale_exp(__builtin_amdgcn_readfirstlane(m));
     };
     auto next_exp = [&](int c, int q) {
-        const uint4 m = *reinterpret_cast<const uint4 *>(&sM[c & 1][q][0]);
-        return scale_exp(__builtin_amdgcn_readfirstlane(max(max(m.x, m.y), max(m.z, m.w))));
+        const uint4 a = *reinterpret_cast<const uint4 *>(&sM[c & 1][q][0]);
+        const uint4 b = *reinterpret_cast<const uint4 *>(&sM[c & 1][q][4]);
+        const uint32_t m = max(max(max(a.x, a.y), max(a.z, a.w)), max(max(b.x, b.y), max(b.z, b.w)));
+        return scale_exp(__builtin_amdgcn_readfirstlane(m));
     };
 
     // XCD-aware numbering: the slices (and prefetch workgroups) of chain c
@@ -1124,13 +1122,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         };
         if constexpr (SCL) {
             // this wave's part of the first chunk's maxima (S_0; the output
-            // waves put U_0's), and step 0's bound buffer cleared
+            // waves put U_0's)
 #pragma unroll
             for (int q = 0; q < NC; ++q) {
                 const uint32_t m = wave_umax(__float_as_uint(state_lmax(q)));
                 if (lane == 0) sM0[wv][q] = __uint_as_float(m);
             }
-            if (wv == 0 && lane < 4 * NC) (&sM[0][0][0])[lane] = 0.f;
         }
         const bool rows = RT::active(wv);
         // last stored k-block of T / P for the wave's row tile j (RPW <= 2)
@@ -1180,11 +1177,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     }
             }
             __syncthreads();   // (1) state tiles and U ready
-            // clear the other parity's bound for the next step (its last
-            // readers passed barrier (1))
-            if constexpr (SCL) {
-                if (wv == 0 && lane < 4 * NC) (&sM[(c + 1) & 1][0][0])[lane] = 0.f;
-            }
             // this lane's max |S_c| and max |Delta_c| per tile (in units of the scale)
             float mS[NC], mD[NC];
 #pragma unroll
@@ -1256,14 +1248,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             pre.load_a(blk_of(c + PD), wv, lane);
             if constexpr (SCL) {
                 // this wave's part of the bound on S_{c+1}: 2 max(|S_c|, CS |Delta_c|),
-                // unscaled, per 16-lane row, added by the rows' first lanes
+                // unscaled
                 uint32_t mr[NC];
 #pragma unroll
                 for (int q = 0; q < NC; ++q)
-                    mr[q] = rowmax16(__float_as_uint(fmaxf(mS[q], (float)CS * mD[q]) * exp2i(esc[q] + 1)));
-                if (m16 == 0) {
+                    mr[q] = wave_umax(__float_as_uint(fmaxf(mS[q], (float)CS * mD[q]) * exp2i(esc[q] + 1)));
+                if (lane == 0) {
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) lds_umax(&sM[c & 1][q][g4], mr[q]);
+                    for (int q = 0; q < NC; ++q) sM[c & 1][q][wv] = __uint_as_float(mr[q]);
                 }
             }
             __syncthreads();   // (2) Delta tiles ready
@@ -1272,15 +1264,28 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             for (int q = 0; q < NC; ++q)
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) Db[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+            // the second half of the prefetch, ahead of the products (2% on
+            // the pass at T = 64K)
+            pre.load_b(blk_of(c + PD), wv, lane);
             // the next chunk's exponents, read after the Delta fragments so
-            // that those reads do not wait behind these
-            int en[NC];
+            // that those reads do not wait behind these, and the factors that
+            // take the state into their units (powers of two: exact)
+            float rs[NC];
             if constexpr (SCL) {
 #pragma unroll
-                for (int q = 0; q < NC; ++q) en[q] = next_exp(c, q);
+                for (int q = 0; q < NC; ++q) {
+                    const int en = next_exp(c, q);
+                    rs[q] = exp2i(min(max(esc[q] - en, -126), 127));
+                    esc[q] = en;
+                }
             }
-            // S_{c+1} = gamma S_c + Khat^T Delta_c, in units of the chunk's
-            // scale: the products accumulate onto the decayed state
+            // S_{c+1} = gamma S_c + Khat^T Delta_c: the products accumulate
+            // onto the decayed state (in the chunk's units), and each tile
+            // leaves for LDS in the next chunk's units as soon as it is done.
+            // (Every tile is multiplied: a branch that skipped the multiply
+            // where the exponent stays gave wrong, run-to-run varying states,
+            // its untaken path reusing the product registers a few
+            // instructions after the matrix instruction that writes them.)
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int ct = wv * TPW + u;
@@ -1290,30 +1295,9 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     f4 s = Sr[q][u] * cur.gam[u];
 #pragma unroll
                     for (int sb = 0; sb < NSB; ++sb) s = M::mma(cur.Kh[u][sb], Db[q][sb], s);
+                    if constexpr (SCL) s = s * rs[q];
                     Sr[q][u] = s;
-                    if constexpr (!SCL) lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
-                }
-            }
-            pre.load_b(blk_of(c + PD), wv, lane);
-            if constexpr (SCL) {
-                // into the next chunk's units (a power of two: exact). Always
-                // multiplied: a branch that skipped this where the exponent
-                // stays gave wrong, run-to-run varying states (its untaken path
-                // reused the product registers a few instructions after the
-                // matrix instruction that writes them).
-#pragma unroll
-                for (int q = 0; q < NC; ++q) {
-                    const float r = exp2i(min(max(esc[q] - en[q], -126), 127));
-#pragma unroll
-                    for (int u = 0; u < TPW; ++u) Sr[q][u] = Sr[q][u] * r;
-                    esc[q] = en[q];
-                }
-#pragma unroll
-                for (int u = 0; u < TPW; ++u) {
-                    const int ct = wv * TPW + u;
-                    if (NCT % 4 != 0 && ct >= NCT) continue;
-#pragma unroll
-                    for (int q = 0; q < NC; ++q) lds_tile_store<Op>(sS[q] + ct * 256, lane, Sr[q][u]);
+                    lds_tile_store<Op>(sS[q] + ct * 256, lane, s);
                 }
             }
             // A device-scope store is written through to memory and, since
@@ -1484,14 +1468,35 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             else return u.q[q + NC * x].ok ? 1.f : 0.f;
         };
         // max |U| over this lane's values of tile q (rows ur + 64 x)
-        auto u_lmax = [&](const UV &u, int q) {
+        // With scales (and no prologue, whose ucarry already holds U) the
+        // products U of the next chunk are formed once, for its maximum a
+        // step ahead, and kept for its write, in slot (chunk parity) of two
+        // (the ring without the prologue has an even length, so the slot of
+        // each step's chunk is sl & 1)
+        constexpr bool UC = SCL && !PRO;
+        static_assert(!UC || ORING % 2 == 0, "cache slots by ring position");
+        float ucache[UC ? 2 : 1][UC ? NC * UR : 1][4];
+        auto u_form = [&](const UV &u, int slot) {
+            if constexpr (UC) {
+#pragma unroll
+                for (int x = 0; x < UR; ++x)
+#pragma unroll
+                    for (int q = 0; q < NC; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ucache[slot & 1][q + NC * x][e] = u_val(u, q, x, e);
+            }
+        };
+        // max |U| over this lane's values of tile q (rows ur + 64 x): of the
+        // cached products, or of ucarry with the prologue
+        auto u_lmax = [&](const UV &u, int q, int slot) {
             float mf = 0.f;
             if (urow) {
 #pragma unroll
                 for (int x = 0; x < UR; ++x) {
                     float mx = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(u_val(u, q, x, e)));
+                    for (int e = 0; e < 4; ++e)
+                        mx = fmaxf(mx, fabsf(UC ? ucache[slot & 1][(q + NC * x) % (UC ? NC * UR : 1)][e] : u_val(u, q, x, e)));
                     mf = fmaxf(mf, mx * u_ok(u, q, x));
                 }
             }
@@ -1506,7 +1511,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             // this wave's part of the first chunk's maxima (U_0; ucarry with the prologue)
 #pragma unroll
             for (int q = 0; q < NC; ++q) {
-                const uint32_t m = nch > 0 ? wave_umax(u_lmax(u0, q)) : 0u;
+                if (q == 0) u_form(u0, 0);
+                const uint32_t m = nch > 0 ? wave_umax(u_lmax(u0, q, 0)) : 0u;
                 if (lane == 0) sM0[4 + wo][q] = __uint_as_float(m);
             }
             __syncthreads();   // pairs with the state waves' barrier for the first chunk's maxima
@@ -1533,17 +1539,36 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         auto step = [&](int c, OF &cur, OF &pre, UV &ucur, UV &unext, UV &upre, int sl) {
             const int sln = sl == ORING - 1 ? 0 : sl + 1;
             if constexpr (PRO) stage_v(unext, sln);
+            // this wave's part of the bound for the next chunk's scale: max |U|
+            // of the next chunk. With a ring of three or four its rows were
+            // loaded steps ago and it goes out first, off the path to the
+            // barriers; with a ring of two it is the load issued after barrier
+            // (1), and with the prologue it is formed there.
+            auto next_umax = [&]() {
+                if constexpr (SCL) {
+                    uint32_t mr[NC];
+                    u_form(ORING >= 3 ? unext : upre, sln);
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) mr[q] = wave_umax(u_lmax(ORING >= 3 ? unext : upre, q, sln));
+                    if (lane == 0) {
+#pragma unroll
+                        for (int q = 0; q < NC; ++q) sM[c & 1][q][4 + wo] = __uint_as_float(mr[q]);
+                    }
+                }
+            };
+            constexpr bool kEarlyU = ORING >= 3 && !PRO;
+            if constexpr (kEarlyU) next_umax();
             if (urow) {
 #pragma unroll
                 for (int x = 0; x < UR; ++x)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
                         // u_ok over the chunk's scale (a power of two: exact)
-                        const float f = SCL ? exp2i(-eo[q]) * u_ok(ucur, q, x) : u_ok(ucur, q, x);
+                        const float f = (SCL ? exp2i(-eo[q]) : 1.f) * u_ok(ucur, q, x);
                         const int sbx = usb + 64 * x / KB;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float uu = u_val(ucur, q, x, e) * f;
+                            const float uu = (UC ? ucache[sl & 1][(q + NC * x) % (UC ? NC * UR : 1)][e] : u_val(ucur, q, x, e)) * f;
                             const Op hi = (Op)uu;
                             const int ln = (uc + e) + 16 * ug;
                             sU[q][((0 * NSB + sbx) * 64 + ln) * NE + ui] = hi;
@@ -1562,23 +1587,8 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             if constexpr (!SAVE) pre.load(blk_of(c + OPD), wo, lane);
             uv_load(upre, c + OPD);
             if constexpr (PRO) conv_u(unext, sln, sl);
-            // this wave's part of the bound for the next chunk's scale: max |U|
-            // of the next chunk (loaded two steps ago, or formed just above
-            // with the prologue; with a ring of two it is the load just
-            // issued), per 16-lane row, added by the rows' first lanes
-            auto next_umax = [&]() {
-                if constexpr (SCL) {
-                    uint32_t mr[NC];
-#pragma unroll
-                    for (int q = 0; q < NC; ++q) mr[q] = rowmax16(u_lmax(ORING >= 3 ? unext : upre, q));
-                    if (m16 == 0) {
-#pragma unroll
-                        for (int q = 0; q < NC; ++q) lds_umax(&sM[c & 1][q][g4], mr[q]);
-                    }
-                }
-            };
             if constexpr (SAVE) {
-                next_umax();
+                if constexpr (!kEarlyU) next_umax();
                 __syncthreads();   // (2)
                 if constexpr (SCL) {
 #pragma unroll
@@ -1603,7 +1613,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                         for (int j = 0; j < RPW; ++j) oacc[j][q] = M::mma(cur.Qp[j][kb], sf, oacc[j][q]);
                     }
             }
-            next_umax();
+            if constexpr (!kEarlyU) next_umax();
             __syncthreads();   // (2)
             if (RT::ALL || rows) {
 #pragma unroll

@@ -201,6 +201,8 @@ WORKLOADS = {
     'prefill_b4_t4096': dict(seed=1, B=4, T=4096, H=16, dk=128, dv=128, dtype='bf16', s0_std=0.0),
     'prefill_t65536': dict(seed=2, B=1, T=65536, H=16, dk=128, dv=128, dtype='bf16', s0_std=0.02),
     'decode_n256': dict(seed=3, N=256, H=16, dk=128, dv=128, dtype='bf16', steps=1000, s0_std=0.02),
+    # a state (1 GiB) four times the size of the last-level cache
+    'decode_n1024': dict(seed=5, N=1024, H=16, dk=128, dv=128, dtype='bf16', steps=20, s0_std=0.02),
     'varlen_32seq': dict(seed=4, n_seqs=32, lo=512, hi=16384, H=32, dk=128, dv=128,
                          dtype='bf16', s0_std=0.02, collapsed=16),
 }
