@@ -522,9 +522,14 @@ __device__ __forceinline__ void col_scan64(float *buf, int ld, float *part, int 
 // Delta G^T in registers. Phase B (key channels in slices, fp32 matrix
 // cores) forms the four decayed products blockwise over 16-row blocks:
 // off-diagonal blocks S < R through the references ref_{S+1} (every factor
-// <= 1), diagonal blocks around the block's middle row (bounded in fp32 for
-// log alpha >= -7 per token), then the elementwise gradients and the reverse
-// cumulative sum.
+// <= 1), diagonal blocks around the block's middle row while the decay
+// across a half block stays within kBwdDiagSpread (factors within e^40 of
+// 1), else with exact pairwise exponents e^{g_r - g_s} <= 1 (any decay),
+// then the elementwise gradients and the reverse cumulative sum.
+// Largest log-decay between a diagonal block's middle row and its ends for
+// the factored form; beyond it the block takes the exact pairwise form.
+constexpr float kBwdDiagSpread = 40.f;
+
 template <typename Op, int DK, int DV> struct GradShape {
     static constexpr int VS = (sizeof(Op) == 2 ? 32 : 16) < DV ? (sizeof(Op) == 2 ? 32 : 16) : DV;   // value cols per slice
     static constexpr int VT = VS / 16, CT = DK / 16;
@@ -578,6 +583,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     // g (the chunk's cumulative log decay, all channels) from phase 0 to the end
     constexpr int LDL = DK + 1;
     __shared__ float sRef[5 * DK], sMid[4 * DK], sPart[NT], sGc[64 * LDL];
+    __shared__ int sExactB[4];   // diagonal blocks that take the exact pairwise form
     __shared__ __attribute__((aligned(16))) unsigned char smem[REGION];
     Op *GT = (Op *)smem + A_GT;
     Op *Gr = (Op *)smem + A_GR, *Sj = (Op *)smem + A_SJ, *Dj = (Op *)smem + A_DJ, *Oj = (Op *)smem + A_OJ;
@@ -676,14 +682,19 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
             const int x = t + NT * u, r = x / DK, c = x % DK;
             sGc[r * LDL + c] = r < n ? lv[u] : 0.f;
         }
+        if (t < 4) sExactB[t] = 0;
         __syncthreads();
         col_scan64<DK, false, NT>(sGc, LDL, sPart, t);
         for (int c = t; c < DK; c += NT) {
             sRef[c] = 0.f;
+            float ref = 0.f;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                sRef[(R + 1) * DK + c] = sGc[(16 * R + 15) * LDL + c];
-                sMid[R * DK + c] = sGc[(16 * R + 7) * LDL + c];
+                const float md = sGc[(16 * R + 7) * LDL + c], ref1 = sGc[(16 * R + 15) * LDL + c];
+                sRef[(R + 1) * DK + c] = ref1;
+                sMid[R * DK + c] = md;
+                if (fmaxf(ref - md, md - ref1) > kBwdDiagSpread) atomicOr(&sExactB[R], 1);
+                ref = ref1;
             }
         }
         __syncthreads();
@@ -889,8 +900,10 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                 const In kr_ = ok ? bc.k[i] : zero_, qr_ = ok ? bc.q[i] : zero_, br_ = ok ? bc.b[i] : zero_;
                 const float kv = in2f<In>(kr_), qv = in2f<In>(qr_), bv = in2f<In>(br_);
                 const float gv = sGc[(rb + e) * LDL + c];
-                const float e1 = __expf(rf1 - gv), em = __expf(md - gv);
-                const float e2 = __expf(gv - rf0), en = __expf(gv - md);
+                // (the middle-row factors of a block that takes the exact
+                // form go unused; capped so that they stay finite)
+                const float e1 = __expf(rf1 - gv), em = __expf(fminf(md - gv, 80.f));
+                const float e2 = __expf(gv - rf0), en = __expf(fminf(gv - md, 80.f));
                 xt[e] = kv * e1;
                 xm[e] = kv * em;
                 bt[e] = bv * kv * e2;   // row side of (dA o Dec)^T (b k), like q
@@ -913,6 +926,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
         }
         __syncthreads();
         const int R = wv;   // this wave's 16-row block (rows for Y, rows s for Z)
+        const bool exactR = __builtin_amdgcn_readfirstlane(sExactB[R]) != 0;   // (uniform per wave)
         // Y1 = (dP o Dec) x, Y2 = (dA o Dec) x for the rows of block R and
         // Z = (dP o Dec)^T q + (dA o Dec)^T (b k) for the rows s of block R,
         // for the half's channel tiles ct = hv + HV j of the slice at once:
@@ -932,7 +946,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
         }
         // row side: off-diagonal blocks S < R through ref_{S+1}, then the
         // diagonal block around its middle row
-        for (int S = 0; S <= R; ++S) {
+        for (int S = 0; S <= (exactR ? R - 1 : R); ++S) {
             const bool dg = S == R;
             const f4 a1 = *reinterpret_cast<const f4 *>(sdP + (16 * R + m16) * LDF + 16 * S + 4 * g4);
             const f4 a2 = *reinterpret_cast<const f4 *>(sdA + (16 * R + m16) * LDF + 16 * S + 4 * g4);
@@ -953,7 +967,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
         }
         // column side: the diagonal block around its middle row, then the
         // off-diagonal blocks Rb > R through ref_Rb
-        for (int Rb = R; Rb < 4; ++Rb) {
+        for (int Rb = exactR ? R + 1 : R; Rb < 4; ++Rb) {
             const bool dg = Rb == R;
             f4 a1, a2;
 #pragma unroll
@@ -976,6 +990,64 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                 }
             }
         }
+        // the diagonal terms dP_rr k_r of Y1 and dP_rr q_r of Z, kept apart in
+        // exact blocks: they cancel in dq q - dk k, and at strong decay the
+        // decay gradient is the small remainder of that difference
+        float dY1[CWH][4], dZ[CWH][4];
+#pragma unroll
+        for (int ct = 0; ct < CWH; ++ct)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) { dY1[ct][ii] = 0.f; dZ[ct][ii] = 0.f; }
+        if (exactR) {
+            // the diagonal block with exact pairwise decay: e^{g_r - g_s}
+            // (s <= r) as the running product of alpha over (s, r], from log
+            // alpha itself (a difference of the chunk's cumulative sums would
+            // carry their rounding, ~1e-4 at a cumulative decay near -1000)
+            //   Y1, Y2 += sum_{s < r} (dP_rs, dA_rs) k_s e^{g_r - g_s}   (row r = this lane's)
+            //   Z      += sum_{r > s} (dP_rs q_r + dA_rs b_r k_r) e^{g_r - g_s}   (row s = this lane's)
+            // (s = r apart; dA_rr = 0)
+#pragma unroll
+            for (int ct = 0; ct < CWH; ++ct) {
+                const int cl = 16 * (hv + HV * ct) + m16, c = c0 + cl;
+                float al[16];   // alpha of the block's rows in channel c (1 past the end)
+#pragma unroll
+                for (int l = 0; l < 16; ++l) {
+                    const int o = 16 * R + l;
+                    al[l] = o < n ? __expf(la[tok_k(o) + c]) : 1.f;
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int xl = 4 * g4 + ii, x = 16 * R + xl;   // r for Y, s for Z
+                    float y1 = 0.f, y2 = 0.f, z = 0.f, fy = 1.f, fz = 1.f;
+#pragma unroll
+                    for (int l = 14; l >= 0; --l) {   // o = s < x, nearest first
+                        const int o = 16 * R + l;
+                        if (l < xl) {
+                            fy *= al[l + 1];
+                            const float ko = in2f<In>(skT[cl * LDR + o]);
+                            y1 += sdP[x * LDF + o] * ko * fy;
+                            y2 += sdA[x * LDF + o] * ko * fy;
+                        }
+                    }
+#pragma unroll
+                    for (int l = 0; l < 16; ++l) {   // o = r > x, nearest first
+                        const int o = 16 * R + l;
+                        if (l > xl) {
+                            fz *= al[l];
+                            const float ko = in2f<In>(skT[cl * LDR + o]);
+                            const float qo = in2f<In>(sqT[cl * LDR + o]), bo = in2f<In>(sbT[cl * LDR + o]);
+                            z += (sdP[o * LDF + x] * qo + sdA[o * LDF + x] * bo * ko) * fz;
+                        }
+                    }
+                    const float dpx = sdP[x * LDF + x];
+                    Y1[ct][ii] += y1;
+                    Y2[ct][ii] += y2;
+                    Z[ct][ii] += z;
+                    dY1[ct][ii] = dpx * in2f<In>(skT[cl * LDR + x]);
+                    dZ[ct][ii] = dpx * in2f<In>(sqT[cl * LDR + x]);
+                }
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < CWH; ++ct) {
             // (F1..F3 hold the half's key channel tiles hv + HV i; this one is
@@ -991,13 +1063,14 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                 const int r = 16 * R + 4 * g4 + ii;
                 const float gv = gR[ct][ii], eg = __expf(gv), egn = __expf(gn - gv);
                 const float qv = in2f<In>(q4.v[ii]), kv = in2f<In>(k4.v[ii]), bv = in2f<In>(b4.v[ii]);
-                const float dqv = F1[ctg][ii] * eg + Y1[ct][ii];
+                const float dqo = F1[ctg][ii] * eg + Y1[ct][ii], dqv = dqo + dY1[ct][ii];
                 const float dEe = -F2[ctg][ii] * eg + Y2[ct][ii];
-                const float dkm = Z[ct][ii];
+                const float dkm = Z[ct][ii] + dZ[ct][ii];
                 const float dkh = F3[ctg][ii] * egn;
                 const float dkv = dkm + dkh + dEe * bv;
                 const float dbv = dEe * kv;
-                sdG[r * LDC + cl] = dqv * qv - dkm * kv - dkh * kv + dEe * bv * kv;
+                // (the diagonal terms dY1 q - dZ k cancel exactly: left out)
+                sdG[r * LDC + cl] = dqo * qv - Z[ct][ii] * kv - dkh * kv + dEe * bv * kv;
                 khk += dkh * kv;
                 if (r < n) {
                     const size_t o = tok_k(r) + c;

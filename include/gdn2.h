@@ -299,8 +299,12 @@ int gdn2_decode_step_prologue(const void *q_raw, const void *k_raw, const void *
  *   workspace        device memory of at least
  *                    gdn2_chunk_bwd_workspace_bytes(...) bytes
  * Gradient outputs must not alias any input. Errors as in gdn2_chunk_fwd.
- * Precondition (not checked): log_alpha >= -7 per token, so that within 16
- * tokens the decay factors stay inside fp32 range.
+ * Any log_alpha <= 0 is handled (16-token blocks whose decay is too wide for
+ * the factored form take exact pairwise exponents). Value range: with bf16
+ * inputs the chunk start states, corrected writes and end-state gradients
+ * that the backward keeps between its kernels are f16 without scales, so
+ * their entries must stay below 65504 in magnitude (the forward alone has no
+ * such bound).
  */
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv,
                                       int in_dtype, int varlen);
