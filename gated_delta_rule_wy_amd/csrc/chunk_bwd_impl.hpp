@@ -1006,38 +1006,32 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
             //   Y1, Y2 += sum_{s < r} (dP_rs, dA_rs) k_s e^{g_r - g_s}   (row r = this lane's)
             //   Z      += sum_{r > s} (dP_rs q_r + dA_rs b_r k_r) e^{g_r - g_s}   (row s = this lane's)
             // (s = r apart; dA_rr = 0)
+            // (loops kept rolled and alpha read where used: this rare path
+            // must not add registers to the common one)
+            auto alpha = [&](int o, int c) { return o < n ? __expf(la[tok_k(o) + c]) : 1.f; };
 #pragma unroll
             for (int ct = 0; ct < CWH; ++ct) {
                 const int cl = 16 * (hv + HV * ct) + m16, c = c0 + cl;
-                float al[16];   // alpha of the block's rows in channel c (1 past the end)
-#pragma unroll
-                for (int l = 0; l < 16; ++l) {
-                    const int o = 16 * R + l;
-                    al[l] = o < n ? __expf(la[tok_k(o) + c]) : 1.f;
-                }
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int xl = 4 * g4 + ii, x = 16 * R + xl;   // r for Y, s for Z
-                    float y1 = 0.f, y2 = 0.f, z = 0.f, fy = 1.f, fz = 1.f;
-#pragma unroll
-                    for (int l = 14; l >= 0; --l) {   // o = s < x, nearest first
+                    float y1 = 0.f, y2 = 0.f, z = 0.f, f = 1.f;
+#pragma unroll 1
+                    for (int l = xl - 1; l >= 0; --l) {   // o = s < x, nearest first
                         const int o = 16 * R + l;
-                        if (l < xl) {
-                            fy *= al[l + 1];
-                            const float ko = in2f<In>(skT[cl * LDR + o]);
-                            y1 += sdP[x * LDF + o] * ko * fy;
-                            y2 += sdA[x * LDF + o] * ko * fy;
-                        }
+                        f *= alpha(o + 1, c);
+                        const float ko = in2f<In>(skT[cl * LDR + o]) * f;
+                        y1 += sdP[x * LDF + o] * ko;
+                        y2 += sdA[x * LDF + o] * ko;
                     }
-#pragma unroll
-                    for (int l = 0; l < 16; ++l) {   // o = r > x, nearest first
+                    f = 1.f;
+#pragma unroll 1
+                    for (int l = xl + 1; l < 16; ++l) {   // o = r > x, nearest first
                         const int o = 16 * R + l;
-                        if (l > xl) {
-                            fz *= al[l];
-                            const float ko = in2f<In>(skT[cl * LDR + o]);
-                            const float qo = in2f<In>(sqT[cl * LDR + o]), bo = in2f<In>(sbT[cl * LDR + o]);
-                            z += (sdP[o * LDF + x] * qo + sdA[o * LDF + x] * bo * ko) * fz;
-                        }
+                        f *= alpha(o, c);
+                        const float ko = in2f<In>(skT[cl * LDR + o]);
+                        const float qo = in2f<In>(sqT[cl * LDR + o]), bo = in2f<In>(sbT[cl * LDR + o]);
+                        z += (sdP[o * LDF + x] * qo + sdA[o * LDF + x] * bo * ko) * f;
                     }
                     const float dpx = sdP[x * LDF + x];
                     Y1[ct][ii] += y1;
