@@ -64,20 +64,30 @@ def traffic_for(kernel: str, workload: str):
     return e['fetch_bytes'] + e['write_bytes']
 
 
-def mfma_summary(model_flop_frac):
+def step_traffic(workload):
+    """Counter HBM bytes of the prefill step (preparation + pass), or None."""
+    t = [traffic_for(k, workload) for k in ('gdn2_chunk_prep', 'gdn2_chunk_pass')]
+    return None if None in t else sum(t)
+
+
+def mfma_summary(model_flop_frac, ms_per_step):
     """Matrix-core use of the T = 64K prefill step: the algorithmic (model)
-    FLOP fraction measured here, and the rocprof MFMA-busy fraction of each
-    kernel from the committed counter summary when it was taken on the
-    current kernel sources (else null)."""
-    out = {'peak_tflops': PEAK_MFMA_F16_TFLOPS, 'model_flop_frac': model_flop_frac, 'busy_frac': None}
+    FLOP fraction measured here, and from the committed counter summary
+    (when it was taken on the current kernel sources, else null) the
+    rocprof MFMA-busy fraction of each kernel and the issued MFMA FLOPs per
+    step over this step's time."""
+    out = {'peak_tflops': PEAK_MFMA_F16_TFLOPS, 'model_flop_frac': model_flop_frac, 'busy_frac': None,
+           'issued_flop_frac': None}
     path = os.path.join(ROOT, 'profiles', 'mfma.json')
     if os.path.exists(path):
         with open(path) as f:
             d = json.load(f)
         if d.get('source_sha') == src_hash():
             out['busy_frac'] = d.get('busy_frac')
-            out['issued_tflops'] = d.get('issued_tflops')
-            out['counters'] = d.get('counters')
+            fl = d.get('issued_flop_per_step')
+            if fl:
+                out['issued_flop_frac'] = round(fl / (ms_per_step * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)
+            out['normalisation'] = d.get('normalisation')
     return out
 
 
@@ -141,7 +151,10 @@ def bench_prefill(args, torch, gdn2, gi):
         'roofline': roofline(dom, alg[dom], avg[dom], name),
         'step_roofline': {'bound': 'hbm', 'alg_bytes_per_step': int(step_bytes),
                           'achieved': round(step_bytes / (ms * 1e-3) / 1e9, 1), 'peak': PEAK_HBM_GBS,
-                          'unit': 'GB/s', 'frac': round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                          'unit': 'GB/s', 'frac': round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          'traffic': step_traffic(name),
+                          'traffic_ratio': (round(step_traffic(name) / step_bytes, 3)
+                                            if step_traffic(name) else None)},
         'kernels_ms': {k: round(v, 5) for k, v in avg.items()},
         'model_flop_frac': round(TH * flops_per_token_head(dk, dv) / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
     }
@@ -537,7 +550,7 @@ def main():
     if 'cpu_baseline' in pre:
         out['cpu_baseline'] = pre['cpu_baseline']
     out['step_roofline'] = pre['step_roofline']
-    out['mfma'] = mfma_summary(pre['model_flop_frac'])
+    out['mfma'] = mfma_summary(pre['model_flop_frac'], pre['ms_per_step'])
     out['kernels_ms'] = pre['kernels_ms']
     out['gate_forms'] = pre['gate_forms']
     out['chunk_sizes'] = pre['chunk_sizes']
