@@ -1032,7 +1032,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
     // per 16-column tile q of the slice
     __shared__ __attribute__((aligned(16))) Op sS[NC][NCT * 64 * 4];        // state operand tiles
     __shared__ __attribute__((aligned(16))) Op sD[NC][NRB * 64 * 4];        // Delta tiles
-    __shared__ __attribute__((aligned(16))) Op sU[NC][2 * NSB * 64 * NE];   // U hi / lo B-fragments
+    // U as B-fragments: f16 hi / lo pairs (U = hi + lo to ~22 bits), or one
+    // f16 part when kUSplit is off
+    constexpr bool kUSplit = false;
+    constexpr int NUP = std::is_same<Op, _Float16>::value && kUSplit ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) Op sU[NC][NUP * NSB * 64 * NE];
     constexpr int LDO = 16 * NC + 4;                                         // o staging row stride (floats)
     __shared__ __attribute__((aligned(16))) float sO[2][CS * LDO];          // o tiles
     constexpr int LDV = 16 * NC;                                             // raw-v row stride (floats)
@@ -1201,12 +1205,12 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
                         const frag uh = *reinterpret_cast<const frag *>(&sU[q][((0 * NSB + sb) * 64 + lane) * NE]);
-                        const frag ul = *reinterpret_cast<const frag *>(&sU[q][((1 * NSB + sb) * 64 + lane) * NE]);
+                        const frag ul = *reinterpret_cast<const frag *>(&sU[q][(((NUP - 1) * NSB + sb) * 64 + lane) * NE]);
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
                             acc[j][q] = M::mma(cur.Ti[j][sb], uh, acc[j][q]);
-                            acc[j][q] = M::mma(cur.Ti[j][sb], ul, acc[j][q]);
+                            if constexpr (NUP == 2) acc[j][q] = M::mma(cur.Ti[j][sb], ul, acc[j][q]);
                         }
                     }
                 }
@@ -1572,7 +1576,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                             const Op hi = (Op)uu;
                             const int ln = (uc + e) + 16 * ug;
                             sU[q][((0 * NSB + sbx) * 64 + ln) * NE + ui] = hi;
-                            sU[q][((1 * NSB + sbx) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
+                            if constexpr (NUP == 2) sU[q][((1 * NSB + sbx) * 64 + ln) * NE + ui] = (Op)(uu - (float)hi);
                         }
                     }
             }
