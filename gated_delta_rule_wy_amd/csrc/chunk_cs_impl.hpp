@@ -389,19 +389,12 @@ __global__ __launch_bounds__(prep_cs_threads<CS>()) void chunk_prep_cs_kernel(
     __syncthreads();
 
     // ---- stage 5: T = (I + A)^{-1}, block forward substitution ----
-    if (wv < NRB && lane < 16) {
-        const float *Ab = sA + PL::bidx(wv, wv) * BSZ;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc -= Ab[r * BLD + s] * x[s];
-            x[r] = acc;
-        }
+    if (wv < NRB) {   // (whole waves: the solve uses all 64 lanes)
+        float x[4];
+        unit_lower_inverse16(sA + PL::bidx(wv, wv) * BSZ, BLD, lane, x);
         Op *Tb = sT + PL::bidx(wv, wv) * BSZ;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Tb[r * BLD + lane] = (Op)x[r];
+        for (int j = 0; j < 4; ++j) Tb[(g4 + 4 * j) * BLD + m16] = (Op)x[j];
     }
     __syncthreads();
     // T_RS = -T_RR sum_{J=S}^{R-1} A_RJ T_JS, by distance R - S

@@ -87,6 +87,36 @@ template <> struct Lim<float> { static constexpr float v = 60.0f, chunk = 40.0f;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Column l = lane & 15 of the inverse of a 16x16 unit lower-triangular block
+// I + A (A strictly lower, fp32, row stride lda, in LDS), by forward
+// substitution on the whole wave: row x_r = [r == l] - sum_{s<r} A_rs x_s,
+// lane l + 16 g summing the terms with s = g (mod 4), and the four 16-lane
+// rows adding their partial sums with gfx950's lane swaps (permlane16_swap
+// pairs rows 0-1 and 2-3, permlane32_swap the halves; each lane gets its own
+// and its partner's value, and both orders of a two-term float sum agree, so
+// every lane of a column holds the same x_r). Returns rows g + 4 j in x[j].
+__device__ __forceinline__ void unit_lower_inverse16(const float *A, int lda, int lane, float x[4])
+{
+    const int l = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < r / 4 + 1; ++j) {
+            const int s = g + 4 * j;
+            if (s < r) part += A[r * lda + s] * x[j];
+        }
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+        const float xr = (r == l ? 1.f : 0.f) - part;
+        if ((r & 3) == g) x[r >> 2] = xr;
+    }
+}
+
 // ---------------------------------------------------------------------------
 
 // Short convolution of one raw input (fused prologue), device pointers:
@@ -558,19 +588,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 
     // ---- stage 5: T = (I + A)^{-1}, block forward substitution ----
     {
+        // diagonal blocks, one per wave, all 64 lanes (see unit_lower_inverse16)
         const int R = wv;
-        if (lane < 16) {
-            float x[16];
+        float x[4];
+        unit_lower_inverse16(sA + (16 * R) * LDA + 16 * R, LDA, lane, x);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc -= sA[(16 * R + r) * LDA + 16 * R + s] * x[s];
-                x[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(16 * R + r) * LDT + 16 * R + lane] = (Op)x[r];
-        }
+        for (int j = 0; j < 4; ++j) sT[(16 * R + g4 + 4 * j) * LDT + 16 * R + m16] = (Op)x[j];
     }
     __syncthreads();
     for (int d = 1; d < 4; ++d) {
