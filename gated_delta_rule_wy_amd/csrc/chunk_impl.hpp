@@ -1604,6 +1604,16 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                     }
             }
             __syncthreads();   // (1)
+            // the state fragments of Q+ S, read first so that the reads
+            // overlap one another and the o tile's store (each waiting on
+            // its own: pass at T = 64K 0.865 -> 0.840 ms)
+            frag sfo[NC][NKB];
+            if (!SAVE && (RT::ALL || rows)) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) sfo[q][kb] = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
+            }
             // The previous chunk's o tile goes out here, ahead of this
             // step's loads, with per-channel gates given as they are; with one
             // w per token and head (fewer loads) or with the fused prologue
@@ -1635,7 +1645,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        const frag sf = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
+                        const frag sf = sfo[q][kb];
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) oacc[j][q] = M::mma(cur.Qp[j][kb], sf, oacc[j][q]);
                     }
@@ -1643,12 +1653,19 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             if constexpr (!kEarlyU) next_umax();
             __syncthreads();   // (2)
             if (RT::ALL || rows) {
+                // likewise the Delta fragments (all k-blocks: a row tile's
+                // unused ones are in bounds and cost one read)
+                frag dfo[NC][NSB];
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int q = 0; q < NC; ++q) dfo[q][sb] = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
                     if (RPW == 1 && sb > sbmax(0)) break;
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        const frag df = lds_bfrag<Op>(sD[q] + sb * TPK * 256, lane);
+                        const frag df = dfo[q][sb];
 #pragma unroll
                         for (int j = 0; j < RPW; ++j) {
                             if (RPW > 1 && sb > sbmax(j)) continue;
