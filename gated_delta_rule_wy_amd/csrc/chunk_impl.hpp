@@ -1209,12 +1209,14 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
             for (int q = 0; q < NC; ++q) { mS[q] = 0.f; mD[q] = 0.f; }
             if (RT::ALL || rows) {
-                // T U, then -W S (both divided by the chunk's scale)
-                f4 acc[RPW][NC], accw[RPW][NC];
+                // T U, then -W S (both divided by the chunk's scale; the -W S
+                // k-blocks in two accumulators by parity, two dependent chains
+                // of half the length: pass at T = 64K 0.838 -> 0.829 ms)
+                f4 acc[RPW][NC], accw[RPW][NC], accw2[RPW][NC];
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
-                    for (int q = 0; q < NC; ++q) { acc[j][q] = f4zero(); accw[j][q] = f4zero(); }
+                    for (int q = 0; q < NC; ++q) { acc[j][q] = f4zero(); accw[j][q] = f4zero(); accw2[j][q] = f4zero(); }
                 // every B fragment is read from LDS before the products, so
                 // that the reads overlap rather than each wait on its own
                 frag sfr[NC][NKB];
@@ -1242,7 +1244,10 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                     for (int q = 0; q < NC; ++q)
 #pragma unroll
-                        for (int j = 0; j < RPW; ++j) accw[j][q] = M::mma(cur.nW[j][kb], sfr[q][kb], accw[j][q]);
+                        for (int j = 0; j < RPW; ++j) {
+                            if (kb & 1) accw2[j][q] = M::mma(cur.nW[j][kb], sfr[q][kb], accw2[j][q]);
+                            else accw[j][q] = M::mma(cur.nW[j][kb], sfr[q][kb], accw[j][q]);
+                        }
                 // the state maxima, while the products run
                 if constexpr (SCL) {
 #pragma unroll
@@ -1252,7 +1257,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 for (int j = 0; j < RPW; ++j)
 #pragma unroll
                     for (int q = 0; q < NC; ++q) {
-                        const f4 d = acc[j][q] + accw[j][q];
+                        const f4 d = acc[j][q] + (accw[j][q] + accw2[j][q]);
                         if constexpr (SCL) {
 #pragma unroll
                             for (int ii = 0; ii < 4; ++ii) mD[q] = fmaxf(mD[q], fabsf(d[ii]));
