@@ -66,11 +66,12 @@ template <typename In, int DK, int DV, bool PRO>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     const In *__restrict__ q, const In *__restrict__ k, const In *__restrict__ v,
     const float *__restrict__ la, const In *__restrict__ b, const In *__restrict__ w,
-    float *__restrict__ S, float *__restrict__ o, int gates, int H, DecConv cq, DecConv ck, DecConv cv)
+    float *__restrict__ S, float *__restrict__ o, int gates, int H, int rev, DecConv cq, DecConv ck, DecConv cv)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int COLG = Sh::COLG, ROWG = Sh::ROWG, RPT = Sh::RPT, NT = Sh::NT;
-    const int nh = blockIdx.x;            // sequence * H + head
+    // sequence * H + head, in the order of this call (see decode_order)
+    const int nh = rev ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
     const int t = threadIdx.x;
     const int cg = t % COLG, rg = t / COLG;
 
@@ -218,6 +219,30 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(
     }
 }
 
+// Order of the chains for this call on state buffer S. Successive calls on
+// one state visit the (sequence, head) chains in alternating directions, so
+// the chains written last, which the last-level cache still holds, are read
+// first: with a state of 1 GiB (four times that cache) the step takes 16%
+// less time (431 -> 363 us at 1024 x 16 chains, d = 128). Each chain is read
+// and written by one workgroup, so the results do not depend on the order.
+// The parity is kept per thread in a small table keyed by the state's
+// address; a state that loses its entry restarts at the forward order.
+static int decode_order(const void *S)
+{
+    constexpr int kSlots = 64;
+    struct Slot {
+        const void *p = nullptr;
+        unsigned n = 0;
+    };
+    thread_local Slot slots[kSlots];
+    Slot &x = slots[((uintptr_t)S >> 8) % kSlots];
+    if (x.p != S) {
+        x.p = S;
+        x.n = 0;
+    }
+    return (int)(x.n++ & 1u);
+}
+
 template <typename In, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st)
 {
@@ -225,11 +250,12 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st)
     const DecConv cq = {a.pro.q.w, a.pro.q.bias, a.pro.q.hist_in, a.pro.q.hist_out};
     const DecConv ck = {a.pro.k.w, a.pro.k.bias, a.pro.k.hist_in, a.pro.k.hist_out};
     const DecConv cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in, a.pro.v.hist_out};
+    const int rev = decode_order(a.S);
     prof_before("gdn2_decode", st);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(a.N * a.H), dim3(NT), 0, st, (const In *)a.q, (const In *)a.k,
                            (const In *)a.v, a.log_alpha, (const In *)a.b, (const In *)a.w, a.S, (float *)a.o,
-                           a.gates, a.H, cq, ck, cv);
+                           a.gates, a.H, rev, cq, ck, cv);
     };
     if (a.pro.on) go(decode_kernel<In, DK, DV, true>);
     else go(decode_kernel<In, DK, DV, false>);

@@ -197,7 +197,10 @@ int gdn2_chunk_fwd_sized(const void *q, const void *k, const void *v, const floa
  *   S          [N, H, dk, dv]   float, read and updated in place
  *   o          [N, H, dv]       out_dtype (GDN2_F32 only)
  *
- * dk, dv in {16, 32, 64, 128}. S is read once and written once.
+ * dk, dv in {16, 32, 64, 128}. S is read once and written once. Successive
+ * calls from one thread on the same S visit the (sequence, head) chains in
+ * alternating order (the chains written last, still in the last-level cache,
+ * are read first); the results do not depend on the order.
  */
 int gdn2_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                      const void *b, const void *w, float *S, void *o, int N, int H, int dk,
