@@ -1573,9 +1573,11 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
             if constexpr (PRO) stage_v(unext, sln);
             // this wave's part of the bound for the next chunk's scale: max |U|
             // of the next chunk. With a ring of three or four its rows were
-            // loaded steps ago and it goes out first, off the path to the
-            // barriers; with a ring of two it is the load issued after barrier
-            // (1), and with the prologue it is formed there.
+            // loaded steps ago and it is formed right after barrier (1), while
+            // the state fragments' LDS reads are in flight (at the start of the
+            // step it sat on the path to barrier (1): pass at T = 64K 0.823 ->
+            // 0.783 ms); with a ring of two it is the load issued after barrier
+            // (1), and with the prologue it is formed there, both before (2).
             auto next_umax = [&]() {
                 if constexpr (SCL) {
                     uint32_t mr[NC];
@@ -1589,7 +1591,6 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                 }
             };
             constexpr bool kEarlyU = ORING >= 3 && !PRO;
-            if constexpr (kEarlyU) next_umax();
             if (urow) {
 #pragma unroll
                 for (int x = 0; x < UR; ++x)
@@ -1619,6 +1620,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
 #pragma unroll
                     for (int q = 0; q < NC; ++q) sfo[q][kb] = lds_bfrag<Op>(sS[q] + kb * TPK * 256, lane);
             }
+            if constexpr (kEarlyU) next_umax();   // (see next_umax)
             // The previous chunk's o tile goes out here, ahead of this
             // step's loads, with per-channel gates given as they are; with one
             // w per token and head (fewer loads) or with the fused prologue
