@@ -336,6 +336,33 @@ def bench_backward(args, torch, gdn2, q, k, v, la, b, w, S0, p):
            'kernels_ms': {kk: round(vv, 5) for kk, vv in avg.items()},
            # the per-chunk gradient kernel reads and writes every per-token tensor
            'roofline': roofline('gdn2_chunk_grad', nbytes, avg['gdn2_chunk_grad'], 'backward_t65536')}
+    # The training step: the forward that keeps what the backward needs
+    # (gdn2_chunk_fwd_keep: o and S_T as gdn2_chunk_fwd, plus the operand
+    # blocks, chunk states and corrected writes) and the backward from them
+    # (gdn2_chunk_bwd_kept), against gdn2_chunk_fwd followed by gdn2_chunk_bwd.
+    def train():
+        gdn2.chunk_fwd_keep(q, k, v, la, b, w, S0, workspace=wsb)
+        return gdn2.chunk_bwd_kept(q, k, v, la, b, w, S0, dO, dST, workspace=wsb)
+    for _ in range(args.warmup):
+        g = train()
+    torch.cuda.synchronize()
+    gdn2.profile_begin(2 * args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g = train()
+    torch.cuda.synchronize()
+    tms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tprof = gdn2.profile_end()
+    tavg = {kk: vv[1] / vv[0] for kk, vv in tprof.items() if vv[0]}
+    log(f'[bench] training step (keep + kept) {tms:.3f} ms/step; kernels: ' +
+        ', '.join(f'{kk} {vv:.4f} ms' for kk, vv in tavg.items()))
+    fwd_bytes = TH * (3 * dk * 2 + dk * 4) + TH * (2 * dv * 2 + dv * 4) + 2 * B * H * dk * dv * 4
+    res['training_step'] = {
+        'ms_per_step': round(tms, 4), 'value': B * T / (tms * 1e-3), 'unit': 'tokens/s',
+        'what': 'gdn2_chunk_fwd_keep then gdn2_chunk_bwd_kept (o, S_T and every gradient)',
+        'alg_bytes_per_step': int(fwd_bytes + nbytes),
+        'step_roofline_frac': round((fwd_bytes + nbytes) / (tms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        'kernels_ms': {kk: round(vv, 5) for kk, vv in tavg.items()}}
     if not args.no_cpu_baseline:
         import oracle
         n_s = min(T, args.cpu_sample_tokens // 4)

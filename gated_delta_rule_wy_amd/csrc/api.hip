@@ -355,11 +355,13 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int N, int H, int dk, int dv
     return bp.total_bytes > 0 ? bp.total_bytes : 256;
 }
 
-int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                   const void *b, const void *w, const float *S0, const float *dO, const float *dST,
-                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
-                   int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
-                   float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes)
+// gdn2_chunk_bwd and its two halves (part: gdn2::kBwdAll, kBwdForward,
+// kBwdFromKept); every check runs before anything is launched
+static int chunk_bwd_impl(const void *q, const void *k, const void *v, const float *log_alpha, const void *b,
+                          const void *w, const float *S0, const float *dO, const float *dST,
+                          const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv, int in_dtype,
+                          float *dq, float *dk_, float *dv_, float *dlog_alpha, float *db, float *dw, float *dS0,
+                          void *o, float *ST, int part, void *workspace, size_t workspace_bytes)
 {
     gdn2::ChunkPlan plan;
     const int varlen = cu_seqlens != nullptr;
@@ -369,11 +371,12 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     if (!gdn2::chunk_bwd_plan(B, T, N, H, dk, dv, in_dtype == GDN2_BF16, varlen != 0, &bp))
         return GDN2_ERR_UNSUPPORTED;
     const bool have_tokens = (long long)B * T > 0;
-    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk_ || !dv_ || !dlog_alpha ||
-                        !db || !dw))
+    if (have_tokens && (!q || !k || !v || !log_alpha || !b || !w)) return GDN2_ERR_INVALID;
+    if (part == gdn2::kBwdForward && have_tokens && !o) return GDN2_ERR_INVALID;
+    if (part != gdn2::kBwdForward && have_tokens && (!dO || !dq || !dk_ || !dv_ || !dlog_alpha || !db || !dw))
         return GDN2_ERR_INVALID;
     const void *ptrs[] = {q, k, v, log_alpha, b, w, S0, dO, dST, cu_seqlens, dq, dk_, dv_, dlog_alpha, db, dw, dS0,
-                          workspace};
+                          o, ST, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return GDN2_ERR_INVALID;
     if (!workspace || workspace_bytes < bp.total_bytes) return GDN2_ERR_WORKSPACE;
@@ -390,9 +393,44 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.dS0 = dS0;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+    a.part = part;
+    a.o = o;
+    a.ST = ST;
     prof_call();
     if (gdn2::launch_chunk_bwd(a, bp, g_stream) != hipSuccess) return GDN2_ERR_HIP;
     return GDN2_OK;
+}
+
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const void *b, const void *w, const float *S0, const float *dO, const float *dST,
+                   const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                   int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                   float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes)
+{
+    return chunk_bwd_impl(q, k, v, log_alpha, b, w, S0, dO, dST, cu_seqlens, B, T, N, H, dk, dv, in_dtype, dq, dk_,
+                          dv_, dlog_alpha, db, dw, dS0, nullptr, nullptr, gdn2::kBwdAll, workspace, workspace_bytes);
+}
+
+int gdn2_chunk_fwd_keep(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const void *b, const void *w, const float *S0, void *o, float *ST,
+                        const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                        int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes)
+{
+    if (out_dtype != GDN2_F32) return out_dtype == GDN2_BF16 ? GDN2_ERR_UNSUPPORTED : GDN2_ERR_INVALID;
+    return chunk_bwd_impl(q, k, v, log_alpha, b, w, S0, nullptr, nullptr, cu_seqlens, B, T, N, H, dk, dv, in_dtype,
+                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, ST, gdn2::kBwdForward,
+                          workspace, workspace_bytes);
+}
+
+int gdn2_chunk_bwd_kept(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const void *b, const void *w, const float *S0, const float *dO, const float *dST,
+                        const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                        int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                        float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes)
+{
+    return chunk_bwd_impl(q, k, v, log_alpha, b, w, S0, dO, dST, cu_seqlens, B, T, N, H, dk, dv, in_dtype, dq, dk_,
+                          dv_, dlog_alpha, db, dw, dS0, nullptr, nullptr, gdn2::kBwdFromKept, workspace,
+                          workspace_bytes);
 }
 
 static int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -576,7 +576,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     constexpr size_t B_DA = 0, B_DP = B_DA + 64 * LDF, B_XT = B_DP + 64 * LDF, B_XM = B_XT + CW * LDF,
                      B_BT = B_XM + CW * LDF, B_BM = B_BT + CW * LDF, B_QT = B_BM + CW * LDF, B_QM = B_QT + CW * LDF,
                      B_DG = B_QM + CW * LDF, B_GAM = B_DG + 64 * LDC, B_KHK = B_GAM + DK,
-                     B_END = B_KHK + DK;                                            // floats
+                     B_KHS = B_KHK + 16 * CW, B_END = B_KHS + CW;                   // floats
     constexpr int LDR = 64 + 4;                           // raw inputs of the slice, transposed
     constexpr size_t B_BYTES = B_END * 4 + 3 * CW * LDR * sizeof(In);
     constexpr size_t REGION = (A_END * sizeof(Op) > B_BYTES ? A_END * sizeof(Op) : B_BYTES);
@@ -592,7 +592,10 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
     float *fb = (float *)smem;
     float *sdA = fb + B_DA, *sdP = fb + B_DP, *XtT = fb + B_XT, *XmT = fb + B_XM, *BtT = fb + B_BT, *BmT = fb + B_BM;
     float *QtT = fb + B_QT, *QmT = fb + B_QM, *sdG = fb + B_DG;
-    float *sGam = fb + B_GAM, *sKhK = fb + B_KHK;
+    // sum over the chunk's rows of (dk through Khat) k, per channel of the
+    // slice: the part of each (wave, 4-row group) in its own slot, then their
+    // sum in a fixed order (deterministic, unlike float atomics)
+    float *sGam = fb + B_GAM, *sKhK = fb + B_KHK, *sKhS = fb + B_KHS;
     In *sqT = (In *)(fb + B_END), *skT = sqT + CW * LDR, *sbT = skT + CW * LDR;
 
     const int t = threadIdx.x, lane = t & 63, wv = wave_id() & 3, hv = wave_id() >> 2, m16 = lane & 15, g4 = lane >> 4;
@@ -868,10 +871,7 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
             sdA[r * LDF + s_] = r > s_ ? -accA[i][ii] : 0.f;
             sdP[r * LDF + s_] = r >= s_ ? accP[i][ii] : 0.f;
         }
-    if (t < DK) {
-        sGam[t] = gam * __expf(sRef[4 * DK + t]);
-        sKhK[t] = 0.f;
-    }
+    if (t < DK) sGam[t] = gam * __expf(sRef[4 * DK + t]);
 
     // ---- phase B, key channels in slices of CW ----
     // Thread t owns channel bcl = t % CW of the slice and the SL consecutive
@@ -1073,14 +1073,20 @@ __global__ __launch_bounds__(NT) void chunk_grad_kernel(
                     db[o] = dbv;
                 }
             }
-            atomicAdd(&sKhK[c], khk);
+            sKhK[(wv * 4 + g4) * CW + cl] = khk;   // rows 16 wv + 4 g4 .. + 3
         }
         __syncthreads();
+        if (t < CW) {
+            float x = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < 16; ++sl) x += sKhK[sl * CW + t];
+            sKhS[t] = x;   // (read after the scan's barriers)
+        }
         col_scan64<CW, true, NT>(sdG, LDC, sPart, t);
 #pragma unroll
         for (int u = 0; u < 64 * CW / NT; ++u) {
             const int x = t + NT * u, r = x / CW, cl = x % CW, c = c0 + cl;
-            if (r < n) dla[tok_k(r) + c] = sdG[r * LDC + cl] + sKhK[c] + sGam[c];
+            if (r < n) dla[tok_k(r) + c] = sdG[r * LDC + cl] + sKhS[cl] + sGam[c];
         }
     }
 }
@@ -1094,18 +1100,23 @@ static hipError_t bwd_t(const ChunkBwdArgs &a, const BwdPlan &bp, hipStream_t st
     fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.b = a.b; fa.w = a.w;
     fa.log_alpha = a.log_alpha;
     fa.S0 = a.S0;
-    fa.o = nullptr;
-    fa.ST = nullptr;
+    fa.o = a.part == kBwdForward ? a.o : nullptr;
+    fa.ST = a.part == kBwdForward ? a.ST : nullptr;
     fa.cu_seqlens = a.cu_seqlens;
     fa.B = a.B; fa.T = a.T; fa.N = a.N; fa.H = a.H; fa.dk = a.dk; fa.dv = a.dv;
     fa.gates = 0;
     fa.bf16 = a.bf16;
     fa.workspace = a.workspace;
     fa.workspace_bytes = a.workspace_bytes;
-    // forward: operand blocks, then the pass keeping S_c and Delta
-    const SaveOut so = {ws + bp.off_states, ws + bp.off_delta};
-    hipError_t err = launch_t<In, Op, DK, DV>(fa, bp.fwd, st, so);
-    if (err != hipSuccess) return err;
+    // forward: operand blocks, then the pass keeping S_c and Delta (the
+    // training forward also forms o and S_T); a backward over what a training
+    // forward kept starts after it
+    hipError_t err = hipSuccess;
+    if (a.part != kBwdFromKept) {
+        const SaveOut so = {ws + bp.off_states, ws + bp.off_delta, a.part == kBwdForward};
+        err = launch_t<In, Op, DK, DV>(fa, bp.fwd, st, so);
+        if (err != hipSuccess || a.part == kBwdForward) return err;
+    }
 
     Seqs sq;
     sq.m.cu = a.cu_seqlens;

@@ -497,7 +497,7 @@ static hipError_t launch_cs(const ChunkArgs &a, const ChunkPlan &p, hipStream_t 
     if ((err = pass_shape<DV>(chains, p, &ps)) != hipSuccess) return err;
     prof_before("gdn2_chunk_pass", st);
     const ConvIn cv = {nullptr, nullptr, nullptr};
-    const SaveOut so = {nullptr, nullptr};
+    const SaveOut so = {nullptr, nullptr, false};
     auto pass = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)ps.grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
                            (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, ps.npf, cv, so);

@@ -1005,9 +1005,14 @@ __device__ __forceinline__ void pass_prefetch(const uint8_t *blk0, const In *v, 
 // operand blocks, in accumulator-tile order: tile (row tile rt, column tile
 // ct) at (rt * dv/16 + ct) * 256, lane l = n + 16g holding rows 4g..4g+3 of
 // column n (one 8- or 16-byte store per lane and tile).
+//
+// KEEP (the training forward): the state waves store S_c and Delta as under
+// SAVE while the output waves form o as in the plain forward, so one pass
+// gives o, S_T and what the backward keeps.
 struct SaveOut {
-    void *S;   // [H * max_chunks][dk/16][dv/16][64][4]
-    void *D;   // [H * max_chunks][4][dv/16][64][4]
+    void *S;          // [H * max_chunks][dk/16][dv/16][64][4]
+    void *D;          // [H * max_chunks][4][dv/16][64][4]
+    bool with_out;    // KEEP: also o and S_T
 };
 
 // (a whole 16x16 tile per wave: non-temporal, like the operand blocks)
@@ -1021,14 +1026,17 @@ __device__ __forceinline__ void tile_store(Op *dst, int lane, const f4 &x)
     __builtin_nontemporal_store(y, reinterpret_cast<op4 *>(dst + lane * 4));
 }
 
-template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false, int CS = 64>
+template <typename In, typename Op, int DK, int DV, int NC, bool WSC, bool PRO, bool SAVE = false, int CS = 64,
+          bool KEEP = false>
 __global__ __launch_bounds__(512) void chunk_pass_kernel(
     const In *__restrict__ v, const In *__restrict__ w, const float *__restrict__ S0,
     float *__restrict__ o, float *__restrict__ ST, Seqs sq, int H,
     const uint8_t *__restrict__ ops, int *__restrict__ prog, int npf, ConvIn cv, SaveOut so)
 {
     static_assert(!PRO || !WSC, "the prologue takes per-channel gates");
-    static_assert(CS == 64 || (!PRO && !SAVE), "the prologue and the backward use 64-token chunks");
+    static_assert(CS == 64 || (!PRO && !SAVE && !KEEP), "the prologue and the backward use 64-token chunks");
+    static_assert(!(SAVE && KEEP) && !(KEEP && (PRO || WSC)), "KEEP: the training forward, per-channel gates");
+    constexpr bool STORE_SD = SAVE || KEEP;   // the state waves keep S_c and Delta
     using M = Mma<Op>;
     using L = Blk<Op, DK, CS>;
     using RT = RowTiles<CS>;
@@ -1191,7 +1199,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
         // the state waves would otherwise wait for the output waves.
         const size_t slot0 = (size_t)h * sq.max_chunks + cbeg;
         auto step = [&](int c, SF &cur, SF &pre) {
-            if constexpr (SAVE) {
+            if constexpr (STORE_SD) {
                 Op *sp = (Op *)so.S + (slot0 + c) * DK * DV;
 #pragma unroll
                 for (int q = 0; q < NC; ++q)
@@ -1263,7 +1271,7 @@ __global__ __launch_bounds__(512) void chunk_pass_kernel(
                             for (int ii = 0; ii < 4; ++ii) mD[q] = fmaxf(mD[q], fabsf(d[ii]));
                         }
                         lds_tile_store<Op>(sD[q] + RT::rt(wv, j) * 256, lane, d);
-                        if constexpr (SAVE) {
+                        if constexpr (STORE_SD) {
                             if (j == 0) {
                                 Op *dp = (Op *)so.D + (slot0 + c) * 64 * DV;
                                 tile_store<Op>(dp + ((size_t)wv * (DV / 16) + NC * js + q) * 256, lane,
@@ -1795,7 +1803,8 @@ template <int DV> static hipError_t pass_shape(long long chains, const ChunkPlan
 }
 
 template <typename In, typename Op, int DK, int DV>
-static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st, SaveOut so = {nullptr, nullptr})
+static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t st,
+                           SaveOut so = {nullptr, nullptr, false})
 {
     uint8_t *ws = (uint8_t *)a.workspace;
     const Seqs sq = make_seqs(a, p);
@@ -1825,14 +1834,20 @@ static hipError_t launch_t(const ChunkArgs &a, const ChunkPlan &p, hipStream_t s
     if ((err = pass_shape<DV>(chains, p, &ps)) != hipSuccess) return err;
     const bool two = ps.two;
     const int npf = ps.npf;
-    prof_before("gdn2_chunk_pass", st);
+    prof_before(so.S && so.with_out ? "gdn2_chunk_pass_keep" : "gdn2_chunk_pass", st);
     const ConvIn cv = {a.pro.v.w, a.pro.v.bias, a.pro.v.hist_in};
     auto pass = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)ps.grid), dim3(512), 0, st, (const In *)a.v, (const In *)a.w, a.S0,
                            (float *)a.o, a.ST, sq, a.H, (const uint8_t *)ops, prog, npf, cv, so);
     };
     const bool wsc = a.gates & kGateW;
-    if (so.S) {
+    if (so.S && so.with_out) {
+        // the training forward: o and S_T, and S_c, Delta kept for the backward
+        if constexpr ((DV / 16) % 2 == 0) {
+            if (two) pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, false, false, 64, true>);
+            else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, false, false, 64, true>);
+        } else pass(chunk_pass_kernel<In, Op, DK, DV, 1, false, false, false, 64, true>);
+    } else if (so.S) {
         // the forward part of the backward: per-channel gates, raw inputs
         if constexpr ((DV / 16) % 2 == 0) {
             if (two) pass(chunk_pass_kernel<In, Op, DK, DV, 2, false, false, true>);

@@ -84,7 +84,15 @@ struct ChunkBwdArgs {
     float *dS0;                  // or null
     void *workspace;
     size_t workspace_bytes;
+    // which part runs: the whole backward (its own forward first), only the
+    // training forward (o and S_T, keeping the operand blocks, S_c and Delta
+    // in the workspace), or only the backward over what a training forward
+    // kept there
+    int part;                    // kBwdAll, kBwdForward, kBwdFromKept
+    void *o;                     // kBwdForward: [tokens][H][dv] float
+    float *ST;                   // kBwdForward: [N][H][dk][dv] float, or null
 };
+enum { kBwdAll = 0, kBwdForward = 1, kBwdFromKept = 2 };
 
 // Backward workspace: the forward plan's regions, then (256-byte aligned)
 //   backward operand blocks   [H * max_chunks] x bblock_bytes

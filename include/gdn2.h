@@ -319,6 +319,40 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
                    float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes);
 
 /*
+ * The training pair: gdn2_chunk_fwd_keep is gdn2_chunk_fwd (per-channel
+ * gates) that also leaves in `workspace` what the backward would otherwise
+ * recompute (each chunk's operand block, start state S_c and corrected
+ * writes), and gdn2_chunk_bwd_kept is gdn2_chunk_bwd without its own run of
+ * the forward, starting from what a gdn2_chunk_fwd_keep left there. A
+ * training step thus runs the forward once (the chunkwise form for GPU
+ * training: aifetchly, "Gated DeltaNet-2 Guide", section "3. Chunkwise
+ * Parallel Algorithm for GPU Training"; snilld.dk, section "Hvad betyder det
+ * for træning og inferens").
+ *
+ * gdn2_chunk_fwd_keep: arguments as gdn2_chunk_fwd, except that `workspace`
+ *   holds at least gdn2_chunk_bwd_workspace_bytes(...) bytes. o and S_T are
+ *   those gdn2_chunk_fwd returns for the same inputs, bit for bit.
+ * gdn2_chunk_bwd_kept: arguments as gdn2_chunk_bwd. The workspace, q, k, v,
+ *   log_alpha, b, w, S0, cu_seqlens and sizes must be those of the last
+ *   gdn2_chunk_fwd_keep on this workspace, with the workspace untouched since
+ *   (on the same stream, or ordered after it); then the gradients equal those
+ *   of gdn2_chunk_bwd bit for bit. Nothing checks this pairing on the device:
+ *   a workspace that another call overwrote gives meaningless gradients.
+ * Errors as in gdn2_chunk_fwd / gdn2_chunk_bwd; nothing is launched on an
+ * error.
+ */
+int gdn2_chunk_fwd_keep(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const void *b, const void *w, const float *S0, void *o, float *ST,
+                        const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                        int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes);
+
+int gdn2_chunk_bwd_kept(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const void *b, const void *w, const float *S0, const float *dO, const float *dST,
+                        const int32_t *cu_seqlens, int B, int T, int N, int H, int dk, int dv,
+                        int in_dtype, float *dq, float *dk_, float *dv_, float *dlog_alpha,
+                        float *db, float *dw, float *dS0, void *workspace, size_t workspace_bytes);
+
+/*
  * Per-kernel timing, for measurement tools (not needed for computing).
  * gdn2_profile_begin(max_calls) makes this thread's next gdn2_chunk_fwd /
  * gdn2_decode_step calls (up to max_calls of them, 1..4096) record a HIP

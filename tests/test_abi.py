@@ -275,3 +275,74 @@ def test_prologue_binding_validates_before_calling():
     with pytest.raises(TypeError):             # history in the wrong dtype
         gdn2.chunk_fwd_prologue(x, x, x, la, x, x, wt,
                                 conv_state=tuple(torch.zeros(1, 1, 3, 128) for _ in range(3)))
+
+
+# ---- the training pair (gdn2_chunk_fwd_keep / gdn2_chunk_bwd_kept): every
+# check runs before a launch, so fake aligned addresses never reach a kernel
+
+def _keep(**kw):
+    P = 0x10000
+    a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S0=None, o=P, ST=P, cu=None, B=1, T=64, N=1, H=1,
+             dk=128, dv=128, dt=gdn2.GDN2_BF16, odt=gdn2.GDN2_F32, ws=P, wsb=1 << 30)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return gdn2.lib().gdn2_chunk_fwd_keep(*(vp(a[x]) if a[x] else None for x in
+                                            ('q', 'k', 'v', 'la', 'b', 'w', 'S0', 'o', 'ST', 'cu')),
+                                          a['B'], a['T'], a['N'], a['H'], a['dk'], a['dv'], a['dt'], a['odt'],
+                                          vp(a['ws']) if a['ws'] else None, a['wsb'])
+
+
+def _kept(**kw):
+    P = 0x10000
+    a = dict(q=P, k=P, v=P, la=P, b=P, w=P, S0=None, dO=P, dST=None, cu=None, B=1, T=64, N=1, H=1,
+             dk=128, dv=128, dt=gdn2.GDN2_BF16, dq=P, dk_=P, dv_=P, dla=P, db=P, dw=P, dS0=None,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    ptr = lambda x: vp(a[x]) if a[x] else None
+    return gdn2.lib().gdn2_chunk_bwd_kept(*(ptr(x) for x in ('q', 'k', 'v', 'la', 'b', 'w', 'S0', 'dO', 'dST', 'cu')),
+                                          a['B'], a['T'], a['N'], a['H'], a['dk'], a['dv'], a['dt'],
+                                          *(ptr(x) for x in ('dq', 'dk_', 'dv_', 'dla', 'db', 'dw', 'dS0', 'ws')),
+                                          a['wsb'])
+
+
+BWS = gdn2.lib().gdn2_chunk_bwd_workspace_bytes
+
+
+@pytest.mark.parametrize('kw,status', [
+    (dict(q=None), gdn2.GDN2_ERR_INVALID),
+    (dict(o=None), gdn2.GDN2_ERR_INVALID),
+    (dict(w=0x10004), gdn2.GDN2_ERR_INVALID),
+    (dict(ST=0x10008), gdn2.GDN2_ERR_INVALID),
+    (dict(N=2), gdn2.GDN2_ERR_INVALID),
+    (dict(odt=gdn2.GDN2_BF16), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(odt=7), gdn2.GDN2_ERR_INVALID),
+    (dict(dk=48), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(ws=None), gdn2.GDN2_ERR_WORKSPACE),
+    # the forward's own workspace is too small: the backward's is needed
+    (dict(wsb=WS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0)), gdn2.GDN2_ERR_WORKSPACE),
+    (dict(wsb=BWS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) - 1), gdn2.GDN2_ERR_WORKSPACE),
+])
+def test_chunk_fwd_keep_rejects(kw, status):
+    assert _keep(**kw) == status
+
+
+@pytest.mark.parametrize('kw,status', [
+    (dict(dO=None), gdn2.GDN2_ERR_INVALID),
+    (dict(dla=None), gdn2.GDN2_ERR_INVALID),
+    (dict(dS0=0x10004), gdn2.GDN2_ERR_INVALID),
+    (dict(T=-1), gdn2.GDN2_ERR_INVALID),
+    (dict(dv=100), gdn2.GDN2_ERR_UNSUPPORTED),
+    (dict(ws=None), gdn2.GDN2_ERR_WORKSPACE),
+    (dict(wsb=BWS(1, 64, 1, 1, 128, 128, gdn2.GDN2_BF16, 0) - 1), gdn2.GDN2_ERR_WORKSPACE),
+])
+def test_chunk_bwd_kept_rejects(kw, status):
+    assert _kept(**kw) == status
+
+
+def test_kept_binding_needs_the_workspace():
+    torch = pytest.importorskip('torch')
+    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    la = torch.zeros(1, 64, 1, 128)
+    with pytest.raises(ValueError, match='workspace'):
+        gdn2.chunk_bwd_kept(x, x, x, la, x, x, None, la, workspace=torch.zeros(16, dtype=torch.uint8))

@@ -137,3 +137,16 @@ def test_full_size_t65536():
     p = gi.prefill(c['seed'], [c['T']], H=c['H'], dk=c['dk'], dv=c['dv'], dtype=c['dtype'], s0_std=c['s0_std'],
                    threads=threads())
     check(p, 'T=65536 H=16')
+
+
+def test_deterministic():
+    """Two runs on the same inputs give the same gradients bit for bit (the
+    per-channel sums over a chunk's rows are taken in a fixed order)."""
+    p = gi.prefill(97, [300, 77, 200], H=4, dk=128, dv=128, dtype='bf16', s0_std=0.05, uniform=False)
+    rng = np.random.default_rng(5)
+    dO = rng.standard_normal((p.tokens, p.H, p.dv)).astype(np.float32)
+    dST = rng.standard_normal((p.N, p.H, p.dk, p.dv)).astype(np.float32)
+    a = grads_gpu(p, dO, dST)
+    b = grads_gpu(p, dO, dST)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), f'd{n} differs between two runs'
